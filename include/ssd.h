@@ -1,0 +1,181 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD layer scan library.
+ *
+ * The operation is the state space duality (SSD) scan of Mamba-2 as stated in
+ * arXiv 2603.09555 (C. Santoni, "Compiler-First State Space Duality and
+ * Portable O(1) Autoregressive Caching for Inference"), abstract, and in the
+ * bqwf.cn article on its compiler-first implementation (§1.1 diagonal
+ * per-head decay and fixed-size chunks, §1.2 intra-chunk einsum, §2.1-§2.2
+ * the constant-size cache and its update).  For every batch element b and
+ * head h, with A_h = -exp(A_log[h]) and g = h / (H / G):
+ *
+ *     state_t = exp(dt[b,t,h] * A_h) * state_{t-1}
+ *               + dt[b,t,h] * x[b,t,h,:] (outer) Bm[b,t,g,:]      [P x N]
+ *     y[b,t,h,p] = sum_n Cm[b,t,g,n] * state_t[p,n] + D[h] * x[b,t,h,p]
+ *
+ * ssd_prefill evaluates it over a whole sequence in chunks of Q tokens;
+ * ssd_decode_step advances it by one token from a cached state, optionally
+ * after one step of the depthwise causal convolution whose (K-1)-token input
+ * window is the other half of the cache; conv_state_update runs that
+ * convolution over T tokens.
+ *
+ * Conventions shared by every entry point
+ *   - Layouts: dense, row-major (C-contiguous) in the shapes given, unless a
+ *     row stride argument says otherwise.
+ *   - Ownership: every pointer is a device pointer owned by the caller.  The
+ *     library allocates nothing, frees nothing and keeps no pointer after the
+ *     call returns.  Scratch memory is the caller's `workspace`.
+ *   - Asynchrony: calls only enqueue kernels on `stream` (0 = the null
+ *     stream) and return without synchronising.  Results are valid once the
+ *     caller has synchronised with the stream.
+ *   - Errors: 0 on success, a negative SSD_ERR_* code otherwise.  All
+ *     argument checks run on the host before any HIP call, so a rejected call
+ *     launches nothing and leaves every output untouched.  A failed launch
+ *     returns SSD_ERR_HIP; its hipError_t is kept per host thread and read by
+ *     ssd_last_hip_error().  Faults inside a kernel surface at the caller's
+ *     next synchronisation, as for any HIP library.  No C++ exception crosses
+ *     this interface.
+ *   - Re-entrancy: no global mutable state apart from the per-thread last
+ *     HIP error; calls on different streams may run concurrently as long as
+ *     their buffers do not overlap.
+ *   - dtype: SSD_F32 or SSD_BF16, the storage type of the activations named
+ *     "void*" below (x, Bm, Cm, y and the conv data).  dt, A_log, D and the
+ *     SSM state are always fp32; all arithmetic accumulates in fp32.
+ */
+#ifndef MAMBA_SSD_H
+#define MAMBA_SSD_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SSD_F32 = 0,
+    SSD_BF16 = 1,
+};
+
+enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARG = -1, /* null required pointer, bad dimension, G not dividing H, K < 2, aliasing */
+    SSD_ERR_UNSUPPORTED = -2, /* shape / dtype combination this build has no kernel for */
+    SSD_ERR_ALIGNMENT = -3,   /* a pointer or row stride breaks the documented alignment */
+    SSD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query returned */
+    SSD_ERR_HIP = -5,         /* a HIP call failed; see ssd_last_hip_error() */
+};
+
+/*
+ * ssd_prefill -- chunked SSD scan over a whole sequence.
+ * Source: bqwf.cn article §1.1 (sequence split into fixed-size chunks; dense
+ * matrix work inside a chunk, a light sequential scan of the state between
+ * chunks; decay matrix tril(exp(segsum(dt*A)))) and §1.2 (intra-chunk
+ * product C B^T masked by the decay, applied to the discretised input).
+ *
+ *   x      [B,L,H,P]  dtype       input of every head
+ *   dt     [B,L,H]    fp32        discretisation step, already positive (the
+ *                                 caller applies softplus / clipping)
+ *   A_log  [H]        fp32        A_h = -exp(A_log[h])
+ *   Bm, Cm [B,L,G,N]  dtype       input and output projections per group
+ *   D      [H]        fp32        skip weight; NULL means 0
+ *   init_state  [B,H,P,N] fp32    state before token 0; NULL means zeros
+ *   y      [B,L,H,P]  dtype       output; must not overlap any input
+ *   final_state [B,H,P,N] fp32    state after token L-1; NULL to skip; may be
+ *                                 the same buffer as init_state
+ *   workspace, workspace_bytes    device scratch of at least
+ *                                 ssd_prefill_workspace_bytes(...) bytes,
+ *                                 256-byte aligned (NULL allowed if that is 0)
+ *
+ * Q is the chunk length (the last chunk may be shorter: L need not be a
+ * multiple of Q).  L = 0 is allowed: y is untouched and final_state receives
+ * init_state (or zeros).  Alignment: x, Bm, Cm, y, init_state, final_state
+ * 16-byte aligned.  Limits: 1 <= P <= 256, 1 <= N <= 256, 16 <= Q <= 256
+ * (Q a multiple of 16); bf16 with (P, N) = (64, 128) and Q in {64, 128, 256}
+ * runs on MFMA, everything else on the fp32 vector path.
+ */
+int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                const void *x, const float *dt, const float *A_log,
+                const void *Bm, const void *Cm, const float *D,
+                const float *init_state, void *y, float *final_state,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssd_prefill needs for these arguments (0 if none).
+ * Returns (size_t)-1 for arguments ssd_prefill would reject. */
+size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N,
+                                   int Q, int dtype);
+
+/*
+ * ssd_decode_step -- one token of the recurrence on the O(1) cache, fused
+ * with one step of the depthwise convolution.
+ * Source: bqwf.cn article §2.1 (state of shape [H,P,N] per layer plus a
+ * (K-1)-token input window per conv channel) and §2.2 (cache update: roll
+ * the window by one and write the new token last; state = state * A_bar +
+ * B_bar * input).
+ *
+ *   x_t    [B, H*P]   dtype   this token's x (row stride in_stride)
+ *   dt_t   [B, H]     fp32    step, already positive
+ *   A_log  [H], D [H] fp32    as in ssd_prefill (D may be NULL)
+ *   B_t, C_t [B, G*N] dtype   this token's Bm / Cm (row stride in_stride)
+ *   ssm_state [B,H,P,N] fp32  read and updated in place; 16-byte aligned
+ *   y_t    [B, H, P]  dtype   output
+ *   in_stride                 elements between rows b and b+1 of x_t, B_t
+ *                             and C_t; 0 means dense (H*P and G*N).  Pass
+ *                             C = H*P + 2*G*N with x_t, B_t, C_t pointing
+ *                             into one [B, C] token row ordered x | B | C.
+ *   conv_state_in [B,C,K-1]   dtype; NULL means x_t, B_t, C_t are already
+ *                             convolved (conv arguments are then ignored).
+ *                             Otherwise x_t, B_t, C_t are the raw inputs of
+ *                             the C = H*P + 2*G*N conv channels, in the
+ *                             order x | B | C; index 0 of the window is the
+ *                             oldest token, K-2 the newest.
+ *   conv_state_out [B,C,K-1]  dtype; receives the window shifted by one with
+ *                             the raw new token last.  Must not overlap
+ *                             conv_state_in (every head reads the shared B/C
+ *                             channels of the input window while the update
+ *                             is written), so callers alternate two buffers.
+ *   conv_w [C,K] dtype, conv_b [C] dtype (NULL means 0)
+ *                             v = conv_b + sum_k conv_w[c,k] * window[k],
+ *                             window[K-1] the new token; then SiLU
+ *                             v / (1 + exp(-v)) if activation == 1.
+ *   K                         2 <= K <= 8
+ * Limits: 1 <= P <= 1024; N in {16, 32, 64, 128, 256}.
+ */
+int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
+                    const void *x_t, const float *dt_t, const float *A_log,
+                    const void *B_t, const void *C_t, const float *D,
+                    float *ssm_state, void *y_t, long in_stride,
+                    const void *conv_state_in, void *conv_state_out,
+                    const void *conv_w, const void *conv_b, int K,
+                    int activation, hipStream_t stream);
+
+/*
+ * conv_state_update -- depthwise causal convolution over T new tokens with
+ * the (K-1)-token window cache (bqwf.cn article §2.1-§2.2).  T = 1 is one
+ * decode step; T = L from a zeroed cache is the convolution of a prompt,
+ * which also leaves the cache ready for decoding.
+ *
+ *   conv_state [B,C,K-1] dtype  updated in place (index K-2 newest)
+ *   xBC   [B,T,C]  dtype        raw inputs
+ *   conv_w [C,K], conv_b [C] (NULL means 0)  dtype, as in ssd_decode_step
+ *   out   [B,T,C]  dtype        convolved (and SiLU'd if activation) values;
+ *                               NULL to update the cache only.  Must not
+ *                               overlap xBC or conv_state.
+ * T = 0 is allowed and changes nothing.  2 <= K <= 8.
+ */
+int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_state,
+                      const void *xBC, const void *conv_w, const void *conv_b,
+                      int activation, void *out, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *ssd_status_string(int status);
+
+/* hipError_t of the last failed HIP call made by this library on the
+ * calling host thread (0 if none). */
+int ssd_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSD_H */

@@ -4,12 +4,3 @@ The compute lives in a C-ABI shared library of hand-written HIP kernels for
 gfx950 (``csrc/``, declared in ``include/ssd.h``).  ``binding`` is a thin
 ctypes layer over it; ``synth`` draws seeded synthetic inputs.
 """
-__all__ = ["binding", "synth"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-
-        return binding
-    raise AttributeError(name)

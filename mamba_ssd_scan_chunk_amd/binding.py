@@ -1,0 +1,181 @@
+"""Thin ctypes binding over libssd.so (declared in include/ssd.h).
+
+Argument marshalling only: shapes are read off torch tensors, device
+pointers and the current HIP stream are passed through, and a non-zero status
+raises ``SSDError``.  Every step of the scan runs in the library's HIP
+kernels; there is no fallback of any kind.  If libssd.so is missing this
+module raises on first use: build it with
+``python -m mamba_ssd_scan_chunk_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+SSD_OK = 0
+SSD_ERR_INVALID_ARG = -1
+SSD_ERR_UNSUPPORTED = -2
+SSD_ERR_ALIGNMENT = -3
+SSD_ERR_WORKSPACE = -4
+SSD_ERR_HIP = -5
+
+# (name, restype, argtypes) of every entry point in include/ssd.h
+_i, _p, _l, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_long, ctypes.c_size_t
+SIGNATURES = {
+    "ssd_prefill": (_i, [_i] * 8 + [_p] * 10 + [_sz, _p]),
+    "ssd_prefill_workspace_bytes": (_sz, [_i] * 8),
+    "ssd_decode_step": (_i, [_i] * 6 + [_p] * 8 + [_l] + [_p] * 4 + [_i, _i, _p]),
+    "conv_state_update": (_i, [_i] * 5 + [_p] * 4 + [_i, _p, _p]),
+    "ssd_status_string": (ctypes.c_char_p, [_i]),
+    "ssd_last_hip_error": (_i, []),
+}
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().ssd_status_string(status).decode()
+        if status == SSD_ERR_HIP:
+            msg += f" (hipError_t {lib().ssd_last_hip_error()})"
+        super().__init__(f"{fn} returned {status}: {msg}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with typed entry points (raises if not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: the HIP library is not built "
+                "(python -m mamba_ssd_scan_chunk_amd.build)")
+        cdll = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(cdll, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = cdll
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(type(t))
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return t.data_ptr()
+
+
+def _dense(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn: str, rc: int):
+    if rc != SSD_OK:
+        raise SSDError(fn, rc)
+
+
+def ssd_prefill_workspace_bytes(B, L, H, P, G, N, Q, dtype) -> int:
+    n = lib().ssd_prefill_workspace_bytes(B, L, H, P, G, N, Q, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("ssd_prefill would reject these arguments")
+    return n
+
+
+def ssd_prefill(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y=None,
+                final_state=None, want_final_state=True, workspace=None, stream=None):
+    """Chunked SSD prefill.  x [B,L,H,P], dt [B,L,H] f32, A_log [H] f32,
+    Bm/Cm [B,L,G,N], D [H] f32 or None, init_state [B,H,P,N] f32 or None.
+    Returns (y, final_state)."""
+    for t, n in ((x, "x"), (dt, "dt"), (A_log, "A_log"), (Bm, "Bm"), (Cm, "Cm"), (D, "D"),
+                 (init_state, "init_state"), (y, "y"), (final_state, "final_state")):
+        _dense(t, n)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, P, N), dtype=torch.float32, device=x.device)
+    need = ssd_prefill_workspace_bytes(B, L, H, P, G, N, Q, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ssd_prefill(B, L, H, P, G, N, Q, code, _ptr(x), _ptr(dt), _ptr(A_log), _ptr(Bm),
+                           _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                           _ptr(workspace), ws_bytes, _stream(stream))
+    _check("ssd_prefill", rc)
+    return y, final_state
+
+
+def ssd_decode_step(x_t, dt_t, A_log, B_t, C_t, D, ssm_state, *, y_t=None, in_stride=0,
+                    conv_state_in=None, conv_state_out=None, conv_w=None, conv_b=None,
+                    K=4, activation=0, H=None, P=None, G=None, N=None, stream=None):
+    """One decode step, in place on ssm_state [B,H,P,N] (and conv_state_out).
+
+    x_t [B,H*P], dt_t [B,H], B_t/C_t [B,G*N] (or views into one [B,C] row with
+    ``in_stride`` = C).  Returns y_t [B,H,P]."""
+    Bsz, H_, P_, N_ = ssm_state.shape
+    H, P, N = H or H_, P or P_, N or N_
+    G = G or (B_t.shape[-1] // N if in_stride == 0 else None)
+    if G is None:
+        raise ValueError("G must be given when in_stride is set")
+    _dense(ssm_state, "ssm_state")
+    code = _dtype_code(x_t)
+    if y_t is None:
+        y_t = torch.empty((Bsz, H, P), dtype=x_t.dtype, device=x_t.device)
+    rc = lib().ssd_decode_step(Bsz, H, P, G, N, code, _ptr(x_t), _ptr(dt_t), _ptr(A_log), _ptr(B_t),
+                               _ptr(C_t), _ptr(D), _ptr(ssm_state), _ptr(y_t), int(in_stride),
+                               _ptr(conv_state_in), _ptr(conv_state_out), _ptr(conv_w), _ptr(conv_b),
+                               int(K), int(activation), _stream(stream))
+    _check("ssd_decode_step", rc)
+    return y_t
+
+
+def conv_state_update(conv_state, xBC, conv_w, conv_b=None, *, activation=0, out=None,
+                      want_out=True, stream=None):
+    """Depthwise causal conv over T tokens; conv_state [B,C,K-1] updated in
+    place.  xBC [B,T,C], conv_w [C,K].  Returns out [B,T,C] (or None)."""
+    for t, n in ((conv_state, "conv_state"), (xBC, "xBC"), (conv_w, "conv_w"), (conv_b, "conv_b"), (out, "out")):
+        _dense(t, n)
+    B, C, Km1 = conv_state.shape
+    T = xBC.shape[1]
+    code = _dtype_code(conv_state)
+    if out is None and want_out:
+        out = torch.empty_like(xBC)
+    rc = lib().conv_state_update(B, T, C, Km1 + 1, code, _ptr(conv_state), _ptr(xBC), _ptr(conv_w),
+                                 _ptr(conv_b), int(activation), _ptr(out), _stream(stream))
+    _check("conv_state_update", rc)
+    return out
+
+
+def ssd_status_string(status: int) -> str:
+    return lib().ssd_status_string(status).decode()
+
+
+def ssd_last_hip_error() -> int:
+    return lib().ssd_last_hip_error()

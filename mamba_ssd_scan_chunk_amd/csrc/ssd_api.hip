@@ -1,0 +1,244 @@
+// ssd_api.hip -- the C ABI declared in include/ssd.h: host-side argument
+// checks, workspace layout and kernel dispatch.  Every check runs before the
+// first HIP call, so a rejected call launches nothing.
+#include "../../include/ssd.h"
+
+#include <stdint.h>
+
+#include "ssd_internal.hpp"
+
+#define SSD_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return SSD_OK;
+    g_last_hip_error = (int)e;
+    return SSD_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [p, p + n) and [q, q + m) share a byte (null or empty never overlaps).
+bool overlap(const void *p, size_t n, const void *q, size_t m) {
+    if (!p || !q || n == 0 || m == 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + m && b < a + n;
+}
+
+bool valid_dtype(int d) { return d == SSD_F32 || d == SSD_BF16; }
+size_t esize(int d) { return d == SSD_BF16 ? 2 : 4; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Product of non-negative factors, or SIZE_MAX on overflow.
+size_t mul(size_t a, size_t b) {
+    if (a != 0 && b > SIZE_MAX / a) return SIZE_MAX;
+    return a * b;
+}
+
+struct PrefillShape {
+    int B, L, H, P, G, N, Q, dtype;
+};
+
+int check_prefill_shape(const PrefillShape &s) {
+    if (!valid_dtype(s.dtype)) return SSD_ERR_INVALID_ARG;
+    if (s.B < 1 || s.L < 0 || s.H < 1 || s.P < 1 || s.G < 1 || s.N < 1 || s.Q < 1) return SSD_ERR_INVALID_ARG;
+    if (s.H % s.G != 0) return SSD_ERR_INVALID_ARG;
+    if (s.P > 256 || s.N > 256 || s.Q > 256) return SSD_ERR_UNSUPPORTED;
+    if (s.B > 65535 || s.H > 65535) return SSD_ERR_UNSUPPORTED;
+    // every element index must fit comfortably in 63 bits
+    if (mul(mul(mul((size_t)s.B, (size_t)s.L + (size_t)s.Q), (size_t)s.H), (size_t)s.P * s.N) >= ((size_t)1 << 60))
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+}  // namespace
+
+namespace ssd {
+
+bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
+    return dtype == SSD_BF16 && P == 64 && N == 128 && (Q == 64 || Q == 128 || Q == 256) && false;
+}
+
+WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, bool mfma) {
+    WorkspaceLayout w{0, 0, 0, 0};
+    if (L <= 0) return w;
+    const size_t nch = ((size_t)L + Q - 1) / Q;
+    const size_t heads = (size_t)B * nch * H;
+    w.off_S = 0;
+    w.off_dec = align_up(w.off_S + heads * P * N * sizeof(float), 256);
+    w.off_cs = align_up(w.off_dec + heads * sizeof(float), 256);
+    const size_t cs_bytes = mfma ? 0 : heads * Q * sizeof(double);
+    w.total = align_up(w.off_cs + cs_bytes, 256);
+    return w;
+}
+
+}  // namespace ssd
+
+SSD_API size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N, int Q, int dtype) {
+    const PrefillShape s{B, L, H, P, G, N, Q, dtype};
+    if (check_prefill_shape(s) != SSD_OK) return (size_t)-1;
+    return ssd::prefill_workspace_layout(B, L, H, P, N, Q, ssd::prefill_uses_mfma(P, N, Q, dtype)).total;
+}
+
+SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                        const void *x, const float *dt, const float *A_log,
+                        const void *Bm, const void *Cm, const float *D,
+                        const float *init_state, void *y, float *final_state,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const PrefillShape s{B, L, H, P, G, N, Q, dtype};
+    int rc = check_prefill_shape(s);
+    if (rc != SSD_OK) return rc;
+    if (!A_log) return SSD_ERR_INVALID_ARG;
+    if (L > 0 && (!x || !dt || !Bm || !Cm || !y)) return SSD_ERR_INVALID_ARG;
+
+    const size_t es = esize(dtype);
+    const size_t n_x = (size_t)B * L * H * P, n_bc = (size_t)B * L * G * N;
+    const size_t n_dt = (size_t)B * L * H, n_state = (size_t)B * H * P * N;
+    const size_t b_x = n_x * es, b_bc = n_bc * es, b_dt = n_dt * 4, b_state = n_state * 4;
+
+    if (!aligned(x, 16) || !aligned(Bm, 16) || !aligned(Cm, 16) || !aligned(y, 16) ||
+        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(dt, 4) ||
+        !aligned(A_log, 4) || !aligned(D, 4) || !aligned(workspace, 256))
+        return SSD_ERR_ALIGNMENT;
+
+    const bool mfma = ssd::prefill_uses_mfma(P, N, Q, dtype);
+    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(B, L, H, P, N, Q, mfma);
+    const size_t b_ws = wl.total;
+
+    // outputs may not overlap inputs, workspace or each other
+    // (final_state == init_state exactly is allowed)
+    struct R { const void *p; size_t n; };
+    const R ins[] = {{x, b_x}, {dt, b_dt}, {A_log, (size_t)H * 4}, {Bm, b_bc}, {Cm, b_bc}, {D, D ? (size_t)H * 4 : 0}};
+    if (L > 0) {
+        for (const R &r : ins) if (overlap(y, b_x, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+        if (overlap(y, b_x, init_state, b_state) || overlap(y, b_x, final_state, b_state) ||
+            overlap(y, b_x, workspace, b_ws))
+            return SSD_ERR_INVALID_ARG;
+    }
+    if (final_state) {
+        for (const R &r : ins) if (overlap(final_state, b_state, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+        if (overlap(final_state, b_state, workspace, b_ws)) return SSD_ERR_INVALID_ARG;
+        if (final_state != init_state && overlap(final_state, b_state, init_state, b_state)) return SSD_ERR_INVALID_ARG;
+    }
+    if (b_ws > 0) {
+        if (!workspace || workspace_bytes < b_ws) return SSD_ERR_WORKSPACE;
+        for (const R &r : ins) if (overlap(workspace, b_ws, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+        if (overlap(workspace, b_ws, init_state, b_state)) return SSD_ERR_INVALID_ARG;
+    }
+
+    if (L == 0) {
+        if (!final_state) return SSD_OK;
+        return hip_status(ssd::launch_state_copy(init_state, final_state, n_state, stream));
+    }
+
+    ssd::PrefillArgs a;
+    a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.Q = Q;
+    a.nchunks = (L + Q - 1) / Q;
+    a.x = x; a.dt = dt; a.A_log = A_log; a.Bm = Bm; a.Cm = Cm; a.D = D;
+    a.init_state = init_state; a.y = y; a.final_state = final_state;
+    char *ws = (char *)workspace;
+    a.ws_S = (float *)(ws + wl.off_S);
+    a.ws_dec = (float *)(ws + wl.off_dec);
+    a.ws_cs = mfma ? nullptr : (double *)(ws + wl.off_cs);
+    hipError_t e = mfma ? ssd::launch_prefill_mfma(a, stream) : ssd::launch_prefill_vector(a, dtype, stream);
+    return hip_status(e);
+}
+
+SSD_API int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
+                            const void *x_t, const float *dt_t, const float *A_log,
+                            const void *B_t, const void *C_t, const float *D,
+                            float *ssm_state, void *y_t, long in_stride,
+                            const void *conv_state_in, void *conv_state_out,
+                            const void *conv_w, const void *conv_b, int K,
+                            int activation, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSD_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || P < 1 || G < 1 || N < 1 || H % G != 0 || in_stride < 0) return SSD_ERR_INVALID_ARG;
+    if (!x_t || !dt_t || !A_log || !B_t || !C_t || !ssm_state || !y_t) return SSD_ERR_INVALID_ARG;
+    if (!(N == 16 || N == 32 || N == 64 || N == 128 || N == 256) || P > 1024) return SSD_ERR_UNSUPPORTED;
+    const long HP = (long)H * P, GN = (long)G * N, C = HP + 2 * GN;
+    if (in_stride != 0 && (in_stride < HP || in_stride < GN)) return SSD_ERR_INVALID_ARG;
+    const bool conv = conv_state_in != nullptr;
+    if (conv) {
+        if (!conv_state_out || !conv_w) return SSD_ERR_INVALID_ARG;
+        if (K < 2 || K > 8 || (activation != 0 && activation != 1)) return SSD_ERR_INVALID_ARG;
+    }
+    const size_t es = esize(dtype);
+    if (!aligned(ssm_state, 16) || !aligned(x_t, es) || !aligned(B_t, es) || !aligned(C_t, es) ||
+        !aligned(y_t, es) || !aligned(dt_t, 4) || !aligned(A_log, 4) || !aligned(D, 4))
+        return SSD_ERR_ALIGNMENT;
+    if (conv && (!aligned(conv_state_in, es) || !aligned(conv_state_out, es) || !aligned(conv_w, es) ||
+                 !aligned(conv_b, es)))
+        return SSD_ERR_ALIGNMENT;
+
+    const long xs = in_stride ? in_stride : HP, bs = in_stride ? in_stride : GN;
+    const size_t b_x = ((size_t)(B - 1) * xs + HP) * es, b_bc = ((size_t)(B - 1) * bs + GN) * es;
+    const size_t b_state = (size_t)B * H * P * N * 4, b_y = (size_t)B * HP * es;
+    const size_t b_conv = conv ? (size_t)B * C * (K - 1) * es : 0;
+    struct R { const void *p; size_t n; };
+    const R ins[] = {{x_t, b_x}, {B_t, b_bc}, {C_t, b_bc}, {dt_t, (size_t)B * H * 4}, {A_log, (size_t)H * 4},
+                     {D, D ? (size_t)H * 4 : 0}, {conv_state_in, b_conv},
+                     {conv ? conv_w : nullptr, conv ? (size_t)C * K * es : 0},
+                     {conv ? conv_b : nullptr, (conv && conv_b) ? (size_t)C * es : 0}};
+    for (const R &r : ins) {
+        if (overlap(y_t, b_y, r.p, r.n) || overlap(ssm_state, b_state, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+        if (conv && overlap(conv_state_out, b_conv, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+    }
+    if (overlap(y_t, b_y, ssm_state, b_state)) return SSD_ERR_INVALID_ARG;
+    if (conv && (overlap(conv_state_out, b_conv, y_t, b_y) || overlap(conv_state_out, b_conv, ssm_state, b_state)))
+        return SSD_ERR_INVALID_ARG;
+
+    ssd::DecodeArgs a;
+    a.B = B; a.H = H; a.P = P; a.G = G; a.N = N; a.K = K; a.activation = activation;
+    a.in_stride = in_stride;
+    a.x_t = x_t; a.dt_t = dt_t; a.A_log = A_log; a.B_t = B_t; a.C_t = C_t; a.D = D;
+    a.state = ssm_state; a.y_t = y_t;
+    a.conv_in = conv ? conv_state_in : nullptr;
+    a.conv_out = conv ? conv_state_out : nullptr;
+    a.conv_w = conv ? conv_w : nullptr;
+    a.conv_b = conv ? conv_b : nullptr;
+    return hip_status(ssd::launch_decode(a, dtype, stream));
+}
+
+SSD_API int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_state,
+                              const void *xBC, const void *conv_w, const void *conv_b,
+                              int activation, void *out, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSD_ERR_INVALID_ARG;
+    if (B < 1 || T < 0 || C < 1 || K < 2 || K > 8 || (activation != 0 && activation != 1)) return SSD_ERR_INVALID_ARG;
+    if (!conv_state || !conv_w || (T > 0 && !xBC)) return SSD_ERR_INVALID_ARG;
+    if (B > 65535 || ((long)T + 15) / 16 > 65535) return SSD_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    if (!aligned(conv_state, es) || !aligned(xBC, es) || !aligned(conv_w, es) || !aligned(conv_b, es) ||
+        !aligned(out, es))
+        return SSD_ERR_ALIGNMENT;
+    const size_t b_state = (size_t)B * C * (K - 1) * es, b_x = (size_t)B * T * C * es;
+    const size_t b_w = (size_t)C * K * es, b_b = conv_b ? (size_t)C * es : 0;
+    if (overlap(conv_state, b_state, xBC, b_x) || overlap(conv_state, b_state, conv_w, b_w) ||
+        overlap(conv_state, b_state, conv_b, b_b))
+        return SSD_ERR_INVALID_ARG;
+    if (out && (overlap(out, b_x, xBC, b_x) || overlap(out, b_x, conv_state, b_state) ||
+                overlap(out, b_x, conv_w, b_w) || overlap(out, b_x, conv_b, b_b)))
+        return SSD_ERR_INVALID_ARG;
+    if (T == 0) return SSD_OK;
+    ssd::ConvArgs a;
+    a.B = B; a.T = T; a.C = C; a.K = K; a.activation = activation;
+    a.state = conv_state; a.xBC = xBC; a.w = conv_w; a.bias = conv_b; a.out = out;
+    return hip_status(ssd::launch_conv_update(a, dtype, stream));
+}
+
+SSD_API const char *ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "success";
+        case SSD_ERR_INVALID_ARG: return "invalid argument (null pointer, bad dimension, G not dividing H, bad K or overlapping buffers)";
+        case SSD_ERR_UNSUPPORTED: return "unsupported shape or dtype for this build";
+        case SSD_ERR_ALIGNMENT: return "pointer or stride breaks the required alignment";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_HIP: return "HIP call failed (see ssd_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+SSD_API int ssd_last_hip_error(void) { return g_last_hip_error; }

@@ -1,0 +1,62 @@
+// ssd_device.hpp -- device helpers shared by the SSD kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// ---------------------------------------------------------------- dtypes
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+    return __uint_as_float(((uint32_t)v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// Two floats -> packed pair of bf16 (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float ld(const T *p);
+template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t *p) { return bf16_to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ void st(T *p, float v);
+template <> __device__ __forceinline__ void st<float>(float *p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st<bf16_t>(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// ---------------------------------------------------------------- wave ops
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
+// the group receives the group total.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace ssd

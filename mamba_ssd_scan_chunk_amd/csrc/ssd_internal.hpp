@@ -1,0 +1,61 @@
+// ssd_internal.hpp -- launch interface between the C ABI layer and kernels.
+// Arguments reaching these launchers have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+struct PrefillArgs {
+    int B, L, H, P, G, N, Q, nchunks;
+    const void *x;
+    const float *dt, *A_log;
+    const void *Bm, *Cm;
+    const float *D, *init_state;
+    void *y;
+    float *final_state;
+    // workspace views
+    float *ws_S;    // [B, nchunks, H, P, N]: chunk states, then carried-in states
+    float *ws_dec;  // [B, nchunks, H]: exp(sum of dt*A over the chunk) - 1
+    double *ws_cs;  // [B, nchunks, H, Q]: in-chunk inclusive cumsum of dt*A (vector path)
+};
+
+struct WorkspaceLayout {
+    size_t off_S, off_dec, off_cs, total;
+};
+WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, bool mfma);
+bool prefill_uses_mfma(int P, int N, int Q, int dtype);
+
+hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_state_pass(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_state_copy(const float *src, float *dst, size_t n, hipStream_t s);
+
+struct DecodeArgs {
+    int B, H, P, G, N, K, activation;
+    long in_stride;
+    const void *x_t;
+    const float *dt_t, *A_log;
+    const void *B_t, *C_t;
+    const float *D;
+    float *state;
+    void *y_t;
+    const void *conv_in;
+    void *conv_out;
+    const void *conv_w, *conv_b;
+};
+hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t s);
+
+struct ConvArgs {
+    int B, T, C, K, activation;
+    void *state;
+    const void *xBC, *w, *bias;
+    void *out;
+};
+hipError_t launch_conv_update(const ConvArgs &a, int dtype, hipStream_t s);
+
+}  // namespace ssd

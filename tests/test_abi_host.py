@@ -1,0 +1,194 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+Every call here fails argument validation, which runs on the host before any
+HIP call, so nothing reaches the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mamba_ssd_scan_chunk_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from mamba_ssd_scan_chunk_amd import build
+
+        build.build(verbose=False)
+    return bd.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"}
+
+
+def test_header_declares_the_abi():
+    assert _declared_functions() == set(bd.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", bd.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert _declared_functions() <= exported
+    for name in _declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert bd.ssd_status_string(code)
+    assert bd.ssd_status_string(-99) == "unknown status"
+    assert bd.ssd_last_hip_error() == 0
+
+
+# fake, well-aligned, non-overlapping device addresses (never dereferenced)
+_BASE = 0x7F0000000000
+_STEP = 1 << 34
+
+
+def _addr(i, off=0):
+    return _BASE + i * _STEP + off
+
+
+def _prefill(lib, B=1, L=64, H=2, P=16, G=1, N=16, Q=32, dtype=0, **over):
+    ptrs = dict(x=_addr(0), dt=_addr(1), A_log=_addr(2), Bm=_addr(3), Cm=_addr(4), D=_addr(5),
+                init=_addr(6), y=_addr(7), final=_addr(8), ws=_addr(9))
+    ws_bytes = over.pop("ws_bytes", 1 << 40)
+    ptrs.update(over)
+    return lib.ssd_prefill(B, L, H, P, G, N, Q, dtype, ptrs["x"], ptrs["dt"], ptrs["A_log"], ptrs["Bm"],
+                           ptrs["Cm"], ptrs["D"], ptrs["init"], ptrs["y"], ptrs["final"], ptrs["ws"],
+                           ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=3, H=4), bd.SSD_ERR_INVALID_ARG),          # G does not divide H
+    (dict(B=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(L=-1), bd.SSD_ERR_INVALID_ARG),
+    (dict(P=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(Q=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(dtype=7), bd.SSD_ERR_INVALID_ARG),
+    (dict(x=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(dt=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(A_log=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(y=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(P=257), bd.SSD_ERR_UNSUPPORTED),
+    (dict(N=512), bd.SSD_ERR_UNSUPPORTED),
+    (dict(Q=512), bd.SSD_ERR_UNSUPPORTED),
+    (dict(x=_addr(0, 2)), bd.SSD_ERR_ALIGNMENT),
+    (dict(y=_addr(7, 8)), bd.SSD_ERR_ALIGNMENT),
+    (dict(final=_addr(8, 4)), bd.SSD_ERR_ALIGNMENT),
+    (dict(ws=_addr(9, 16)), bd.SSD_ERR_ALIGNMENT),
+    (dict(y=_addr(0, 64)), bd.SSD_ERR_INVALID_ARG),      # y overlaps x
+    (dict(final=_addr(4, 0)), bd.SSD_ERR_INVALID_ARG),   # final_state overlaps Cm
+    (dict(final=_addr(6, 16)), bd.SSD_ERR_INVALID_ARG),  # partial overlap with init_state
+    (dict(ws=_addr(3, 0)), bd.SSD_ERR_INVALID_ARG),      # workspace overlaps Bm
+    (dict(ws=None), bd.SSD_ERR_WORKSPACE),
+    (dict(ws_bytes=16), bd.SSD_ERR_WORKSPACE),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+
+
+def test_prefill_empty_sequence_without_outputs_is_a_no_op(lib):
+    # L = 0 and no final_state: nothing to do, returns before any HIP call
+    assert _prefill(lib, L=0, final=None, x=None, y=None) == bd.SSD_OK
+
+
+def test_workspace_query(lib):
+    assert lib.ssd_prefill_workspace_bytes(1, 0, 2, 16, 1, 16, 64, 0) == 0
+    n1 = lib.ssd_prefill_workspace_bytes(1, 256, 2, 16, 1, 16, 64, 0)
+    n2 = lib.ssd_prefill_workspace_bytes(1, 257, 2, 16, 1, 16, 64, 0)  # one more (ragged) chunk
+    assert 0 < n1 < n2 and n1 % 256 == 0
+    assert n1 >= 4 * 2 * 16 * 16 * 4  # at least one fp32 state per head-chunk
+    assert lib.ssd_prefill_workspace_bytes(1, 256, 3, 16, 2, 16, 64, 0) == ctypes.c_size_t(-1).value
+
+
+def _decode(lib, B=2, H=2, P=16, G=1, N=16, dtype=0, K=4, act=1, stride=0, **over):
+    p = dict(x=_addr(0), dt=_addr(1), A_log=_addr(2), Bt=_addr(3), Ct=_addr(4), D=_addr(5), state=_addr(6),
+             y=_addr(7), cin=_addr(8), cout=_addr(9), w=_addr(10), b=_addr(11))
+    p.update(over)
+    return lib.ssd_decode_step(B, H, P, G, N, dtype, p["x"], p["dt"], p["A_log"], p["Bt"], p["Ct"], p["D"],
+                               p["state"], p["y"], stride, p["cin"], p["cout"], p["w"], p["b"], K, act, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=3, H=4), bd.SSD_ERR_INVALID_ARG),
+    (dict(B=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(state=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(y=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(K=1), bd.SSD_ERR_INVALID_ARG),
+    (dict(K=9), bd.SSD_ERR_INVALID_ARG),
+    (dict(act=2), bd.SSD_ERR_INVALID_ARG),
+    (dict(cout=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(w=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(stride=-1), bd.SSD_ERR_INVALID_ARG),
+    (dict(stride=8), bd.SSD_ERR_INVALID_ARG),          # shorter than H*P
+    (dict(cout=_addr(8)), bd.SSD_ERR_INVALID_ARG),     # conv out aliases conv in
+    (dict(y=_addr(6, 64)), bd.SSD_ERR_INVALID_ARG),    # y inside the state
+    (dict(state=_addr(0, 0)), bd.SSD_ERR_INVALID_ARG),  # state overlaps x_t
+    (dict(N=48), bd.SSD_ERR_UNSUPPORTED),
+    (dict(N=512), bd.SSD_ERR_UNSUPPORTED),
+    (dict(P=2048), bd.SSD_ERR_UNSUPPORTED),
+    (dict(state=_addr(6, 4)), bd.SSD_ERR_ALIGNMENT),
+    (dict(x=_addr(0, 2)), bd.SSD_ERR_ALIGNMENT),        # fp32 element misaligned
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def _conv(lib, B=2, T=8, C=40, K=4, dtype=1, act=1, **over):
+    p = dict(state=_addr(0), x=_addr(1), w=_addr(2), b=_addr(3), out=_addr(4))
+    p.update(over)
+    return lib.conv_state_update(B, T, C, K, dtype, p["state"], p["x"], p["w"], p["b"], act, p["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=1), bd.SSD_ERR_INVALID_ARG),
+    (dict(K=9), bd.SSD_ERR_INVALID_ARG),
+    (dict(T=-1), bd.SSD_ERR_INVALID_ARG),
+    (dict(C=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(dtype=3), bd.SSD_ERR_INVALID_ARG),
+    (dict(act=5), bd.SSD_ERR_INVALID_ARG),
+    (dict(state=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(w=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(x=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(out=_addr(1, 32)), bd.SSD_ERR_INVALID_ARG),   # out overlaps xBC
+    (dict(state=_addr(1, 0)), bd.SSD_ERR_INVALID_ARG),  # cache overlaps xBC
+    (dict(T=65536 * 16), bd.SSD_ERR_UNSUPPORTED),
+    (dict(state=_addr(0, 1)), bd.SSD_ERR_ALIGNMENT),
+])
+def test_conv_rejects(lib, kw, code):
+    assert _conv(lib, **kw) == code
+
+
+def test_conv_zero_tokens_is_a_no_op(lib):
+    assert _conv(lib, T=0, x=None) == bd.SSD_OK
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        bd.ssd_prefill(x, torch.zeros(1, 4, 1), torch.zeros(1), torch.zeros(1, 4, 1, 16),
+                       torch.zeros(1, 4, 1, 16), Q=16)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package and its sources never import or link the oracle."""
+    pkg = os.path.join(ROOT, "mamba_ssd_scan_chunk_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "ssd_oracle" not in text, f

@@ -1,0 +1,160 @@
+"""GPU parity of ssd_prefill against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from mamba_ssd_scan_chunk_amd import binding as bd
+from mamba_ssd_scan_chunk_amd import synth
+from tests.gpu_utils import TOL_BF16, TOL_F32, announce, dev, f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(dtype):
+    return TOL_F32 if dtype == "f32" else TOL_BF16
+
+
+def _run(d, Q, init=None, **kw):
+    dd = dev(d)
+    y, fs = bd.ssd_prefill(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"],
+                           None if init is None else init.cuda(), Q=Q, **kw)
+    torch.cuda.synchronize()
+    return y, fs
+
+
+CASES = [
+    # name, B, L, H, P, G, N, Q, dtype
+    ("ssd-f32-tiny", 1, 256, 2, 16, 1, 16, 64, "f32"),
+    ("ragged", 2, 200, 3, 16, 1, 16, 64, "f32"),
+    ("q16", 1, 100, 2, 16, 1, 16, 16, "f32"),
+    ("q32-groups", 2, 130, 4, 8, 2, 32, 32, "f32"),
+    ("odd-dims", 1, 77, 3, 3, 3, 5, 24, "f32"),
+    ("one-token", 2, 1, 2, 16, 1, 16, 64, "f32"),
+    ("q-eq-l", 1, 64, 2, 16, 1, 16, 64, "f32"),
+    ("bf16-small", 1, 300, 4, 32, 1, 64, 32, "bf16"),
+    ("bf16-q256-ragged", 1, 700, 2, 64, 1, 128, 256, "bf16"),
+    ("bf16-q128", 2, 384, 3, 64, 1, 128, 128, "bf16"),
+    ("bf16-q64-groups", 1, 333, 4, 64, 2, 128, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("variant", ["spec", "d0", "slow"])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_prefill_matches_oracle(oracle, case, variant, with_init):
+    name, B, L, H, P, G, N, Q, dtype = case
+    d = synth.make_prefill(B, L, H, P, G, N, dtype, seed=100 + [c[0] for c in CASES].index(name), variant=variant)
+    init = synth.make_state(B, H, P, N, seed=5, scale=0.5) if with_init else None
+    announce("prefill", name, variant, with_init)
+    y, fs = _run(d, Q, init)
+    y_ref, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], init)
+    assert rel_err(y, y_ref) <= _tol(dtype)
+    assert rel_err(fs, fs_ref) <= _tol(dtype)
+
+
+@pytest.mark.parametrize("with_init", [False, True])
+def test_prefill_empty_sequence(with_init):
+    B, H, P, N = 2, 3, 16, 16
+    init = synth.make_state(B, H, P, N, seed=1).cuda() if with_init else None
+    x = torch.empty((B, 0, H, P), device="cuda")
+    Bm = torch.empty((B, 0, 1, N), device="cuda")
+    announce("prefill L=0", with_init)
+    y, fs = bd.ssd_prefill(x, torch.empty((B, 0, H), device="cuda"), torch.zeros(H, device="cuda"), Bm, Bm,
+                           None, init, Q=64, final_state=torch.full((B, H, P, N), 7.0, device="cuda"))
+    torch.cuda.synchronize()
+    if with_init:
+        assert torch.equal(fs, init)
+    else:
+        assert torch.count_nonzero(fs) == 0
+
+
+def test_final_state_may_alias_init_state(oracle):
+    d = synth.make_prefill(1, 150, 2, 16, 1, 16, "f32", seed=3)
+    init = synth.make_state(1, 2, 16, 16, seed=4)
+    st = init.clone().cuda()
+    dd = dev(d)
+    announce("prefill alias")
+    bd.ssd_prefill(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], st, Q=64, final_state=st)
+    torch.cuda.synchronize()
+    _, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], init)
+    assert rel_err(st, fs_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype,P,N,Q", [("f32", 16, 16, 64), ("bf16", 64, 128, 256)])
+def test_prefill_is_deterministic(dtype, P, N, Q):
+    d = synth.make_prefill(1, 1000, 4, P, 1, N, dtype, seed=9)
+    announce("prefill determinism", dtype)
+    y1, f1 = _run(d, Q)
+    y2, f2 = _run(d, Q)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype,P,N,Q", [("f32", 16, 16, 64), ("bf16", 64, 128, 256)])
+def test_split_prefill_equals_one_prefill(oracle, dtype, P, N, Q):
+    B, L1, L2, H = 1, 300, 213, 3
+    d = synth.make_prefill(B, L1 + L2, H, P, 1, N, dtype, seed=10, variant="slow")
+    announce("split prefill", dtype)
+    y, fs = _run(d, Q)
+    first = {k: (v[:, :L1].contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+    second = {k: (v[:, L1:].contiguous() if v.dim() > 1 else v) for k, v in d.items()}
+    y1, f1 = _run(first, Q)
+    y2, f2 = _run(second, Q, init=f1.cpu())
+    y_ref, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"])
+    assert rel_err(torch.cat([y1, y2], 1), y_ref) <= _tol(dtype)
+    assert rel_err(f2, fs_ref) <= _tol(dtype)
+    assert rel_err(torch.cat([y1, y2], 1), y) <= 2 * _tol(dtype)
+
+
+@pytest.mark.parametrize("dtype,P,N,Q", [("f32", 16, 16, 64), ("bf16", 64, 128, 256)])
+def test_prefill_then_decode_equals_longer_prefill(oracle, dtype, P, N, Q):
+    """prefill(L) then k decode steps gives the outputs and state of
+    prefill(L + k)."""
+    B, L, k, H, G = 2, 520, 24, 4, 1
+    d = synth.make_prefill(B, L + k, H, P, G, N, dtype, seed=11)
+    dd = dev(d)
+    announce("prefill+decode", dtype)
+    y_long, fs_long = bd.ssd_prefill(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], Q=Q)
+    head = {kk: (v[:, :L].contiguous() if v.dim() > 1 else v) for kk, v in dd.items()}
+    _, state = bd.ssd_prefill(head["x"], head["dt"], head["A_log"], head["Bm"], head["Cm"], head["D"], Q=Q)
+    ys = []
+    for t in range(L, L + k):
+        ys.append(bd.ssd_decode_step(dd["x"][:, t].reshape(B, H * P).contiguous(), dd["dt"][:, t].contiguous(),
+                                     dd["A_log"], dd["Bm"][:, t].reshape(B, G * N).contiguous(),
+                                     dd["Cm"][:, t].reshape(B, G * N).contiguous(), dd["D"], state))
+    torch.cuda.synchronize()
+    y_ref, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"])
+    y_dec = torch.stack(ys, 1)
+    assert rel_err(y_dec, y_ref[:, L:]) <= _tol(dtype)
+    assert rel_err(y_long[:, L:], y_ref[:, L:]) <= _tol(dtype)
+    assert rel_err(state, fs_ref) <= _tol(dtype)
+    assert rel_err(fs_long, fs_ref) <= _tol(dtype)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mamba2-130m-prefill", "mamba2-2.7b-prefill"])
+@pytest.mark.parametrize("variant", ["spec", "d0", "slow"])
+def test_full_size_prefill_matches_oracle(oracle, name, variant):
+    """Whole outputs of the 130M- and 2.7B-shaped layers (L=4096, Q=256)."""
+    w = synth.WORKLOADS[name]
+    d = synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, w.dtype, seed=1, variant=variant)
+    announce("full prefill", name, variant)
+    y, fs = _run(d, w.Q)
+    y_ref, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"])
+    assert rel_err(y, y_ref) <= TOL_BF16
+    assert rel_err(fs, fs_ref) <= TOL_BF16
+
+
+@pytest.mark.slow
+def test_long_context_prefill_sampled_heads(oracle):
+    """B=8, L=16384 2.7B-shaped layer: whole-run GPU outputs checked on
+    sampled (batch, head) pairs, each replayed by the oracle in full."""
+    w = synth.WORKLOADS["mamba2-2.7b-longctx"]
+    d = synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, w.dtype, seed=4)
+    announce("longctx prefill")
+    y, fs = _run(d, w.Q)
+    for b, h in [(0, 0), (3, 41), (7, 79)]:
+        sub = dict(x=d["x"][b:b + 1, :, h:h + 1], dt=d["dt"][b:b + 1, :, h:h + 1], A_log=d["A_log"][h:h + 1],
+                   Bm=d["Bm"][b:b + 1], Cm=d["Cm"][b:b + 1], D=d["D"][h:h + 1])
+        y_ref, fs_ref = oracle.ssd_scan(**sub)
+        assert rel_err(y[b:b + 1, :, h:h + 1], y_ref) <= TOL_BF16, (b, h)
+        assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
