@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X SSD scan: prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one ssd_prefill call over the 2.7B-shaped Mamba-2 layer
+(B=1, L=4096, H=80, P=64, N=128, G=1, Q=256, bf16 x/Bm/Cm, fp32 dt/A/state):
+every stage of the chunked scan (in-chunk cumsum and decay, intra-chunk
+C*B^T (.) decay * X, chunk states, the chunk-to-chunk state pass, C*h + D*x).
+``value`` is prefill tokens/s.  In the same run, and reported beside it:
+  * decode: 4096 consecutive fused decode steps (conv window + state update +
+    readout) of the 2.7B-shaped layer at B=16 (conv C=5376, K=4), on one state
+    as specified, and again over rotated state buffers larger than the
+    256 MB Infinity Cache (the HBM-honest figure);
+  * conv: conv_state_update over the 4096-token prompt (C=5376);
+  * cpu_baseline: the CPU oracle on the same prefill workload.
+Inputs are seeded synthetic tensors (mamba_ssd_scan_chunk_amd.synth), resident
+in device memory before timing starts.  GPU times come from HIP events on the
+stream the kernels run on, with the queue pre-filled behind a short GPU sleep
+so that host launch overhead is not timed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def prefill_flops(B, L, H, P, G, N, Q):
+    """Algorithmic flops of the causal chunked scan (C*B^T once per
+    (batch, chunk, group); per (batch, chunk, head): masked M*X, chunk state,
+    C*h and the state pass)."""
+    total = 0
+    for c0 in range(0, L, Q):
+        q = min(Q, L - c0)
+        total += G * N * q * (q + 1) + H * (P * q * (q + 1) + 4 * q * N * P + 2 * P * N)
+    return B * total
+
+
+def prefill_bytes(B, L, H, P, G, N, esize=2):
+    return (2 * B * L * H * P * esize + 4 * B * L * H + 2 * B * L * G * N * esize
+            + 4 * B * H * P * N + 8 * H)
+
+
+def decode_bytes(B, H, P, G, N, K, esize=2):
+    C = H * P + 2 * G * N
+    return (8 * B * H * P * N + 2 * B * C * (K - 1) * esize + B * C * esize + 4 * B * H
+            + C * K * esize + B * H * P * esize + 8 * H)
+
+
+def _src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_tag):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, or None if absent or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != _src_hash(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+HOST_BOUND = []
+
+
+def _timed(fn, steps, warmup, name):
+    """GPU ms per call over ``steps`` back-to-back calls.  A GPU sleep sized
+    to the measured host enqueue time keeps the device busy until the whole
+    sequence is queued, so host launch overhead stays out of the figure."""
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(min(steps, 64)):
+        fn(i)
+    per_call = (time.perf_counter() - t0) / min(steps, 64)
+    torch.cuda.synchronize()
+    # calibrate the sleep kernel's clock
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    torch.cuda._sleep(1_000_000)
+    s1.record()
+    torch.cuda.synchronize()
+    cyc_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
+    sleep_ms = 1.5 * per_call * steps * 1e3 + 5.0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(sleep_ms * cyc_per_ms))
+    start.record()
+    h0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    host_ms = (time.perf_counter() - h0) * 1e3
+    end.record()
+    torch.cuda.synchronize()
+    gpu_ms = start.elapsed_time(end)
+    if host_ms > sleep_ms:
+        HOST_BOUND.append(name)
+    return gpu_ms / steps
+
+
+def bench_prefill(args):
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    d = {k: v.cuda() for k, v in synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, w.dtype, seed=2).items()}
+    y = torch.empty_like(d["x"])
+    fs = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+    code = bd.SSD_BF16 if w.dtype == "bf16" else bd.SSD_F32
+    ws = torch.empty(max(1, bd.ssd_prefill_workspace_bytes(w.B, w.L, w.H, w.P, w.G, w.N, w.Q, code)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(_):
+        bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], None, Q=w.Q, y=y,
+                       final_state=fs, workspace=ws)
+
+    ms = _timed(step, args.steps, args.warmup, "prefill")
+    flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
+    nbytes = prefill_bytes(w.B, w.L, w.H, w.P, w.G, w.N, 2 if w.dtype == "bf16" else 4)
+    return w, ms, flops, nbytes
+
+
+def bench_decode(args, rotate):
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.decode_workload]
+    B, H, P, G, N, K, C = w.B, w.H, w.P, w.G, w.N, w.K, w.conv_channels
+    steps = args.decode_steps
+    tdt = synth.torch_dtype(w.dtype)
+    # the cache a 4096-token prefill leaves, produced by this library
+    pre = {k: v.cuda() for k, v in synth.make_prefill(B, w.L, H, P, G, N, w.dtype, seed=3).items()}
+    _, state = bd.ssd_prefill(pre["x"], pre["dt"], pre["A_log"], pre["Bm"], pre["Cm"], pre["D"], Q=w.Q)
+    A_log, D = pre["A_log"], pre["D"]
+    del pre
+    xbc, dts = synth.make_decode_stream(steps, B, H, P, G, N, w.dtype, seed=4)
+    xbc, dts = xbc.cuda(), dts.cuda()
+    cw, _ = synth.make_conv(C, K, w.dtype, seed=5)
+    cw = cw.cuda()
+    conv = [torch.zeros((B, C, K - 1), dtype=tdt, device="cuda") for _ in range(2)]
+    y = torch.empty((B, H, P), dtype=tdt, device="cuda")
+    nrot = 1
+    states = [state]
+    if rotate:
+        # distinct states whose total exceeds the 256 MB Infinity Cache
+        nrot = max(2, -(-600 * 2**20 // state.numel() // 4))
+        states = [state.clone() for _ in range(nrot)]
+    HP, GN = H * P, G * N
+
+    def step(i):
+        row = xbc[i % steps]
+        bd.ssd_decode_step(row[:, :HP], dts[i % steps], A_log, row[:, HP:HP + GN], row[:, HP + GN:], D,
+                           states[i % nrot], y_t=y, in_stride=C, G=G, conv_state_in=conv[i & 1],
+                           conv_state_out=conv[(i + 1) & 1], conv_w=cw, K=K, activation=1)
+
+    ms = _timed(step, steps, min(args.warmup, 8), "decode")
+    return w, ms, decode_bytes(B, H, P, G, N, K, 2 if w.dtype == "bf16" else 4), nrot
+
+
+def bench_conv(args):
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    C, K = w.conv_channels, w.K
+    xbc = synth.make_tokens(w.B, w.L, C, w.dtype, seed=6).cuda()
+    cw, _ = synth.make_conv(C, K, w.dtype, seed=7)
+    cw = cw.cuda()
+    st = torch.zeros((w.B, C, K - 1), dtype=xbc.dtype, device="cuda")
+    out = torch.empty_like(xbc)
+
+    def step(_):
+        bd.conv_state_update(st, xbc, cw, activation=1, out=out)
+
+    ms = _timed(step, args.steps, args.warmup, "conv")
+    es = xbc.element_size()
+    nbytes = 2 * w.B * w.L * C * es + 2 * w.B * C * (K - 1) * es + C * K * es
+    return ms, nbytes
+
+
+def cpu_baseline(args):
+    import oracle
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    d = synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, w.dtype, seed=2)
+    oracle.build()
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ssd_scan(**d, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or reps >= 100:
+            break
+    return dict(value=round(reps * w.B * w.L / el, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"whole {w.name} prefill (B={w.B}, L={w.L}, H={w.H}, P={w.P}, N={w.N}) "
+                       f"run {reps} times in {el:.1f} s, fp64, one thread per (batch, head) share")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2-2.7b-prefill")
+    ap.add_argument("--decode-workload", default="mamba2-2.7b-decode-b16")
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="skip the decode and conv legs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; the scan "
+              "shards over (batch, head) with no communication, so N GPUs run N independent copies",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    w, ms, flops, nbytes = bench_prefill(args)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "SSD prefill tokens/s + TFLOPS (% MFMA peak); decode step GB/s (% HBM peak)",
+        "value": round(w.B * w.L / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.P,
+                   "state_dim": w.N, "groups": w.G, "chunk": w.Q, "parallelism": "single-gpu"},
+        "prefill": {"tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                    "algorithmic_gflop": round(flops / 1e9, 3), "compulsory_mb": round(nbytes / 1e6, 2),
+                    "gbs_compulsory": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "attainable_frac": round(tflops / min(PEAK_BF16_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
+                     "kernel": "ssd_prefill (all stages of one call)"},
+    }
+    if not args.prefill_only:
+        dw, dms, dbytes, _ = bench_decode(args, rotate=False)
+        _, rms, _, nrot = bench_decode(args, rotate=True)
+        gbs, rgbs = dbytes / (dms * 1e-3) / 1e9, dbytes / (rms * 1e-3) / 1e9
+        out["decode"] = {"workload": dw.name, "batch": dw.B, "steps": args.decode_steps,
+                         "us_per_step": round(dms * 1e3, 3), "steps_per_s": round(1e3 / dms, 1),
+                         "gbs": round(gbs, 1), "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "bytes_per_step": dbytes,
+                         "rotated": {"states": nrot, "us_per_step": round(rms * 1e3, 3), "gbs": round(rgbs, 1),
+                                     "hbm_peak_frac": round(rgbs / PEAK_HBM_GBS, 4)}}
+        out["roofline_decode"] = {"bound": "hbm", "achieved": round(rgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(rgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
+                                  "kernel": "ssd_decode_step (rotated states)"}
+        cms, cbytes = bench_conv(args)
+        out["conv"] = {"tokens": w.L, "channels": w.conv_channels, "us": round(cms * 1e3, 3),
+                       "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1)}
+    if HOST_BOUND:
+        out["host_bound_legs"] = HOST_BOUND
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
