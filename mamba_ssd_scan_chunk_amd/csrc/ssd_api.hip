@@ -49,6 +49,8 @@ int check_prefill_shape(const PrefillShape &s) {
     if (s.H % s.G != 0) return SSD_ERR_INVALID_ARG;
     if (s.P > 256 || s.N > 256 || s.Q > 256) return SSD_ERR_UNSUPPORTED;
     if (s.B > 65535 || s.H > 65535) return SSD_ERR_UNSUPPORTED;
+    // in-chunk row offsets are 32-bit: Q * H * P and Q * G * N below 2^31
+    if ((long)s.Q * s.H * s.P >= (1L << 31) || (long)s.Q * s.G * s.N >= (1L << 31)) return SSD_ERR_UNSUPPORTED;
     // every element index must fit comfortably in 63 bits
     if (mul(mul(mul((size_t)s.B, (size_t)s.L + (size_t)s.Q), (size_t)s.H), (size_t)s.P * s.N) >= ((size_t)1 << 60))
         return SSD_ERR_UNSUPPORTED;
@@ -60,19 +62,26 @@ int check_prefill_shape(const PrefillShape &s) {
 namespace ssd {
 
 bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
-    return dtype == SSD_BF16 && P == 64 && N == 128 && (Q == 64 || Q == 128 || Q == 256) && false;
+    return dtype == SSD_BF16 && P == 64 && N == 128 && Q == 256;
 }
 
-WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, bool mfma) {
-    WorkspaceLayout w{0, 0, 0, 0};
+WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, int G, bool mfma) {
+    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0};
     if (L <= 0) return w;
     const size_t nch = ((size_t)L + Q - 1) / Q;
     const size_t heads = (size_t)B * nch * H;
+    const size_t groups = (size_t)B * nch * G;
     w.off_S = 0;
     w.off_dec = align_up(w.off_S + heads * P * N * sizeof(float), 256);
     w.off_cs = align_up(w.off_dec + heads * sizeof(float), 256);
     const size_t cs_bytes = mfma ? 0 : heads * Q * sizeof(double);
-    w.total = align_up(w.off_cs + cs_bytes, 256);
+    w.off_hb = align_up(w.off_cs + cs_bytes, 256);
+    const size_t hb_bytes = mfma ? heads * P * N * sizeof(uint16_t) : 0;
+    w.off_gt = align_up(w.off_hb + hb_bytes, 256);
+    const size_t gt_bytes = mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t) : 0;
+    w.off_bt = align_up(w.off_gt + gt_bytes, 256);
+    const size_t bt_bytes = mfma ? groups * prefill_mfma_bt_elems_per_chunk() * sizeof(uint16_t) : 0;
+    w.total = align_up(w.off_bt + bt_bytes, 256);
     return w;
 }
 
@@ -81,7 +90,7 @@ WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int 
 SSD_API size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N, int Q, int dtype) {
     const PrefillShape s{B, L, H, P, G, N, Q, dtype};
     if (check_prefill_shape(s) != SSD_OK) return (size_t)-1;
-    return ssd::prefill_workspace_layout(B, L, H, P, N, Q, ssd::prefill_uses_mfma(P, N, Q, dtype)).total;
+    return ssd::prefill_workspace_layout(B, L, H, P, N, Q, G, ssd::prefill_uses_mfma(P, N, Q, dtype)).total;
 }
 
 SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
@@ -106,7 +115,7 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
         return SSD_ERR_ALIGNMENT;
 
     const bool mfma = ssd::prefill_uses_mfma(P, N, Q, dtype);
-    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(B, L, H, P, N, Q, mfma);
+    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(B, L, H, P, N, Q, G, mfma);
     const size_t b_ws = wl.total;
 
     // outputs may not overlap inputs, workspace or each other
@@ -144,6 +153,9 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
     a.ws_S = (float *)(ws + wl.off_S);
     a.ws_dec = (float *)(ws + wl.off_dec);
     a.ws_cs = mfma ? nullptr : (double *)(ws + wl.off_cs);
+    a.ws_hb = mfma ? (uint16_t *)(ws + wl.off_hb) : nullptr;
+    a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
+    a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     hipError_t e = mfma ? ssd::launch_prefill_mfma(a, stream) : ssd::launch_prefill_vector(a, dtype, stream);
     return hip_status(e);
 }

@@ -22,12 +22,17 @@ struct PrefillArgs {
     float *ws_S;    // [B, nchunks, H, P, N]: chunk states, then carried-in states
     float *ws_dec;  // [B, nchunks, H]: exp(sum of dt*A over the chunk) - 1
     double *ws_cs;  // [B, nchunks, H, Q]: in-chunk inclusive cumsum of dt*A (vector path)
+    uint16_t *ws_hb;  // [B, nchunks, H, P, N] bf16: carried-in states (MFMA path)
+    uint16_t *ws_gt;  // [B, nchunks, G, tiles, lanes, 16] bf16: masked C B^T (MFMA path)
+    uint16_t *ws_bt;  // [B, nchunks, G, Q*N] bf16: B in MFMA operand order (MFMA path)
 };
 
 struct WorkspaceLayout {
-    size_t off_S, off_dec, off_cs, total;
+    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, total;
 };
-WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, bool mfma);
+long prefill_mfma_gt_elems_per_chunk();
+long prefill_mfma_bt_elems_per_chunk();
+WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, int G, bool mfma);
 bool prefill_uses_mfma(int P, int N, int Q, int dtype);
 
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s);
