@@ -11,7 +11,8 @@ C*B^T (.) decay * X, chunk states, the chunk-to-chunk state pass, C*h + D*x).
   * decode: 4096 consecutive fused decode steps (conv window + state update +
     readout) of the 2.7B-shaped layer at B=16 (conv C=5376, K=4), on one state
     as specified, and again over rotated state buffers larger than the
-    256 MB Infinity Cache (the HBM-honest figure);
+    256 MB Infinity Cache (the HBM-honest figure); each both as eager launches
+    and as one HIP graph holding all 4096 steps (the on-device decode loop);
   * conv: conv_state_update over the 4096-token prompt (C=5376);
   * cpu_baseline: the CPU oracle on the same prefill workload.
 Inputs are seeded synthetic tensors (mamba_ssd_scan_chunk_amd.synth), resident
@@ -177,8 +178,38 @@ def bench_decode(args, rotate):
                            states[i % nrot], y_t=y, in_stride=C, G=G, conv_state_in=conv[i & 1],
                            conv_state_out=conv[(i + 1) & 1], conv_w=cw, K=K, activation=1)
 
-    ms = _timed(step, steps, min(args.warmup, 8), "decode")
-    return w, ms, decode_bytes(B, H, P, G, N, K, 2 if w.dtype == "bf16" else 4), nrot
+    eager_ms = _timed(step, steps, min(args.warmup, 8), "decode")
+    graph_ms = _graph_timed(step, steps)
+    return w, eager_ms, graph_ms, decode_bytes(B, H, P, G, N, K, 2 if w.dtype == "bf16" else 4), nrot
+
+
+def _graph_timed(fn, steps, reps=3):
+    """GPU ms per step with all ``steps`` steps captured in one HIP graph
+    (the on-device decode loop: no host work between steps); best of
+    ``reps`` replays."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        best = min(best, start.elapsed_time(end))
+    del g
+    return best / steps
 
 
 def bench_conv(args):
@@ -235,6 +266,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode and conv legs")
+    ap.add_argument("--legs", default="prefill,decode,conv",
+                    help="comma-separated subset of prefill,decode,conv (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; the scan "
@@ -249,9 +282,28 @@ def main():
         return 1
     torch.cuda.set_device(0)
 
+    legs = set(args.legs.split(","))
+    if args.prefill_only:
+        legs = {"prefill"}
+    out = {}
+    if "prefill" in legs:
+        out.update(prefill_record(args))
+    if "decode" in legs:
+        out.update(decode_record(args))
+    if "conv" in legs:
+        out.update(conv_record(args))
+    if HOST_BOUND:
+        out["host_bound_legs"] = HOST_BOUND
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def prefill_record(args):
     w, ms, flops, nbytes = bench_prefill(args)
     tflops = flops / (ms * 1e-3) / 1e12
-    out = {
+    return {
         "metric": "SSD prefill tokens/s + TFLOPS (% MFMA peak); decode step GB/s (% HBM peak)",
         "value": round(w.B * w.L / (ms * 1e-3), 1),
         "unit": "tokens/s",
@@ -274,28 +326,33 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "ssd_prefill (all stages of one call)"},
     }
-    if not args.prefill_only:
-        dw, dms, dbytes, _ = bench_decode(args, rotate=False)
-        _, rms, _, nrot = bench_decode(args, rotate=True)
-        gbs, rgbs = dbytes / (dms * 1e-3) / 1e9, dbytes / (rms * 1e-3) / 1e9
-        out["decode"] = {"workload": dw.name, "batch": dw.B, "steps": args.decode_steps,
-                         "us_per_step": round(dms * 1e3, 3), "steps_per_s": round(1e3 / dms, 1),
-                         "gbs": round(gbs, 1), "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "bytes_per_step": dbytes,
-                         "rotated": {"states": nrot, "us_per_step": round(rms * 1e3, 3), "gbs": round(rgbs, 1),
-                                     "hbm_peak_frac": round(rgbs / PEAK_HBM_GBS, 4)}}
-        out["roofline_decode"] = {"bound": "hbm", "achieved": round(rgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(rgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
-                                  "kernel": "ssd_decode_step (rotated states)"}
-        cms, cbytes = bench_conv(args)
-        out["conv"] = {"tokens": w.L, "channels": w.conv_channels, "us": round(cms * 1e3, 3),
-                       "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1)}
-    if HOST_BOUND:
-        out["host_bound_legs"] = HOST_BOUND
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args)
-    print(json.dumps(out), flush=True)
-    return 0
+
+
+def decode_record(args):
+    dw, dms, gms, dbytes, _ = bench_decode(args, rotate=False)
+    _, rms, rgms, _, nrot = bench_decode(args, rotate=True)
+    gbs = lambda ms: dbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    return {
+        "decode": {"workload": dw.name, "batch": dw.B, "steps": args.decode_steps, "bytes_per_step": dbytes,
+                   "graph": {"us_per_step": round(gms * 1e3, 3), "steps_per_s": round(1e3 / gms, 1),
+                             "gbs": round(gbs(gms), 1), "hbm_peak_frac": round(gbs(gms) / PEAK_HBM_GBS, 4)},
+                   "eager": {"us_per_step": round(dms * 1e3, 3), "gbs": round(gbs(dms), 1)},
+                   "rotated": {"states": nrot, "graph_us_per_step": round(rgms * 1e3, 3),
+                               "graph_gbs": round(gbs(rgms), 1), "hbm_peak_frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
+                               "eager_us_per_step": round(rms * 1e3, 3)}},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs(rgms), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
+                            "kernel": "ssd_decode_step, rotated states, 4096 steps in one HIP graph"},
+    }
+
+
+def conv_record(args):
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    cms, cbytes = bench_conv(args)
+    return {"conv": {"tokens": w.L, "channels": w.conv_channels, "us": round(cms * 1e3, 3),
+                     "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1)}}
 
 
 if __name__ == "__main__":

@@ -26,83 +26,102 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxK = 8;
 
-template <int N>
+template <int N, int RPT>
 struct DecodeShape {
     static constexpr int LPR = N / 4;                  // lanes per state row
     static constexpr int ROWS_PER_PASS = kThreads / LPR;
-    static constexpr int PBLK = ROWS_PER_PASS >= 16 ? ROWS_PER_PASS : 16;
-    static constexpr int RPT = PBLK / ROWS_PER_PASS;   // rows per thread
+    static constexpr int PBLK = ROWS_PER_PASS * RPT;   // state rows per workgroup
 };
 
-template <typename T, int N, bool CONV>
+// Convolved value of conv channel `cidx` at this step (raw input `raw`); the
+// shifted window goes to conv_out when `write_out`.
+template <typename T, bool CONV>
+__device__ __forceinline__ float conv_channel(const DecodeArgs &a, long C, int b, long cidx, float raw, bool write_out) {
+    if (!CONV) return raw;
+    const int K = a.K;
+    const T *cin = (const T *)a.conv_in + ((long)b * C + cidx) * (K - 1);
+    const T *w = (const T *)a.conv_w + cidx * K;
+    float win[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) win[k] = (k < K - 1) ? ld(cin + k) : (k == K - 1 ? raw : 0.0f);
+    float acc = a.conv_b ? ld((const T *)a.conv_b + cidx) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+        if (k < K) acc = fmaf(ld(w + k), win[k], acc);
+    if (write_out) {
+        T *cout = (T *)a.conv_out + ((long)b * C + cidx) * (K - 1);
+#pragma unroll
+        for (int k = 0; k < kMaxK - 1; ++k)
+            if (k < K - 1) st(cout + k, win[k + 1]);
+    }
+    return a.activation ? silu(acc) : acc;
+}
+
+// One workgroup per block of PBLK consecutive state rows of one (batch,
+// group): rows are the flattened (head, p) pairs of the group, contiguous in
+// the state, x and y, so a block may cover several heads and the 2N B/C
+// channels of the group are convolved once per block.  The state loads are
+// issued first so their HBM latency overlaps the convolution stage.
+template <typename T, int N, bool CONV, int RPT>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
-    using S = DecodeShape<N>;
+    using S = DecodeShape<N, RPT>;
     __shared__ float xs[S::PBLK];
     __shared__ float Bs[N];
     __shared__ float Cs[N];
+    __shared__ float hdt[S::PBLK], hdm1[S::PBLK], hD[S::PBLK];  // per head of the block
 
-    const int npb = (a.P + S::PBLK - 1) / S::PBLK;
-    int bid = blockIdx.x;
-    const int pb = bid % npb;
-    bid /= npb;
-    const int h = bid % a.H;
-    const int b = bid / a.H;
-    const int hpg = a.H / a.G;
-    const int g = h / hpg;
-    const int P = a.P;
-    const int p0 = pb * S::PBLK;
-    const int prows = min(S::PBLK, P - p0);
-    const long HP = (long)a.H * P, GN = (long)a.G * N;
+    const int P = a.P, H = a.H;
+    const int hpg = H / a.G;
+    const int GR = hpg * P;                      // state rows per (batch, group)
+    const int npb = (GR + S::PBLK - 1) / S::PBLK;
+    const int pb = blockIdx.x % npb;
+    const long bg = blockIdx.x / npb;            // b * G + g
+    const int g = (int)(bg % a.G);
+    const int b = (int)(bg / a.G);
+    const int r0 = pb * S::PBLK;                 // first row within the group
+    const int prows = min(S::PBLK, GR - r0);
+    const long HP = (long)H * P, GN = (long)a.G * N, C = HP + 2 * GN;
     const long xstride = a.in_stride ? a.in_stride : HP;
     const long bcstride = a.in_stride ? a.in_stride : GN;
-    const T *xin = (const T *)a.x_t + b * xstride + (long)h * P + p0;
+    const long row_base = (long)b * HP + (long)g * GR + r0;  // row index in [B*H*P)
+    const int lr = threadIdx.x % S::LPR;
+    const int row0 = threadIdx.x / S::LPR;
+    const int n0 = lr * 4;
+
+    float *sbase = a.state + row_base * N + n0;
+    float4 hv[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int pr = row0 + r * S::ROWS_PER_PASS;
+        hv[r] = pr < prows ? *(const float4 *)(sbase + (long)pr * N) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // ---- per-head step constants, this block's x channels and the 2N B/C
+    //      channels of its group
+    const int hfirst = g * hpg + r0 / P;  // first head of the block
+    const int nheads = (r0 + prows - 1) / P - r0 / P + 1;
+    for (int i = threadIdx.x; i < nheads; i += kThreads) {
+        const int h = hfirst + i;
+        const float dtv = a.dt_t[(long)b * H + h];
+        hdt[i] = dtv;
+        hdm1[i] = expm1f(dtv * -expf(a.A_log[h]));
+        hD[i] = a.D ? a.D[h] : 0.0f;
+    }
+    const bool bc_writer = pb == 0;
+    const long xch0 = (long)g * GR + r0;  // conv channel of the block's first row
+    const T *xin = (const T *)a.x_t + b * xstride + xch0;
     const T *Bin = (const T *)a.B_t + b * bcstride + (long)g * N;
     const T *Cin = (const T *)a.C_t + b * bcstride + (long)g * N;
-
-    // ---- stage this block's x, B, C (through the conv window if any)
-    const int nch = prows + 2 * N;
-    for (int i = threadIdx.x; i < nch; i += kThreads) {
-        long cidx;
-        float raw;
-        float *dst;
+    for (int i = threadIdx.x; i < prows + 2 * N; i += kThreads) {
         if (i < prows) {
-            cidx = (long)h * P + p0 + i;
-            raw = ld(xin + i);
-            dst = &xs[i];
+            xs[i] = conv_channel<T, CONV>(a, C, b, xch0 + i, ld(xin + i), true);
         } else if (i < prows + N) {
             const int n = i - prows;
-            cidx = HP + (long)g * N + n;
-            raw = ld(Bin + n);
-            dst = &Bs[n];
+            Bs[n] = conv_channel<T, CONV>(a, C, b, HP + (long)g * N + n, ld(Bin + n), bc_writer);
         } else {
             const int n = i - prows - N;
-            cidx = HP + GN + (long)g * N + n;
-            raw = ld(Cin + n);
-            dst = &Cs[n];
+            Cs[n] = conv_channel<T, CONV>(a, C, b, HP + GN + (long)g * N + n, ld(Cin + n), bc_writer);
         }
-        float v = raw;
-        if (CONV) {
-            const int K = a.K;
-            const long C = HP + 2 * GN;
-            const T *cin = (const T *)a.conv_in + ((long)b * C + cidx) * (K - 1);
-            const T *w = (const T *)a.conv_w + cidx * K;
-            float win[kMaxK];
-#pragma unroll
-            for (int k = 0; k < kMaxK; ++k)
-                win[k] = (k < K - 1) ? ld(cin + k) : (k == K - 1 ? raw : 0.0f);
-            float acc = a.conv_b ? ld((const T *)a.conv_b + cidx) : 0.0f;
-#pragma unroll
-            for (int k = 0; k < kMaxK; ++k)
-                if (k < K) acc = fmaf(ld(w + k), win[k], acc);
-            v = a.activation ? silu(acc) : acc;
-            if (i < prows || ((h % hpg) == 0 && pb == 0)) {
-                T *cout = (T *)a.conv_out + ((long)b * C + cidx) * (K - 1);
-#pragma unroll
-                for (int k = 0; k < kMaxK - 1; ++k)
-                    if (k < K - 1) st(cout + k, win[k + 1]);
-            }
-        }
-        *dst = v;
     }
     __syncthreads();
 
@@ -114,28 +133,17 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     // and fma(expm1, h, h + dt*x*B) (the nearly constant decrement is rounded
     // against the fp32 grid the same way every step).  Here the only
     // state-sized rounding is of h plus a random increment.
-    const float A = -expf(a.A_log[h]);
-    const float dtv = a.dt_t[(long)b * a.H + h];
-    const float dm1 = expm1f(dtv * A);
-    const float Dh = a.D ? a.D[h] : 0.0f;
-    const int lr = threadIdx.x % S::LPR;
-    const int row0 = threadIdx.x / S::LPR;
-    const int n0 = lr * 4;
     const float4 Bv = make_float4(Bs[n0], Bs[n0 + 1], Bs[n0 + 2], Bs[n0 + 3]);
     const float4 Cv = make_float4(Cs[n0], Cs[n0 + 1], Cs[n0 + 2], Cs[n0 + 3]);
-    float *sbase = a.state + (((long)b * a.H + h) * P + p0) * N + n0;
-
-    float4 hv[S::RPT];
+    T *yout = (T *)a.y_t + row_base;
 #pragma unroll
-    for (int r = 0; r < S::RPT; ++r) {
-        const int pr = row0 + r * S::ROWS_PER_PASS;
-        hv[r] = pr < prows ? *(const float4 *)(sbase + (long)pr * N) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    T *yout = (T *)a.y_t + ((long)b * a.H + h) * P + p0;
-#pragma unroll
-    for (int r = 0; r < S::RPT; ++r) {
+    for (int r = 0; r < RPT; ++r) {
         const int pr = row0 + r * S::ROWS_PER_PASS;
         const bool valid = pr < prows;
+        const int hi = (r0 + (valid ? pr : 0)) / P - r0 / P;  // head of this row within the block
+        const float dtv = hdt[hi];
+        const float dm1 = hdm1[hi];
+        const float Dh = hD[hi];
         const float xv = valid ? xs[pr] : 0.0f;
         const float coef = dtv * xv;
         float4 v = hv[r];
@@ -155,17 +163,30 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     }
 }
 
-template <typename T, int N>
-hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
-    using S = DecodeShape<N>;
-    const long npb = (a.P + S::PBLK - 1) / S::PBLK;
-    const long blocks = (long)a.B * a.H * npb;
+template <typename T, int N, int RPT>
+hipError_t launch_nr(const DecodeArgs &a, hipStream_t s) {
+    using S = DecodeShape<N, RPT>;
+    const long GR = (long)(a.H / a.G) * a.P;
+    const long npb = (GR + S::PBLK - 1) / S::PBLK;
+    const long blocks = (long)a.B * a.G * npb;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (a.conv_in)
-        hipLaunchKernelGGL((decode_step_kernel<T, N, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((decode_step_kernel<T, N, true, RPT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_step_kernel<T, N, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((decode_step_kernel<T, N, false, RPT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
+}
+
+// Rows per workgroup: 16-row blocks while the grid is small (more
+// workgroups in flight), 4x larger blocks once there are enough of them to
+// fill the machine (measured at B=16, H=80, P=64, N=128: 64-row blocks take
+// 17.5 us per step, 32-row 23.9 us, 16-row 35 us, 128-row 18.3 us).
+template <typename T, int N>
+hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
+    constexpr int base = DecodeShape<N, 1>::ROWS_PER_PASS >= 16 ? 1 : 16 / DecodeShape<N, 1>::ROWS_PER_PASS;
+    const long big = (long)a.B * a.H * ((a.P + DecodeShape<N, 4 * base>::PBLK - 1) / DecodeShape<N, 4 * base>::PBLK);
+    if (big >= 1024) return launch_nr<T, N, 4 * base>(a, s);
+    return launch_nr<T, N, base>(a, s);
 }
 
 template <typename T>

@@ -1,0 +1,107 @@
+"""HIP-graph capture of the C-ABI calls (the on-device decode loop).
+
+Each graph is captured once and replayed several times, with the program's
+own eager work and synchronisations between replays; every replay must equal
+the eager result bit for bit (the kernels are deterministic).
+"""
+import pytest
+import torch
+
+from mamba_ssd_scan_chunk_amd import binding as bd
+from mamba_ssd_scan_chunk_amd import synth
+from tests.gpu_utils import announce
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_setup(B=2, H=4, P=64, G=1, N=128, K=4, steps=6):
+    C = H * P + 2 * G * N
+    xbc, dts = synth.make_decode_stream(steps, B, H, P, G, N, "bf16", seed=70)
+    w, _ = synth.make_conv(C, K, "bf16", seed=71)
+    pre = synth.make_prefill(B, 1, H, P, G, N, "bf16", seed=72)
+    state0 = synth.make_state(B, H, P, N, seed=73, scale=0.3).cuda()
+    conv0 = synth.make_tokens(B, K - 1, C, "bf16", seed=74).transpose(1, 2).contiguous().cuda()
+    return dict(B=B, H=H, P=P, G=G, N=N, K=K, C=C, steps=steps, xbc=xbc.cuda(), dts=dts.cuda(), w=w.cuda(),
+                A_log=pre["A_log"].cuda(), D=pre["D"].cuda(), state0=state0, conv0=conv0)
+
+
+def _run_steps(s, state, conv, ys):
+    H, P, G, N, C = s["H"], s["P"], s["G"], s["N"], s["C"]
+    for i in range(s["steps"]):
+        row = s["xbc"][i]
+        bd.ssd_decode_step(row[:, :H * P], s["dts"][i], s["A_log"], row[:, H * P:H * P + G * N],
+                           row[:, H * P + G * N:], s["D"], state, y_t=ys[i], in_stride=C, G=G,
+                           conv_state_in=conv[i & 1], conv_state_out=conv[(i + 1) & 1], conv_w=s["w"], K=s["K"],
+                           activation=1)
+
+
+def test_decode_loop_graph_replays_match_eager():
+    s = _decode_setup()
+    announce("graph decode")
+    ys_ref = torch.empty((s["steps"], s["B"], s["H"], s["P"]), dtype=torch.bfloat16, device="cuda")
+    st_ref = s["state0"].clone()
+    cv_ref = [s["conv0"].clone(), torch.empty_like(s["conv0"])]
+    _run_steps(s, st_ref, cv_ref, ys_ref)
+    torch.cuda.synchronize()
+
+    state = s["state0"].clone()
+    conv = [s["conv0"].clone(), torch.empty_like(s["conv0"])]
+    ys = torch.empty_like(ys_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _run_steps(s, state, conv, ys)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _run_steps(s, state, conv, ys)
+    other = s["state0"].clone()
+    for rep in range(3):
+        # restore the cache eagerly, do unrelated eager work, then replay
+        state.copy_(s["state0"])
+        conv[0].copy_(s["conv0"])
+        ys.zero_()
+        _run_steps(s, other, [s["conv0"].clone(), torch.empty_like(s["conv0"])],
+                   torch.empty_like(ys_ref))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, ys_ref), rep
+        assert torch.equal(state, st_ref), rep
+        final = conv[s["steps"] & 1]
+        assert torch.equal(final, cv_ref[s["steps"] & 1]), rep
+
+
+def test_prefill_graph_replays_match_eager():
+    w = synth.WORKLOADS["mamba2-130m-prefill"]
+    d = {k: v.cuda() for k, v in synth.make_prefill(w.B, 1000, w.H, w.P, w.G, w.N, w.dtype, seed=75).items()}
+    announce("graph prefill")
+    y_ref, fs_ref = bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=w.Q)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_ref)
+    fs = torch.empty_like(fs_ref)
+    need = bd.ssd_prefill_workspace_bytes(w.B, 1000, w.H, w.P, w.G, w.N, w.Q, bd.SSD_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def call():
+        bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=w.Q, y=y, final_state=fs,
+                       workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        y.zero_()
+        fs.zero_()
+        ws.fill_(0xAB)
+        bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], None, Q=w.Q)  # unrelated eager call
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), rep
+        assert torch.equal(fs, fs_ref), rep
