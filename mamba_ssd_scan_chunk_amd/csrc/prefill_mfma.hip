@@ -106,22 +106,26 @@ __device__ __forceinline__ void chunk_cumsum(const PrefillArgs &a, int b, int t0
     dts[t] = dtv;
 }
 
-// Load the x chunk of head h ([Q tokens][P] bf16, row stride H*P), scale
-// token s by scale(s), and store it transposed ([P][Q], swizzled) in LDS.
-// Thread t owns the 8x8 block of tokens 8*(t/8).. and features 8*(t%8)..
-template <typename ScaleFn>
-__device__ __forceinline__ void load_x_transposed(const PrefillArgs &a, int b, int t0, int Qc, int h, char *xt,
-                                                  ScaleFn scale) {
+// Load the x chunk of head h ([Q tokens][P] bf16, row stride H*P): thread t
+// owns the 8x8 block of tokens 8*(t/8).. and features 8*(t%8)..
+__device__ __forceinline__ void load_x_raw(const PrefillArgs &a, int b, int t0, int Qc, int h, u32x4 (&raw)[8]) {
     const int t = threadIdx.x;
     const int sb = t >> 3, pb = t & 7;
     const bf16_t *xg = (const bf16_t *)a.x + (((long)b * a.L + t0) * a.H + h) * kP + pb * 8;
     const int rs = a.H * kP;  // in-chunk row offsets fit in 32 bits (Q * H * P < 2^31)
-    u32x4 raw[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int s = sb * 8 + r;
         raw[r] = s < Qc ? *(const u32x4 *)(xg + s * rs) : u32x4{0u, 0u, 0u, 0u};
     }
+}
+
+// Scale token s of the thread's block by scale(s) and store the block
+// transposed ([P][Q], swizzled) in LDS.
+template <typename ScaleFn>
+__device__ __forceinline__ void store_x_transposed(const u32x4 (&raw)[8], char *xt, ScaleFn scale) {
+    const int t = threadIdx.x;
+    const int sb = t >> 3, pb = t & 7;
     float v[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) v[r] = scale(sb * 8 + r);
@@ -249,18 +253,25 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
 
+    // every global load of this workgroup is issued before the cumsum
+    u32x4 raw[8];
+    load_x_raw(a, b, t0, Qc, h, raw);
+    const long cg = ((long)b * a.nchunks + c) * a.G + g;
+    const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
+    u32x4 bq[kQ / 16];
+#pragma unroll
+    for (int kk = 0; kk < kQ / 16; ++kk) bq[kk] = bt[kk * 64];
+
     chunk_cumsum(a, b, t0, Qc, h, cs, dts, wsum);
     __syncthreads();
     const double cs_last = cs[kQ - 1];
-    load_x_transposed(a, b, t0, Qc, h, xt, [&](int s) { return expf((float)(cs_last - cs[s])) * dts[s]; });
+    store_x_transposed(raw, xt, [&](int s) { return expf((float)(cs_last - cs[s])) * dts[s]; });
     __syncthreads();
 
-    const long cg = ((long)b * a.nchunks + c) * a.G + g;
-    const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     f32x16 acc0 = {}, acc1 = {};
-#pragma unroll 4
+#pragma unroll
     for (int kk = 0; kk < kQ / 16; ++kk) {
-        const u32x4 bv = bt[kk * 64];
+        const u32x4 bv = bq[kk];
         const u32x4 a0 = lds16(xt, sw32(li, kk * 2 + lh));
         const u32x4 a1 = lds16(xt, sw32(32 + li, kk * 2 + lh));
         acc0 = mfma32(a0, bv, acc0);
@@ -293,9 +304,9 @@ constexpr int K3_LDS = K3_WS + 64;
 // One G^T tile (si, lt) applied to x'^T: unpack, add D/dt on the diagonal,
 // scale by the lane's column factor, repack as the bf16 A operand, then two
 // K=16 MFMAs per 32-wide feature tile.
-__device__ __forceinline__ void intra_tile(const u32x4 *gsrc, f32x16 (&Y)[2], const char *xt, const double *cs,
-                                           const float *dts, float Dh, int si, int lt, int li, int lh) {
-    const u32x4 g0 = gsrc[0], g1 = gsrc[1];
+__device__ __forceinline__ void intra_tile(const u32x4 g0, const u32x4 g1, f32x16 (&Y)[2], const char *xt,
+                                           const double *cs, const float *dts, float Dh, int si, int lt, int li,
+                                           int lh) {
     float gv[16];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -353,10 +364,29 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
     const long hc = ((long)b * a.nchunks + c) * a.H + h;
     const long cg = ((long)b * a.nchunks + c) * a.G + g;
 
+    // x and the first two G^T tiles of this wave are requested before the
+    // cumsum; the other tiles are requested two slots ahead of their use.
+    // Slot k of wave w: k <= w -> (token tile k, column tile w),
+    // k > w -> (token tile k-w-1, column tile 7-w).
+    u32x4 raw[8];
+    load_x_raw(a, b, t0, Qc, h, raw);
+    const u32x4 *gt = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane * 2;
+    auto slot_src = [&](int k) {
+        const int si = k <= wave ? k : k - wave - 1;
+        const int lt = k <= wave ? ltA : ltB;
+        return gt + gt_index(si, lt) * 128;
+    };
+    u32x4 gq[3][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        gq[k][0] = slot_src(k)[0];
+        gq[k][1] = slot_src(k)[1];
+    }
+
     chunk_cumsum(a, b, t0, Qc, h, cs, dts, wsum);
     el[tid] = expf((float)cs[tid]);
     __syncthreads();
-    load_x_transposed(a, b, t0, Qc, h, xt, [&](int s) {
+    store_x_transposed(raw, xt, [&](int s) {
         const double ce = cs[(s & ~31) + 31];
         return expf((float)(ce - cs[s])) * dts[s];
     });
@@ -402,9 +432,17 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
 
     // ---- intra-chunk term and D x: Y += (G^T o decay + D/dt on the diagonal)^T x'
     const float Dh = a.D ? a.D[h] : 0.0f;
-    const u32x4 *gt = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane * 2;
-    for (int si = 0; si <= ltA; ++si) intra_tile(gt + gt_index(si, ltA) * 128, Y[0], xt, cs, dts, Dh, si, ltA, li, lh);
-    for (int si = 0; si <= ltB; ++si) intra_tile(gt + gt_index(si, ltB) * 128, Y[1], xt, cs, dts, Dh, si, ltB, li, lh);
+#pragma unroll
+    for (int k = 0; k <= kTiles; ++k) {
+        if (k + 2 <= kTiles) {
+            gq[(k + 2) % 3][0] = slot_src(k + 2)[0];
+            gq[(k + 2) % 3][1] = slot_src(k + 2)[1];
+        }
+        if (k <= wave)
+            intra_tile(gq[k % 3][0], gq[k % 3][1], Y[0], xt, cs, dts, Dh, k, ltA, li, lh);
+        else
+            intra_tile(gq[k % 3][0], gq[k % 3][1], Y[1], xt, cs, dts, Dh, k - wave - 1, ltB, li, lh);
+    }
 
     // ---- epilogue: stage y (bf16) through LDS, then 16-byte coalesced stores
     __syncthreads();  // every wave is done reading x'^T
