@@ -36,6 +36,8 @@
 // D x is added through the diagonal of the masked product: with x' = v x and
 // M = u G^T, adding D / dt_l to G^T[l,l] before the scale by u_l adds
 // u_l v_l D/dt_l x_l = D x_l (u_l v_l = dt_l).
+#include <algorithm>
+
 #include "ssd_device.hpp"
 #include "ssd_internal.hpp"
 
@@ -106,18 +108,36 @@ __device__ __forceinline__ void chunk_cumsum(const PrefillArgs &a, int b, int t0
     dts[t] = dtv;
 }
 
+// Buffer resource over `bytes` bytes from p: loads at or past the end
+// return zeros, which is how the ragged last chunk reads its missing tokens.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // Load the x chunk of head h ([Q tokens][P] bf16, row stride H*P): thread t
-// owns the 8x8 block of tokens 8*(t/8).. and features 8*(t%8)..
-__device__ __forceinline__ void load_x_raw(const PrefillArgs &a, int b, int t0, int Qc, int h, u32x4 (&raw)[8]) {
-    const int t = threadIdx.x;
+// owns the 8x8 block of tokens 8*(t/8).. and features 8*(t%8)..; tokens at
+// or past Qc read as zero.
+__device__ __forceinline__ void load_x_raw(const PrefillArgs &a, int b, int t0, int Qc, int h, u32x4 (&raw)[8],
+                                           int t) {
     const int sb = t >> 3, pb = t & 7;
-    const bf16_t *xg = (const bf16_t *)a.x + (((long)b * a.L + t0) * a.H + h) * kP + pb * 8;
-    const int rs = a.H * kP;  // in-chunk row offsets fit in 32 bits (Q * H * P < 2^31)
+    const unsigned rs = (unsigned)a.H * kP * 2;  // row stride in bytes
+    const bf16_t *x0 = (const bf16_t *)a.x + (((long)b * a.L + t0) * a.H + h) * kP;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(x0, (unsigned)(Qc - 1) * rs + kP * 2);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int s = sb * 8 + r;
-        raw[r] = s < Qc ? *(const u32x4 *)(xg + s * rs) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int k = 0; k < 8; ++k) raw[k] = buf_load16(r, (unsigned)(sb * 8 + k) * rs + pb * 16);
+}
+
+// dt of token tid of the chunk (0 at or past Qc).
+__device__ __forceinline__ float load_dt(const PrefillArgs &a, int b, int t0, int Qc, int h, int t) {
+    const float *d0 = a.dt + ((long)b * a.L + t0) * a.H + h;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(d0, (unsigned)((Qc - 1) * a.H + 1) * 4);
+    return buf_load_f32(r, (unsigned)t * a.H * 4);
 }
 
 // Scale token s of the thread's block by scale(s) and store the block
@@ -255,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
 
     // every global load of this workgroup is issued before the cumsum
     u32x4 raw[8];
-    load_x_raw(a, b, t0, Qc, h, raw);
+    load_x_raw(a, b, t0, Qc, h, raw, tid);
     const long cg = ((long)b * a.nchunks + c) * a.G + g;
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[kQ / 16];
@@ -290,185 +310,344 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
 
 // ------------------------------------------------------------------------
 // K3: outputs.  Grid (nchunks * H, 1, B), one workgroup per (batch, chunk,
-// head).  Wave w owns token tiles w and 7-w (balanced causal work) and both
-// 32-wide feature tiles of P.
+// head).  The output is formed transposed, Y^T [P x Q]; wave w owns the
+// column (token) tiles w and 7-w and both 32-row feature tiles.
+//
+// Decay bookkeeping.  R_k is the cumsum at the 16th token of token tile k.
+// With
+//   x'_s = exp(R_k(s) - cs_s) dt_s x_s      (folded into x in LDS)
+//   Q_k  = exp(R_k - R_{k-1}),  R_{-1} = 0   (one scalar per tile)
+//   u_l  = exp(cs_l - R_k(l))               (one scalar per output column)
+// column tile lt is accumulated tile by tile as a Horner scheme,
+//   acc <- h_{c-1} C^T,   acc <- Q_si acc + x'^T_si G^T_(si,lt)   (si = 0..lt),
+// and Y^T = u_l acc: the intra-chunk term gets exp(cs_l - cs_s) dt_s and the
+// carried-in state exp(cs_l).  G^T tiles enter the MFMA as K0 stored them; the
+// only per-element work on them is D x, added as D / dt_l on the diagonal of
+// the diagonal tile (u_l v_l = dt_l).  The fast path needs every token within
+// 60 of its tile reference in cumsum and consecutive references at most 80
+// apart, so that no factor leaves the normal fp32 range; a workgroup whose
+// chunk breaks that, or has dt <= 0 or |D/dt| > 1e30, takes the exact path
+// instead: x' = x, Q = u = 1, h C^T scaled by exp(cs_l), each G^T element
+// scaled by exp(min(cs_l - cs_s, 0)) dt_s, and D added on the diagonal after
+// that scaling.
 // ------------------------------------------------------------------------
-constexpr int K3_XT = 0;                       // x'^T [P][Q] bf16, later y staging [Q][P] bf16
-constexpr int K3_H = K3_XT + kP * kQ * 2;      // h [P][N] bf16
-constexpr int K3_CS = K3_H + kP * kN * 2;      // cs [Q] f64
-constexpr int K3_EL = K3_CS + kQ * 8;          // exp(cs) [Q]
-constexpr int K3_DT = K3_EL + kQ * 4;          // dt [Q]
-constexpr int K3_WS = K3_DT + kQ * 4;
-constexpr int K3_LDS = K3_WS + 64;
+constexpr int kXRow = kQ * 2 + 16;        // x'^T row stride in LDS (bytes), padded against bank conflicts
+constexpr int K3_XT = 0;                  // x'^T [P][Q] bf16, tokens in MFMA K order
+constexpr int K3_H = K3_XT + kP * kXRow;  // h_{c-1} [P][N] bf16, 16-byte chunks XOR-swizzled by row
+constexpr int K3_V = K3_H + kP * kN * 2;  // x' scale per token (fast path) or cs (exact path)
+constexpr int K3_U = K3_V + kQ * 4;       // u_l
+constexpr int K3_DT = K3_U + kQ * 4;      // dt
+constexpr int K3_W = K3_DT + kQ * 4;      // per wave: cumsum at tokens 15, 47, 63; Q_k
+constexpr int K3_LDS = K3_W + 32 * 4;
+constexpr int kYRow = kP * 2 + 16;        // output staging row stride (bytes), after the main phase
+static_assert(4 * 2 * 32 * kYRow <= K3_V, "output staging must fit in the x'^T and h areas");
 
-// One G^T tile (si, lt) applied to x'^T: unpack, add D/dt on the diagonal,
-// scale by the lane's column factor, repack as the bf16 A operand, then two
-// K=16 MFMAs per 32-wide feature tile.
-__device__ __forceinline__ void intra_tile(const u32x4 g0, const u32x4 g1, f32x16 (&Y)[2], const char *xt,
-                                           const double *cs, const float *dts, float Dh, int si, int lt, int li,
-                                           int lh) {
-    float gv[16];
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// Byte offset in x'^T of the 16 bytes that lane (row p, half lh) feeds to the
+// MFMA for token tile si, K half hf.  Within every 16-token group the four
+// 4-token runs are stored in the order 0, 2, 1, 3, so that the tokens
+// {0-3, 8-11} (lh = 0) and {4-7, 12-15} (lh = 1) -- the K order in which a
+// G^T accumulator tile is consumed -- are contiguous.
+__device__ __forceinline__ int xt_operand(int p, int lh, int si, int hf) {
+    return p * kXRow + 32 * (2 * si + hf) + 16 * lh;
+}
+
+// Scale token s of the thread's 8x8 block (tokens 8*(t/8).., features
+// 8*(t%8)..) by sc[s] and store it transposed into x'^T.
+__device__ __forceinline__ void store_xt_korder(const u32x4 (&raw)[8], const float (&sc)[8], char *xt, int t) {
+    const int sb = t >> 3, pb = t & 7;
+    // tokens 8sb..8sb+3 and 8sb+4..8sb+7 are runs 2(sb&1) and 2(sb&1)+1 of
+    // group sb/2, stored at positions (sb&1) and 2+(sb&1)
+    char *dst = xt + (pb * 8) * kXRow + 32 * (sb >> 1) + 8 * (sb & 1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        gv[e * 2] = lo_bf16(g0[e]);
-        gv[e * 2 + 1] = hi_bf16(g0[e]);
-        gv[8 + e * 2] = lo_bf16(g1[e]);
-        gv[8 + e * 2 + 1] = hi_bf16(g1[e]);
-    }
-    const int l = lt * 32 + li;
-    if (si == lt) {
-        // this lane holds G^T[l, l] iff bit 2 of l matches its row half
-        const float dtl = dts[l];
-        const float add = (((li >> 2) & 1) == lh && dtl > 0.0f) ? Dh / dtl : 0.0f;
-        const int vd = ((li >> 3) << 2) | (li & 3);
+    for (int j = 0; j < 8; ++j) {
+        unsigned o[4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) gv[v] += (v == vd) ? add : 0.0f;
-    }
-    const float u = expf((float)(cs[l] - cs[si * 32 + 31]));
-    u32x4 f[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[hf][e] = pack_bf16(gv[hf * 8 + e * 2] * u, gv[hf * 8 + e * 2 + 1] * u);
-#pragma unroll
-    for (int ptile = 0; ptile < 2; ++ptile) {
-        const int p = ptile * 32 + li;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int ch = si * 4 + hf * 2;
-            const u32x2 xa = lds8(xt, sw32(p, ch) + lh * 8);
-            const u32x2 xb = lds8(xt, sw32(p, ch + 1) + lh * 8);
-            const u32x4 bv = {xa[0], xa[1], xb[0], xb[1]};
-            Y[ptile] = mfma32(f[hf], bv, Y[ptile]);
+        for (int e = 0; e < 4; ++e) {
+            const unsigned w0 = raw[2 * e][j >> 1], w1 = raw[2 * e + 1][j >> 1];
+            const float f0 = (j & 1) ? hi_bf16(w0) : lo_bf16(w0);
+            const float f1 = (j & 1) ? hi_bf16(w1) : lo_bf16(w1);
+            o[e] = pack_bf16(f0 * sc[2 * e], f1 * sc[2 * e + 1]);
         }
+        *(u32x2 *)(dst + j * kXRow) = u32x2{o[0], o[1]};
+        *(u32x2 *)(dst + j * kXRow + 16) = u32x2{o[2], o[3]};
     }
 }
 
+// Exact path: scale the G^T tile (si, lt) held by this lane (column l, rows
+// s = 32 si + 8q + 4 lh + r in register 4q + r) by exp(min(cs_l - cs_s, 0)) dt_s.
+__device__ __forceinline__ void scale_tile_exact(u32x4 (&gt)[2], const float *cst, const float *dtt, float csl,
+                                                 int si, int lh) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int s0 = 32 * si + 8 * q + 4 * lh;
+        const float4 cs4 = *(const float4 *)(cst + s0);
+        const float4 dt4 = *(const float4 *)(dtt + s0);
+        const float f[4] = {exp_fast(fminf(csl - cs4.x, 0.f)) * dt4.x, exp_fast(fminf(csl - cs4.y, 0.f)) * dt4.y,
+                            exp_fast(fminf(csl - cs4.z, 0.f)) * dt4.z, exp_fast(fminf(csl - cs4.w, 0.f)) * dt4.w};
+        const int i0 = 2 * (q & 1);
+        const unsigned w0 = gt[q >> 1][i0], w1 = gt[q >> 1][i0 + 1];
+        gt[q >> 1][i0] = pack_bf16(lo_bf16(w0) * f[0], hi_bf16(w0) * f[1]);
+        gt[q >> 1][i0 + 1] = pack_bf16(lo_bf16(w1) * f[2], hi_bf16(w1) * f[3]);
+    }
+}
+
+// Add dl to G^T[l, l] of the diagonal tile.  Lane (li, lh) holds it iff bit 2
+// of li equals lh, in register 4(li>>3) + (li&3): word widx of the two u32x4.
+__device__ __forceinline__ void add_diagonal(u32x4 (&gt)[2], float dl, int li, int lh) {
+    const int widx = ((li >> 4) << 2) | (((li >> 3) & 1) << 1) | ((li & 3) >> 1);
+    const bool hi = li & 1;
+    unsigned w = gt[0][0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) w = (widx == k) ? gt[k >> 2][k & 3] : w;
+    const float f = (hi ? hi_bf16(w) : lo_bf16(w)) + ((((li >> 2) & 1) == lh) ? dl : 0.0f);
+    const unsigned nb = f32_to_bf16(f);
+    const unsigned w2 = hi ? ((w & 0xffffu) | (nb << 16)) : ((w & 0xffff0000u) | nb);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gt[k >> 2][k & 3] = (widx == k) ? w2 : gt[k >> 2][k & 3];
+}
+
+// Grid (B * nchunks * H): workgroup = item (b, c, h), h fastest.  Wave w
+// owns column tiles ltA = w and ltB = 7 - w and processes them side by side:
+// step k applies token tile k to both (while k <= lt), so the two Horner
+// chains of a wave (four accumulators) hide each other's MFMA -> VALU -> MFMA
+// latency, and the x'^T operands of token tile k are read once for both.
 __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char *xt = smem + K3_XT;
     char *hl = smem + K3_H;
-    double *cs = (double *)(smem + K3_CS);
-    float *el = (float *)(smem + K3_EL);
-    float *dts = (float *)(smem + K3_DT);
-    double *wsum = (double *)(smem + K3_WS);
+    float *vt = (float *)(smem + K3_V);
+    float *ut = (float *)(smem + K3_U);
+    float *dtt = (float *)(smem + K3_DT);
+    float *wv = (float *)(smem + K3_W);
 
-    const int c = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H, b = blockIdx.z;
-    const int t0 = c * kQ;
-    const int Qc = min(kQ, a.L - t0);
-    const int g = h / (a.H / a.G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
     const int ltA = wave, ltB = kTiles - 1 - wave;
-    const long hc = ((long)b * a.nchunks + c) * a.H + h;
-    const long cg = ((long)b * a.nchunks + c) * a.G + g;
+    const int item = blockIdx.x;
+    const int h = item % a.H, bc = item / a.H;
+    const int c = bc % a.nchunks, b = bc / a.nchunks;
+    const int t0 = c * kQ;
+    const int Qc = min(kQ, a.L - t0);
+    const int g = h / (a.H / a.G);
+    const long cg = (long)bc * a.G + g;
 
-    // x and the first two G^T tiles of this wave are requested before the
-    // cumsum; the other tiles are requested two slots ahead of their use.
-    // Slot k of wave w: k <= w -> (token tile k, column tile w),
-    // k > w -> (token tile k-w-1, column tile 7-w).
-    u32x4 raw[8];
-    load_x_raw(a, b, t0, Qc, h, raw);
-    const u32x4 *gt = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane * 2;
-    auto slot_src = [&](int k) {
-        const int si = k <= wave ? k : k - wave - 1;
-        const int lt = k <= wave ? ltA : ltB;
-        return gt + gt_index(si, lt) * 128;
-    };
-    u32x4 gq[3][2];
+    // ---- global loads, all issued before the cumsum: x, dt, h_{c-1}, the C
+    // operands of column tile ltA and the first G^T tiles
+    u32x4 raw[8], hv[4];
+    load_x_raw(a, b, t0, Qc, h, raw, tid);
+    const float dtv = load_dt(a, b, t0, Qc, h, tid);
+    {
+        const bf16_t *hg = a.ws_hb + (long)item * kP * kN;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        gq[k][0] = slot_src(k)[0];
-        gq[k][1] = slot_src(k)[1];
+        for (int k = 0; k < 4; ++k) hv[k] = *(const u32x4 *)(hg + (tid + k * kThreads) * 8);
+    }
+    const unsigned rs_c = (unsigned)a.G * kN * 2;  // C row stride in bytes
+    const __amdgpu_buffer_rsrc_t crs =
+        make_rsrc((const bf16_t *)a.Cm + (((long)b * a.L + t0) * a.G + g) * kN, (unsigned)(Qc - 1) * rs_c + kN * 2);
+    auto load_c = [&](int lt, u32x4 (&cop)[8]) {
+        const unsigned off = (unsigned)(lt * 32 + li) * rs_c + 16 * lh;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) cop[kk] = buf_load16(crs, off + 32 * kk);
+    };
+    u32x4 cop[8];
+    load_c(ltA, cop);
+    const u32x4 *gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane * 2;
+    auto tile_ptr = [&](int si, int lt) { return gtp + gt_index(si, lt) * 128; };
+    // G^T tiles of steps k and k+1 (ring of 2), for both column tiles
+    u32x4 gA[2][2], gB[2][2];
+#pragma unroll
+    for (int k = 0; k < 1; ++k) {
+        const u32x4 *pa = tile_ptr(0, ltA);
+        const u32x4 *pb = tile_ptr(k, ltB);
+        gA[k][0] = pa[0];
+        gA[k][1] = pa[1];
+        gB[k][0] = pb[0];
+        gB[k][1] = pb[1];
     }
 
-    chunk_cumsum(a, b, t0, Qc, h, cs, dts, wsum);
-    el[tid] = expf((float)cs[tid]);
+    // ---- cumsum of dt*A within each 64-token wave (fp32), per-token factors
+    const float Af = -expf(a.A_log[h]);
+    const float loc = wave_inclusive_sum(dtv * Af);
+    const float r15 = __shfl(loc, 15, 64), r47 = __shfl(loc, 47, 64);
+    const float e = loc - ((lane & 32) ? r47 : r15);  // cs_t - R_k(t)
+    if (lane == 63) {
+        wv[3 * wave] = r15;
+        wv[3 * wave + 1] = r47;
+        wv[3 * wave + 2] = loc;
+    }
     __syncthreads();
-    store_x_transposed(raw, xt, [&](int s) {
-        const double ce = cs[(s & ~31) + 31];
-        return expf((float)(ce - cs[s])) * dts[s];
-    });
+    // R_k - R_{k-1}: within a wave r47 - r15; across waves total - r47 + r15
+    float dq = 0.0f;
+    if (tid < kTiles) {
+        const int w = tid >> 1;
+        dq = (tid & 1) ? wv[3 * w + 1] - wv[3 * w]
+                       : (w == 0 ? wv[0] : wv[3 * (w - 1) + 2] - wv[3 * (w - 1) + 1] + wv[3 * w]);
+    }
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    const bool valid = tid < Qc;
+    const float dl_fast = dtv > 0.0f ? Dh / dtv : 0.0f;
+    const bool ok = (!valid || (fabsf(e) <= 60.0f && dtv > 0.0f && fabsf(dl_fast) <= 1e30f)) &&
+                    (tid >= kTiles || fabsf(dq) <= 80.0f);
+    const bool exact = __syncthreads_or(!ok);
+    if (!exact) {
+        vt[tid] = exp_fast(-e) * dtv;
+        ut[tid] = exp_fast(e);
+    } else {
+        float pre = 0.0f;
+        for (int w = 0; w < wave; ++w) pre += wv[3 * w + 2];
+        vt[tid] = pre + loc;  // cs
+        ut[tid] = 1.0f;
+    }
+    dtt[tid] = dtv;
+    if (tid < kTiles) wv[16 + tid] = exact ? 1.0f : exp_fast(dq);
+    __syncthreads();
+
+    // ---- x' into LDS (tokens in K order), h_{c-1} into LDS
     {
-        const bf16_t *hg = a.ws_hb + hc * kP * kN;
+        float sc[8];
+        if (!exact) {
+            const float4 s0 = *(const float4 *)(vt + (tid >> 3) * 8);
+            const float4 s1 = *(const float4 *)(vt + (tid >> 3) * 8 + 4);
+            sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+            sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+        } else {
 #pragma unroll
-        for (int k = 0; k < (kP * kN / 8) / kThreads; ++k) {
+            for (int r = 0; r < 8; ++r) sc[r] = 1.0f;
+        }
+        store_xt_korder(raw, sc, xt, tid);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
             const int idx = tid + k * kThreads;
             const int r = idx >> 4, ch = idx & 15;
-            *(u32x4 *)(hl + sw16(r, ch)) = *(const u32x4 *)(hg + r * kN + ch * 8);
+            *(u32x4 *)(hl + r * 256 + ((ch ^ (r & 15)) << 4)) = hv[k];
         }
     }
     __syncthreads();
 
-    // ---- inter-chunk term: Y = exp(cs_l) * C h^T   (K = N); C read from L2
-    const bf16_t *cgp = (const bf16_t *)a.Cm + (((long)b * a.L + t0) * a.G + g) * kN;
-    const int rs_c = a.G * kN;
-    f32x16 Y[2][2];
+    const float *cst = vt;  // cs on the exact path
+    const int hrow = li * 256;
+    const int hsw = li & 15;
+
+    // carried-in state: acc = h_{c-1} C^T (K = N) for both column tiles
+    auto state_term = [&](const u32x4 (&cp)[8], f32x16 &y0, f32x16 &y1) {
+        y0 = f32x16{};
+        y1 = f32x16{};
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        const int lt = s2 ? ltB : ltA;
-        const int l = lt * 32 + li;
-        const bf16_t *crow = cgp + l * rs_c + lh * 8;
-        const bool lv = l < Qc;
-        f32x16 y0 = {}, y1 = {};
-#pragma unroll
-        for (int kk = 0; kk < kN / 16; ++kk) {
-            const u32x4 av = lv ? *(const u32x4 *)(crow + kk * 16) : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 b0 = lds16(hl, sw16(li, kk * 2 + lh));
-            const u32x4 b1 = lds16(hl, sw16(32 + li, kk * 2 + lh));
-            y0 = mfma32(av, b0, y0);
-            y1 = mfma32(av, b1, y1);
+        for (int kk = 0; kk < 8; ++kk) {
+            const int off = hrow + (((2 * kk + lh) ^ hsw) << 4);
+            const u32x4 a0 = *(const u32x4 *)(hl + off);
+            const u32x4 a1 = *(const u32x4 *)(hl + off + 32 * 256);
+            y0 = mfma32(a0, cp[kk], y0);
+            y1 = mfma32(a1, cp[kk], y1);
         }
+    };
+    f32x16 yA0, yA1, yB0, yB1;
+    state_term(cop, yA0, yA1);
+    load_c(ltB, cop);
+    state_term(cop, yB0, yB1);
+    const int lA = ltA * 32 + li, lB = ltB * 32 + li;
+    if (exact) {
+        const float eA = exp_fast(cst[lA]), eB = exp_fast(cst[lB]);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float e = el[lt * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)];
-            y0[v] *= e;
-            y1[v] *= e;
+            yA0[v] *= eA;
+            yA1[v] *= eA;
+            yB0[v] *= eB;
+            yB1[v] *= eB;
         }
-        Y[s2][0] = y0;
-        Y[s2][1] = y1;
     }
+    const float dlA = exact ? Dh : (dtt[lA] > 0.0f ? Dh / dtt[lA] : 0.0f);
+    const float dlB = exact ? Dh : (dtt[lB] > 0.0f ? Dh / dtt[lB] : 0.0f);
+    const float cslA = exact ? cst[lA] : 0.0f, cslB = exact ? cst[lB] : 0.0f;
 
-    // ---- intra-chunk term and D x: Y += (G^T o decay + D/dt on the diagonal)^T x'
-    const float Dh = a.D ? a.D[h] : 0.0f;
+    // Y^T = u_l acc, staged through LDS as bf16 rows [l][P] (144-byte stride:
+    // 2-way bank conflicts at most) so that each global store instruction
+    // writes eight whole 128-byte rows of y.
+    auto stage_tile = [&](char *st, int l, const f32x16 &y0, const f32x16 &y1) {
+        const float u = ut[l];
+        char *row = st + li * kYRow + 8 * lh;
 #pragma unroll
-    for (int k = 0; k <= kTiles; ++k) {
-        if (k + 2 <= kTiles) {
-            gq[(k + 2) % 3][0] = slot_src(k + 2)[0];
-            gq[(k + 2) % 3][1] = slot_src(k + 2)[1];
+        for (int q = 0; q < 4; ++q) {
+            *(u32x2 *)(row + 16 * q) = u32x2{pack_bf16(y0[4 * q] * u, y0[4 * q + 1] * u),
+                                             pack_bf16(y0[4 * q + 2] * u, y0[4 * q + 3] * u)};
+            *(u32x2 *)(row + 64 + 16 * q) = u32x2{pack_bf16(y1[4 * q] * u, y1[4 * q + 1] * u),
+                                                  pack_bf16(y1[4 * q + 2] * u, y1[4 * q + 3] * u)};
         }
-        if (k <= wave)
-            intra_tile(gq[k % 3][0], gq[k % 3][1], Y[0], xt, cs, dts, Dh, k, ltA, li, lh);
-        else
-            intra_tile(gq[k % 3][0], gq[k % 3][1], Y[1], xt, cs, dts, Dh, k - wave - 1, ltB, li, lh);
-    }
+    };
+    auto store_tile = [&](const char *st, int lt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const u32x4 v = *(const u32x4 *)(st + r * kYRow + 16 * (lane & 7));
+            const int l = lt * 32 + r;
+            if (l < Qc) *(u32x4 *)((bf16_t *)a.y + (((long)b * a.L + t0 + l) * a.H + h) * kP + 8 * (lane & 7)) = v;
+        }
+    };
 
-    // ---- epilogue: stage y (bf16) through LDS, then 16-byte coalesced stores
-    __syncthreads();  // every wave is done reading x'^T
-    char *ys = xt;    // [Q][P] bf16, rows of 128 bytes, 8 chunks, swizzled by row
+    // ---- intra-chunk term: step k applies token tile k to both column tiles
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        const int lt = s2 ? ltB : ltA;
+    for (int k = 0; k < kTiles; ++k) {
+        if (k <= ltB) {
+            if (k + 1 <= ltB) {
+                const u32x4 *pb = tile_ptr(k + 1, ltB);
+                gB[(k + 1) & 1][0] = pb[0];
+                gB[(k + 1) & 1][1] = pb[1];
+                if (k + 1 <= ltA) {
+                    const u32x4 *pa = tile_ptr(k + 1, ltA);
+                    gA[(k + 1) & 1][0] = pa[0];
+                    gA[(k + 1) & 1][1] = pa[1];
+                }
+            }
+            u32x4 xa[2][2];
 #pragma unroll
-        for (int ptile = 0; ptile < 2; ++ptile) {
-            const int p = ptile * 32 + li;
+            for (int hf = 0; hf < 2; ++hf) {
+                xa[0][hf] = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
+                xa[1][hf] = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
+            }
+            const float qv = wv[16 + k];
+            if (k <= ltA) {
+                u32x4 g2[2] = {gA[k & 1][0], gA[k & 1][1]};
+                if (exact) scale_tile_exact(g2, cst, dtt, cslA, k, lh);
+                if (k == ltA) add_diagonal(g2, dlA, li, lh);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int l = lt * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-                *(bf16_t *)(ys + l * 128 + (((p >> 3) ^ (l & 7)) << 4) + (p & 7) * 2) = f32_to_bf16(Y[s2][ptile][v]);
+                for (int v = 0; v < 16; ++v) {
+                    yA0[v] *= qv;
+                    yA1[v] *= qv;
+                }
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    yA0 = mfma32(xa[0][hf], g2[hf], yA0);
+                    yA1 = mfma32(xa[1][hf], g2[hf], yA1);
+                }
+            }
+            {
+                u32x4 g2[2] = {gB[k & 1][0], gB[k & 1][1]};
+                if (exact) scale_tile_exact(g2, cst, dtt, cslB, k, lh);
+                if (k == ltB) add_diagonal(g2, dlB, li, lh);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    yB0[v] *= qv;
+                    yB1[v] *= qv;
+                }
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    yB0 = mfma32(xa[0][hf], g2[hf], yB0);
+                    yB1 = mfma32(xa[1][hf], g2[hf], yB1);
+                }
             }
         }
     }
+
+    // ---- outputs: every wave is done with x'^T and h; reuse their LDS
     __syncthreads();
-    bf16_t *yg = (bf16_t *)a.y + (((long)b * a.L + t0) * a.H + h) * kP;
-    const int rs_y = a.H * kP;
-#pragma unroll
-    for (int k = 0; k < (kQ * kP / 8) / kThreads; ++k) {
-        const int idx = tid + k * kThreads;
-        const int l = idx >> 3, ch = idx & 7;
-        if (l < Qc) *(u32x4 *)(yg + l * rs_y + ch * 8) = *(const u32x4 *)(ys + l * 128 + ((ch ^ (l & 7)) << 4));
-    }
+    char *st = smem + wave * 2 * 32 * kYRow;
+    stage_tile(st, lA, yA0, yA1);
+    stage_tile(st + 32 * kYRow, lB, yB0, yB1);
+    store_tile(st, ltA);
+    store_tile(st + 32 * kYRow, ltB);
 }
 
 // ------------------------------------------------------------------------
@@ -517,6 +696,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long 
 
 bool g_attr_set = false;
 
+
 }  // namespace
 
 long prefill_mfma_gt_elems_per_chunk() { return kGTChunk; }
@@ -542,7 +722,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
                        a, total);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_out_mfma, grid, dim3(kThreads), K3_LDS, s, a);
+    const long nitems = (long)a.B * a.nchunks * a.H;
+    if (nitems > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(chunk_out_mfma, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
     return hipGetLastError();
 }
 

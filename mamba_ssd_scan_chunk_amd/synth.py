@@ -15,7 +15,10 @@ Distributions (``N(mu, v)`` has variance ``v``):
     conv_w ~ N(0, 0.02),  raw conv inputs ~ N(0, 1)
 Variants: "spec" (as above), "d0" (D = 0, so the output is the SSM term
 alone), "slow" (A_log ~ U(-7, -4) and dt = 1e-3, so state survives across
-thousands of tokens and every chunk hand-off matters).
+thousands of tokens and every chunk hand-off matters), "steep" (A_log ~
+U(0, ln 64) and dt = clip(softplus(N(0.5, 0.5)), 0.05, 3), so some heads decay
+by up to ~190 per token and others by ~1), "dtzero" (as "spec" but dt = 0 on
+every token t with t % 5 == 3).
 """
 from __future__ import annotations
 
@@ -25,7 +28,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-VARIANTS = ("spec", "d0", "slow")
+VARIANTS = ("spec", "d0", "slow", "steep", "dtzero")
 
 
 @dataclass(frozen=True)
@@ -107,6 +110,12 @@ def make_prefill(B, L, H, P, G, N, dtype="f32", seed=0, variant="spec"):
     elif variant == "slow":
         A_log = rng.uniform(-7.0, -4.0, size=H).astype(np.float32)
         dt[:] = np.float32(1e-3)
+    elif variant == "steep":
+        A_log = rng.uniform(0.0, math.log(64.0), size=H).astype(np.float32)
+        z = 0.5 + math.sqrt(0.5) * rng.standard_normal(size=(B, L, H), dtype=np.float32).astype(np.float64)
+        dt = np.clip(np.logaddexp(0.0, z), 0.05, 3.0).astype(np.float32)
+    elif variant == "dtzero":
+        dt[:, 3::5] = np.float32(0.0)
     return dict(
         x=_store(x, dtype), dt=torch.from_numpy(dt), A_log=torch.from_numpy(A_log),
         Bm=_store(Bm, dtype), Cm=_store(Cm, dtype), D=torch.from_numpy(D),

@@ -39,7 +39,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("variant", ["spec", "d0", "slow"])
+@pytest.mark.parametrize("variant", ["spec", "d0", "slow", "steep", "dtzero"])
 @pytest.mark.parametrize("with_init", [False, True])
 def test_prefill_matches_oracle(oracle, case, variant, with_init):
     name, B, L, H, P, G, N, Q, dtype = case
