@@ -60,14 +60,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte chunk `ch` of row `r`, XOR-swizzled so that the 32
-// rows one MFMA operand read touches land in distinct LDS banks.
-__device__ __forceinline__ int sw16(int r, int ch) { return r * 256 + ((ch ^ (r & 15)) << 4); }  // 128-bf16 rows
-__device__ __forceinline__ int sw32(int r, int ch) { return r * 512 + ((ch ^ (r & 31)) << 4); }  // 256-bf16 rows
-
-__device__ __forceinline__ u32x4 lds16(const char *base, int off) { return *(const u32x4 *)(base + off); }
-__device__ __forceinline__ u32x2 lds8(const char *base, int off) { return *(const u32x2 *)(base + off); }
-
 __device__ __forceinline__ float lo_bf16(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
@@ -81,32 +73,6 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 
 // index of causal tile (token tile si, column tile lt), si <= lt
 __device__ __forceinline__ int gt_index(int si, int lt) { return lt * (lt + 1) / 2 + si; }
-
-__device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        double o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
-
-// In-chunk inclusive cumsum of dt*A over the Q tokens of (b, chunk, h), in
-// fp64 so that differences cs_l - cs_s keep full fp32 accuracy.  Token t is
-// thread t; padded tokens (t >= Qc) get dt = 0.  Writes cs[] and dt[].
-__device__ __forceinline__ void chunk_cumsum(const PrefillArgs &a, int b, int t0, int Qc, int h, double *cs,
-                                             float *dts, double *wsum) {
-    const int t = threadIdx.x;
-    const float dtv = t < Qc ? a.dt[((long)b * a.L + t0 + t) * a.H + h] : 0.0f;
-    const float Af = -expf(a.A_log[h]);
-    double inc = wave_inclusive_sum_f64((double)(dtv * Af));
-    if ((t & 63) == 63) wsum[t >> 6] = inc;
-    __syncthreads();
-    for (int w = 0; w < (t >> 6); ++w) inc += wsum[w];
-    cs[t] = inc;
-    dts[t] = dtv;
-}
 
 // Buffer resource over `bytes` bytes from p: loads at or past the end
 // return zeros, which is how the ragged last chunk reads its missing tokens.
@@ -140,197 +106,6 @@ __device__ __forceinline__ float load_dt(const PrefillArgs &a, int b, int t0, in
     return buf_load_f32(r, (unsigned)t * a.H * 4);
 }
 
-// Scale token s of the thread's block by scale(s) and store the block
-// transposed ([P][Q], swizzled) in LDS.
-template <typename ScaleFn>
-__device__ __forceinline__ void store_x_transposed(const u32x4 (&raw)[8], char *xt, ScaleFn scale) {
-    const int t = threadIdx.x;
-    const int sb = t >> 3, pb = t & 7;
-    float v[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = scale(sb * 8 + r);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const unsigned w0 = raw[2 * e][j >> 1], w1 = raw[2 * e + 1][j >> 1];
-            const float f0 = (j & 1) ? hi_bf16(w0) : lo_bf16(w0);
-            const float f1 = (j & 1) ? hi_bf16(w1) : lo_bf16(w1);
-            o[e] = pack_bf16(f0 * v[2 * e], f1 * v[2 * e + 1]);
-        }
-        *(u32x4 *)(xt + sw32(pb * 8 + j, sb)) = o;
-    }
-}
-
-// ------------------------------------------------------------------------
-// K0: per (batch, chunk, group, part): masked G^T tiles of the column-tile
-// pair (part, 7-part), and the part-th 32-wide slice of B in K1's operand
-// order.  Grid (nchunks, 4 * G, B).
-// ------------------------------------------------------------------------
-constexpr int K0_LDS = 2 * kQ * kN * 2;  // B and C of the chunk
-
-__global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    char *bl = smem;
-    char *cl = smem + kQ * kN * 2;
-    const int c = blockIdx.x, b = blockIdx.z;
-    const int part = blockIdx.y & 3, g = blockIdx.y >> 2;
-    const int t0 = c * kQ;
-    const int Qc = min(kQ, a.L - t0);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 31, lh = lane >> 5;
-    const long cg = ((long)b * a.nchunks + c) * a.G + g;  // (batch, chunk, group) index
-    {
-        const bf16_t *bg = (const bf16_t *)a.Bm + (((long)b * a.L + t0) * a.G + g) * kN;
-        const bf16_t *cgp = (const bf16_t *)a.Cm + (((long)b * a.L + t0) * a.G + g) * kN;
-        const int rs = a.G * kN;
-#pragma unroll
-        for (int k = 0; k < (kQ * kN / 8) / kThreads; ++k) {
-            const int idx = tid + k * kThreads;
-            const int r = idx >> 4, ch = idx & 15;
-            u32x4 vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
-            if (r < Qc) {
-                vb = *(const u32x4 *)(bg + r * rs + ch * 8);
-                vc = *(const u32x4 *)(cgp + r * rs + ch * 8);
-            }
-            *(u32x4 *)(bl + sw16(r, ch)) = vb;
-            *(u32x4 *)(cl + sw16(r, ch)) = vc;
-        }
-    }
-    __syncthreads();
-
-    // G^T tiles: slot k -> (si, lt); slots 0..part belong to column tile
-    // `part`, slots part+1..8 to column tile 7-part.  Wave w takes slots
-    // w, w+4, w+8.
-    u32x4 *gt = (u32x4 *)(a.ws_gt + cg * kGTChunk);
-    for (int k = wave; k <= kTiles; k += 4) {
-        const int si = k <= part ? k : k - part - 1;
-        const int lt = k <= part ? part : kTiles - 1 - part;
-        f32x16 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < kN / 16; ++kk) {
-            const u32x4 av = lds16(bl, sw16(si * 32 + li, kk * 2 + lh));
-            const u32x4 bv = lds16(cl, sw16(lt * 32 + li, kk * 2 + lh));
-            acc = mfma32(av, bv, acc);
-        }
-        if (si == lt) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                if ((v >> 2) * 8 + lh * 4 + (v & 3) > li) acc[v] = 0.0f;  // token s after token l
-        }
-        u32x4 o0, o1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            o0[e] = pack_bf16(acc[e * 2], acc[e * 2 + 1]);
-            o1[e] = pack_bf16(acc[8 + e * 2], acc[8 + e * 2 + 1]);
-        }
-        u32x4 *dst = gt + ((long)gt_index(si, lt) * 64 + lane) * 2;
-        dst[0] = o0;
-        dst[1] = o1;
-    }
-
-    // B in K1's operand order: [nt][kk][lane] 16 bytes = B[kk*16 + lh*8 + j][nt*32 + li]
-    u32x4 *bt = (u32x4 *)(a.ws_bt + cg * kBTChunk);
-    const int nt = part;
-    for (int idx = tid; idx < (kQ / 16) * 64; idx += kThreads) {
-        const int kk = idx >> 6, ln = idx & 63;
-        const int n = nt * 32 + (ln & 31), s0 = kk * 16 + (ln >> 5) * 8;
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const unsigned short lo = *(const unsigned short *)(bl + sw16(s0 + 2 * e, n >> 3) + (n & 7) * 2);
-            const unsigned short hi = *(const unsigned short *)(bl + sw16(s0 + 2 * e + 1, n >> 3) + (n & 7) * 2);
-            o[e] = (unsigned)lo | ((unsigned)hi << 16);
-        }
-        bt[(nt * (kQ / 16) + kk) * 64 + ln] = o;
-    }
-}
-
-// ------------------------------------------------------------------------
-// K1: chunk states S_c = (w o X)^T B, w_s = exp(cs_last - cs_s) dt_s.
-// Grid (nchunks * H, 1, B), one workgroup per (batch, chunk, head).
-// Wave w computes the 64 x 32 slice of S for state columns 32w..32w+31.
-// ------------------------------------------------------------------------
-constexpr int K1_XT = 0;
-constexpr int K1_CS = K1_XT + kP * kQ * 2;
-constexpr int K1_DT = K1_CS + kQ * 8;
-constexpr int K1_WS = K1_DT + kQ * 4;
-constexpr int K1_LDS = K1_WS + 64;
-
-__global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    char *xt = smem + K1_XT;
-    double *cs = (double *)(smem + K1_CS);
-    float *dts = (float *)(smem + K1_DT);
-    double *wsum = (double *)(smem + K1_WS);
-    const int c = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H, b = blockIdx.z;
-    const int t0 = c * kQ;
-    const int Qc = min(kQ, a.L - t0);
-    const int g = h / (a.H / a.G);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 31, lh = lane >> 5;
-
-    // every global load of this workgroup is issued before the cumsum
-    u32x4 raw[8];
-    load_x_raw(a, b, t0, Qc, h, raw, tid);
-    const long cg = ((long)b * a.nchunks + c) * a.G + g;
-    const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
-    u32x4 bq[kQ / 16];
-#pragma unroll
-    for (int kk = 0; kk < kQ / 16; ++kk) bq[kk] = bt[kk * 64];
-
-    chunk_cumsum(a, b, t0, Qc, h, cs, dts, wsum);
-    __syncthreads();
-    const double cs_last = cs[kQ - 1];
-    store_x_transposed(raw, xt, [&](int s) { return expf((float)(cs_last - cs[s])) * dts[s]; });
-    __syncthreads();
-
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int kk = 0; kk < kQ / 16; ++kk) {
-        const u32x4 bv = bq[kk];
-        const u32x4 a0 = lds16(xt, sw32(li, kk * 2 + lh));
-        const u32x4 a1 = lds16(xt, sw32(32 + li, kk * 2 + lh));
-        acc0 = mfma32(a0, bv, acc0);
-        acc1 = mfma32(a1, bv, acc1);
-    }
-    const long hc = ((long)b * a.nchunks + c) * a.H + h;
-    float *Sg = a.ws_S + hc * kP * kN + wave * 32 + li;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int p = (v >> 2) * 8 + lh * 4 + (v & 3);
-        Sg[p * kN] = acc0[v];
-        Sg[(32 + p) * kN] = acc1[v];
-    }
-    if (tid == 0) a.ws_dec[hc] = expm1f((float)cs_last);
-}
-
-// ------------------------------------------------------------------------
-// K3: outputs.  Grid (nchunks * H, 1, B), one workgroup per (batch, chunk,
-// head).  The output is formed transposed, Y^T [P x Q]; wave w owns the
-// column (token) tiles w and 7-w and both 32-row feature tiles.
-//
-// Decay bookkeeping.  R_k is the cumsum at the 16th token of token tile k.
-// With
-//   x'_s = exp(R_k(s) - cs_s) dt_s x_s      (folded into x in LDS)
-//   Q_k  = exp(R_k - R_{k-1}),  R_{-1} = 0   (one scalar per tile)
-//   u_l  = exp(cs_l - R_k(l))               (one scalar per output column)
-// column tile lt is accumulated tile by tile as a Horner scheme,
-//   acc <- h_{c-1} C^T,   acc <- Q_si acc + x'^T_si G^T_(si,lt)   (si = 0..lt),
-// and Y^T = u_l acc: the intra-chunk term gets exp(cs_l - cs_s) dt_s and the
-// carried-in state exp(cs_l).  G^T tiles enter the MFMA as K0 stored them; the
-// only per-element work on them is D x, added as D / dt_l on the diagonal of
-// the diagonal tile (u_l v_l = dt_l).  The fast path needs every token within
-// 60 of its tile reference in cumsum and consecutive references at most 80
-// apart, so that no factor leaves the normal fp32 range; a workgroup whose
-// chunk breaks that, or has dt <= 0 or |D/dt| > 1e30, takes the exact path
-// instead: x' = x, Q = u = 1, h C^T scaled by exp(cs_l), each G^T element
-// scaled by exp(min(cs_l - cs_s, 0)) dt_s, and D added on the diagonal after
-// that scaling.
-// ------------------------------------------------------------------------
 constexpr int kXRow = kQ * 2 + 16;        // x'^T row stride in LDS (bytes), padded against bank conflicts
 constexpr int K3_XT = 0;                  // x'^T [P][Q] bf16, tokens in MFMA K order
 constexpr int K3_H = K3_XT + kP * kXRow;  // h_{c-1} [P][N] bf16, 16-byte chunks XOR-swizzled by row
@@ -375,6 +150,195 @@ __device__ __forceinline__ void store_xt_korder(const u32x4 (&raw)[8], const flo
     }
 }
 
+// ------------------------------------------------------------------------
+// K0: per (batch, chunk, group), shared by every head of the group.  Grid
+// (nchunks, 13 * G, B).  Blocks y % 13 < 9 form the 36 causal 32x32 tiles of
+// G^T = B C^T, one per wave, masked (s > l -> 0) and stored as bf16 in the
+// exact register order of the MFMA accumulator; blocks y % 13 >= 9 write the
+// 32-column slice y % 13 - 9 of B in the order of K1's MFMA B operand.  The
+// operands are read straight from L2; tokens past the end read as zero.
+// ------------------------------------------------------------------------
+constexpr int kK0Tiles = kGTiles / 4;         // workgroups forming G^T tiles
+constexpr int kK0Blocks = kK0Tiles + kN / 32;  // plus one per 32 columns of B
+
+__global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) char bl[kQ * 64];  // B[:, 32 columns] as [token][32] bf16
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int part = blockIdx.y % kK0Blocks, g = blockIdx.y / kK0Blocks;
+    const int t0 = c * kQ;
+    const int Qc = min(kQ, a.L - t0);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+    const long cg = ((long)b * a.nchunks + c) * a.G + g;
+    const unsigned rs = (unsigned)a.G * kN * 2;  // token stride of B and C in bytes
+    const long base = (((long)b * a.L + t0) * a.G + g) * kN;
+    const unsigned bytes = (unsigned)(Qc - 1) * rs + kN * 2;
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc((const bf16_t *)a.Bm + base, bytes);
+
+    if (part < kK0Tiles) {
+        const __amdgpu_buffer_rsrc_t crs = make_rsrc((const bf16_t *)a.Cm + base, bytes);
+        const int tix = part * 4 + wave;  // = gt_index(si, lt)
+        int lt = 0;
+        while ((lt + 1) * (lt + 2) / 2 <= tix) ++lt;
+        const int si = tix - lt * (lt + 1) / 2;
+        const unsigned oa = (unsigned)(si * 32 + li) * rs + 16 * lh;
+        const unsigned ob = (unsigned)(lt * 32 + li) * rs + 16 * lh;
+        u32x4 av[8], bv[8];
+#pragma unroll
+        for (int kk = 0; kk < kN / 16; ++kk) {
+            av[kk] = buf_load16(brs, oa + 32 * kk);
+            bv[kk] = buf_load16(crs, ob + 32 * kk);
+        }
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < kN / 16; ++kk) acc = mfma32(av[kk], bv[kk], acc);
+        if (si == lt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if ((v >> 2) * 8 + lh * 4 + (v & 3) > li) acc[v] = 0.0f;  // token s after token l
+        }
+        u32x4 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o0[e] = pack_bf16(acc[e * 2], acc[e * 2 + 1]);
+            o1[e] = pack_bf16(acc[8 + e * 2], acc[8 + e * 2 + 1]);
+        }
+        u32x4 *dst = (u32x4 *)(a.ws_gt + cg * kGTChunk) + ((long)tix * 64 + lane) * 2;
+        dst[0] = o0;
+        dst[1] = o1;
+        return;
+    }
+
+    // B columns 32 nt .. 32 nt + 31 into LDS, then K1's operand order:
+    // [nt][group gg of 16 tokens][lane] 16 bytes = B[s_j][32 nt + li] with
+    // s_j = 16 gg + 4 lh + (j & 3) + 8 (j >> 2), the token order of x'^T.
+    const int nt = part - kK0Tiles;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = tid + k * kThreads;
+        const int s = idx >> 2, q = idx & 3;
+        *(u32x4 *)(bl + s * 64 + q * 16) = buf_load16(brs, (unsigned)s * rs + nt * 64 + q * 16);
+    }
+    __syncthreads();
+    u32x4 *bt = (u32x4 *)(a.ws_bt + cg * kBTChunk) + nt * (kQ / 16) * 64;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = tid + k * kThreads;
+        const int gg = idx >> 6, ln = idx & 63;
+        const int s0 = 16 * gg + 4 * (ln >> 5);
+        const char *col = bl + (ln & 31) * 2;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int sa = s0 + 2 * (e & 1) + 8 * (e >> 1);
+            const unsigned lo = *(const unsigned short *)(col + sa * 64);
+            const unsigned hi = *(const unsigned short *)(col + (sa + 1) * 64);
+            o[e] = lo | (hi << 16);
+        }
+        bt[gg * 64 + ln] = o;
+    }
+}
+
+// ------------------------------------------------------------------------
+// K1: chunk states.  Grid (B * nchunks * H), workgroup = item (b, c, h):
+//   S_c[p, n] = sum_s exp(cs_last - cs_s) dt_s x_s[p] B_s[n]
+// with x'' = exp(cs_last - cs_s) dt_s x_s <= dt_s folded into x in LDS.
+// Wave w computes the 64 x 32 slice of S for columns n in [32w, 32w + 32).
+// Also writes exp(cs_last) - 1 for the state pass.
+// ------------------------------------------------------------------------
+constexpr int K1_XT = 0;
+constexpr int K1_V = K1_XT + kP * kXRow;
+constexpr int K1_W = K1_V + kQ * 4;
+constexpr int K1_LDS = K1_W + 16 * 4;
+
+__global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char *xt = smem + K1_XT;
+    float *vt = (float *)(smem + K1_V);
+    float *wv = (float *)(smem + K1_W);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x;
+    const int h = item % a.H, bc = item / a.H;
+    const int c = bc % a.nchunks, b = bc / a.nchunks;
+    const int t0 = c * kQ;
+    const int Qc = min(kQ, a.L - t0);
+    const int g = h / (a.H / a.G);
+    const long cg = (long)bc * a.G + g;
+
+    // every global load of this workgroup is issued before the cumsum
+    u32x4 raw[8];
+    load_x_raw(a, b, t0, Qc, h, raw, tid);
+    const float dtv = load_dt(a, b, t0, Qc, h, tid);
+    const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
+    u32x4 bq[kQ / 16];
+#pragma unroll
+    for (int gg = 0; gg < kQ / 16; ++gg) bq[gg] = bt[gg * 64];
+
+    // cumsum within each 64-token wave (fp32); cs_last - cs_t from the wave totals
+    const float loc = wave_inclusive_sum(dtv * -expf(a.A_log[h]));
+    if (lane == 63) wv[wave] = loc;
+    __syncthreads();
+    float after = 0.0f, total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float tw = wv[w];
+        total += tw;
+        after += w > wave ? tw : 0.0f;
+    }
+    vt[tid] = exp_fast(wv[wave] - loc + after) * dtv;  // dt = 0 past Qc
+    if (tid == 0) a.ws_dec[item] = expm1f(total);
+    __syncthreads();
+    {
+        const float4 s0 = *(const float4 *)(vt + (tid >> 3) * 8);
+        const float4 s1 = *(const float4 *)(vt + (tid >> 3) * 8 + 4);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        store_xt_korder(raw, sc, xt, tid);
+    }
+    __syncthreads();
+
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int gg = 0; gg < kQ / 16; ++gg) {
+        const u32x4 a0 = *(const u32x4 *)(xt + xt_operand(li, lh, gg >> 1, gg & 1));
+        const u32x4 a1 = *(const u32x4 *)(xt + xt_operand(32 + li, lh, gg >> 1, gg & 1));
+        acc0 = mfma32(a0, bq[gg], acc0);
+        acc1 = mfma32(a1, bq[gg], acc1);
+    }
+    float *Sg = a.ws_S + (long)item * kP * kN + wave * 32 + li;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int p = (v >> 2) * 8 + lh * 4 + (v & 3);
+        Sg[p * kN] = acc0[v];
+        Sg[(32 + p) * kN] = acc1[v];
+    }
+}
+
+// ------------------------------------------------------------------------
+// K3: outputs.  Grid (nchunks * H, 1, B), one workgroup per (batch, chunk,
+// head).  The output is formed transposed, Y^T [P x Q]; wave w owns the
+// column (token) tiles w and 7-w and both 32-row feature tiles.
+//
+// Decay bookkeeping.  R_k is the cumsum at the 16th token of token tile k.
+// With
+//   x'_s = exp(R_k(s) - cs_s) dt_s x_s      (folded into x in LDS)
+//   Q_k  = exp(R_k - R_{k-1}),  R_{-1} = 0   (one scalar per tile)
+//   u_l  = exp(cs_l - R_k(l))               (one scalar per output column)
+// column tile lt is accumulated tile by tile as a Horner scheme,
+//   acc <- h_{c-1} C^T,   acc <- Q_si acc + x'^T_si G^T_(si,lt)   (si = 0..lt),
+// and Y^T = u_l acc: the intra-chunk term gets exp(cs_l - cs_s) dt_s and the
+// carried-in state exp(cs_l).  G^T tiles enter the MFMA as K0 stored them; the
+// only per-element work on them is D x, added as D / dt_l on the diagonal of
+// the diagonal tile (u_l v_l = dt_l).  The fast path needs every token within
+// 60 of its tile reference in cumsum and consecutive references at most 80
+// apart, so that no factor leaves the normal fp32 range; a workgroup whose
+// chunk breaks that, or has dt <= 0 or |D/dt| > 1e30, takes the exact path
+// instead: x' = x, Q = u = 1, h C^T scaled by exp(cs_l), each G^T element
+// scaled by exp(min(cs_l - cs_s, 0)) dt_s, and D added on the diagonal after
+// that scaling.
+// ------------------------------------------------------------------------
 // Exact path: scale the G^T tile (si, lt) held by this lane (column l, rows
 // s = 32 si + 8q + 4 lh + r in register 4q + r) by exp(min(cs_l - cs_s, 0)) dt_s.
 __device__ __forceinline__ void scale_tile_exact(u32x4 (&gt)[2], const float *cst, const float *dtt, float csl,
@@ -694,7 +658,6 @@ __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long 
     if (a.final_state) ((float4 *)a.final_state)[bh * PN4 + pn] = hv;
 }
 
-bool g_attr_set = false;
 
 
 }  // namespace
@@ -703,18 +666,12 @@ long prefill_mfma_gt_elems_per_chunk() { return kGTChunk; }
 long prefill_mfma_bt_elems_per_chunk() { return kBTChunk; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
-    if (!g_attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_pack_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           K0_LDS);
-        if (e != hipSuccess) return e;
-        g_attr_set = true;
-    }
-    if ((long)a.nchunks * a.H > 0x7fffffffL || a.G * 4 > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chunk_pack_mfma, dim3(a.nchunks, 4 * a.G, a.B), dim3(kThreads), K0_LDS, s, a);
+    const long nitems = (long)a.B * a.nchunks * a.H;
+    if (nitems > 0x7fffffffL || (long)a.G * kK0Blocks > 65535 || a.nchunks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(chunk_pack_mfma, dim3(a.nchunks, kK0Blocks * a.G, a.B), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)(a.nchunks * a.H), 1, a.B);
-    hipLaunchKernelGGL(chunk_state_mfma, grid, dim3(kThreads), K1_LDS, s, a);
+    hipLaunchKernelGGL(chunk_state_mfma, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
@@ -722,8 +679,6 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
                        a, total);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long nitems = (long)a.B * a.nchunks * a.H;
-    if (nitems > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chunk_out_mfma, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
     return hipGetLastError();
 }
