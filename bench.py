@@ -59,22 +59,48 @@ def decode_bytes(B, H, P, G, N, K, esize=2):
             + C * K * esize + B * H * P * esize + 8 * H)
 
 
-def _src_hash(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+KERNEL_SOURCES = ["mamba_ssd_scan_chunk_amd/csrc/prefill_mfma.hip", "mamba_ssd_scan_chunk_amd/csrc/ssd_device.hpp",
+                  "mamba_ssd_scan_chunk_amd/csrc/ssd_internal.hpp"]
 
 
-def measured_traffic(kernel_tag):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    runs, or None if absent or taken on different kernel sources."""
-    path = os.path.join(PROFILES, f"traffic_{kernel_tag}.json")
+def stage_work(kernel, B, L, H, P, G, N, Q, esize=2):
+    """Algorithmic (bytes, flops) of one launch of a prefill kernel of the
+    MFMA path: every input and output of that kernel moved once, and the flops
+    of its stage of the chunked scan (causal, as in prefill_flops)."""
+    nch = -(-L // Q)
+    items, groups = B * nch * H, B * nch * G
+    tile_bytes = (Q // 32) * (Q // 32 + 1) // 2 * 32 * 32 * 2  # masked C B^T tiles, bf16
+    qs = [min(Q, L - c * Q) for c in range(nch)]
+    if kernel == "chunk_pack_mfma":
+        nbytes = 2 * B * L * G * N * esize + groups * (tile_bytes + Q * N * 2)
+        flops = B * G * sum(N * q * (q + 1) for q in qs)
+    elif kernel == "chunk_state_mfma":
+        nbytes = B * L * H * (P * esize + 4) + groups * Q * N * 2 + items * (P * N * 4 + 4)
+        flops = B * H * sum(2 * q * N * P for q in qs)
+    elif kernel == "state_pass_bf16":
+        nbytes = items * (P * N * 4 + 4 + P * N * 2) + B * H * P * N * 4
+        flops = items * 2 * P * N
+    elif kernel == "chunk_out_mfma":
+        nbytes = (B * L * H * (2 * P * esize + 4) + B * L * G * N * esize + items * P * N * 2
+                  + groups * tile_bytes)
+        flops = B * H * sum(P * q * (q + 1) + 2 * q * N * P for q in qs)
+    else:
+        raise KeyError(kernel)
+    return nbytes, flops
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (profiles/traffic_<kernel>.json, written by
+    mamba_ssd_scan_chunk_amd.profiling), or None if absent or taken on
+    kernel sources that have changed since."""
+    from mamba_ssd_scan_chunk_amd.profiling import source_hash
+
+    path = os.path.join(PROFILES, f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != _src_hash(rec.get("sources", [])):
+    if rec.get("source_hash") != source_hash(rec.get("sources", [])):
         return None
     return rec.get("bytes_per_launch")
 
@@ -140,7 +166,21 @@ def bench_prefill(args):
     ms = _timed(step, args.steps, args.warmup, "prefill")
     flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
     nbytes = prefill_bytes(w.B, w.L, w.H, w.P, w.G, w.N, 2 if w.dtype == "bf16" else 4)
-    return w, ms, flops, nbytes
+    # per-kernel durations: HIP events the library records between its
+    # kernels on the call's stream; each sample is the last of four
+    # back-to-back calls, so the queue is busy as in the timed loop
+    bd.stage_timing(True)
+    stages = {}
+    try:
+        for _ in range(args.stage_runs):
+            for _ in range(4):
+                step(0)
+            for name, kms in bd.stage_times():
+                stages.setdefault(name, []).append(kms)
+    finally:
+        bd.stage_timing(False)
+    stages = {k: sum(v) / len(v) for k, v in stages.items()}
+    return w, ms, flops, nbytes, stages
 
 
 def bench_decode(args, rotate):
@@ -267,7 +307,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode and conv legs")
     ap.add_argument("--legs", default="prefill,decode,conv",
-                    help="comma-separated subset of prefill,decode,conv (for profiling runs)")
+                    help="comma-separated subset of prefill,decode,conv,copy (for profiling runs)")
+    ap.add_argument("--stage-runs", type=int, default=20, help="timed calls for the per-kernel durations")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; the scan "
@@ -292,6 +333,8 @@ def main():
         out.update(decode_record(args))
     if "conv" in legs:
         out.update(conv_record(args))
+    if "copy" in legs:
+        out.update(copy_record(args))
     if HOST_BOUND:
         out["host_bound_legs"] = HOST_BOUND
     if not args.no_cpu_baseline:
@@ -301,8 +344,25 @@ def main():
 
 
 def prefill_record(args):
-    w, ms, flops, nbytes = bench_prefill(args)
+    w, ms, flops, nbytes, stages = bench_prefill(args)
     tflops = flops / (ms * 1e-3) / 1e12
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/B
+    stage_rec = {}
+    for name, sms in stages.items():
+        sb, sf = stage_work(name, w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
+        stage_rec[name] = {"us": round(sms * 1e3, 2), "algorithmic_mb": round(sb / 1e6, 2),
+                           "gbs": round(sb / (sms * 1e-3) / 1e9, 1), "tflops": round(sf / (sms * 1e-3) / 1e12, 2)}
+    dom = max(stages, key=stages.get)
+    db, dfl = stage_work(dom, w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
+    dt_s = stages[dom] * 1e-3
+    if dfl / db < ridge:
+        roof = {"bound": "hbm", "achieved": round(db / dt_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(db / dt_s / 1e9 / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(dfl / dt_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dfl / dt_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    roof.update({"traffic": measured_traffic(dom), "kernel": dom, "algorithmic_bytes_per_launch": db,
+                 "algorithmic_flops_per_launch": dfl, "avg_launch_us": round(stages[dom] * 1e3, 2)})
     return {
         "metric": "SSD prefill tokens/s + TFLOPS (% MFMA peak); decode step GB/s (% HBM peak)",
         "value": round(w.B * w.L / (ms * 1e-3), 1),
@@ -321,11 +381,24 @@ def prefill_record(args):
         "prefill": {"tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                     "algorithmic_gflop": round(flops / 1e9, 3), "compulsory_mb": round(nbytes / 1e6, 2),
                     "gbs_compulsory": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                    "attainable_frac": round(tflops / min(PEAK_BF16_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3), 4)},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
-                     "kernel": "ssd_prefill (all stages of one call)"},
+                    "attainable_frac": round(tflops / min(PEAK_BF16_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3), 4),
+                    "kernels": stage_rec},
+        "roofline": roof,
     }
+
+
+def copy_record(args):
+    """A plain streaming kernel of known size, the reference for calibrating
+    rocprofv3's FETCH_SIZE / WRITE_SIZE counters: torch.neg reading 256 MiB
+    and writing 256 MiB (a kernel of its own name, unlike a memcpy)."""
+    import torch
+
+    n = 64 * 2**20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _timed(lambda _: torch.neg(src, out=dst), max(3, min(args.steps, 20)), 2, "copy")
+    return {"copy": {"bytes_read": 4 * n, "bytes_written": 4 * n, "us": round(ms * 1e3, 2),
+                     "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}}
 
 
 def decode_record(args):
@@ -341,7 +414,7 @@ def decode_record(args):
                                "graph_gbs": round(gbs(rgms), 1), "hbm_peak_frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
                                "eager_us_per_step": round(rms * 1e3, 3)}},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs(rgms), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
+                            "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_step_kernel"),
                             "kernel": "ssd_decode_step, rotated states, 4096 steps in one HIP graph"},
     }
 

@@ -35,9 +35,10 @@
  *     ssd_last_hip_error().  Faults inside a kernel surface at the caller's
  *     next synchronisation, as for any HIP library.  No C++ exception crosses
  *     this interface.
- *   - Re-entrancy: no global mutable state apart from the per-thread last
- *     HIP error; calls on different streams may run concurrently as long as
- *     their buffers do not overlap.
+ *   - Re-entrancy: no global mutable state apart from two per-host-thread
+ *     records (the last HIP error and the optional stage timing below);
+ *     calls on different streams may run concurrently as long as their
+ *     buffers do not overlap.
  *   - dtype: SSD_F32 or SSD_BF16, the storage type of the activations named
  *     "void*" below (x, Bm, Cm, y and the conv data).  dt, A_log, D and the
  *     SSM state are always fp32; all arithmetic accumulates in fp32.
@@ -91,8 +92,13 @@ enum {
  * multiple of Q).  L = 0 is allowed: y is untouched and final_state receives
  * init_state (or zeros).  Alignment: x, Bm, Cm, y, init_state, final_state
  * 16-byte aligned.  Limits: 1 <= P <= 256, 1 <= N <= 256, 16 <= Q <= 256
- * (Q a multiple of 16); bf16 with (P, N) = (64, 128) and Q in {64, 128, 256}
- * runs on MFMA, everything else on the fp32 vector path.
+ * (Q a multiple of 16).  bf16 with (P, N, Q) = (64, 128, 256) runs on MFMA
+ * (bf16 operands, fp32 accumulation, decay factors in fp32); every other
+ * shape runs on the fp32 vector path.  The MFMA path factors the decay
+ * exp(cs_l - cs_s) per 32-token tile; a chunk whose factors would leave the
+ * normal fp32 range (a token more than 60 from its tile reference in cumsum
+ * of dt*A, tile references more than 80 apart, dt <= 0, or |D/dt| > 1e30)
+ * is computed on an exact per-element path instead, automatically.
  */
 int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
                 const void *x, const float *dt, const float *A_log,
@@ -166,6 +172,21 @@ int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
 int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_state,
                       const void *xBC, const void *conv_w, const void *conv_b,
                       int activation, void *out, hipStream_t stream);
+
+/*
+ * Stage timing -- a profiling aid, kept per host thread.
+ * ssd_stage_timing(1) makes the following ssd_prefill calls of the calling
+ * thread launch each kernel with a pair of HIP events stamped when that
+ * kernel's dispatch starts and ends (events created once, on the device
+ * current at this call); ssd_stage_timing(0) stops it.  ssd_stage_times
+ * waits for the last such call, stores in *count the number of kernels it
+ * ran, and writes up to `capacity` of their durations in milliseconds, in
+ * launch order; ssd_stage_name(i) names kernel i of that call (NULL out of
+ * range).  Do not enable it while the stream is being captured into a graph.
+ */
+int ssd_stage_timing(int enable);
+int ssd_stage_times(float *ms, int capacity, int *count);
+const char *ssd_stage_name(int index);
 
 /* Static, human-readable text for a status code. */
 const char *ssd_status_string(int status);

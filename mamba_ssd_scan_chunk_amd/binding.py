@@ -32,6 +32,9 @@ SIGNATURES = {
     "ssd_prefill_workspace_bytes": (_sz, [_i] * 8),
     "ssd_decode_step": (_i, [_i] * 6 + [_p] * 8 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "conv_state_update": (_i, [_i] * 5 + [_p] * 4 + [_i, _p, _p]),
+    "ssd_stage_timing": (_i, [_i]),
+    "ssd_stage_times": (_i, [ctypes.POINTER(ctypes.c_float), _i, ctypes.POINTER(_i)]),
+    "ssd_stage_name": (ctypes.c_char_p, [_i]),
     "ssd_status_string": (ctypes.c_char_p, [_i]),
     "ssd_last_hip_error": (_i, []),
 }
@@ -179,3 +182,17 @@ def ssd_status_string(status: int) -> str:
 
 def ssd_last_hip_error() -> int:
     return lib().ssd_last_hip_error()
+
+
+def stage_timing(enable: bool) -> None:
+    """Turn per-kernel event timing of later ssd_prefill calls (this thread) on or off."""
+    _check("ssd_stage_timing", lib().ssd_stage_timing(1 if enable else 0))
+
+
+def stage_times() -> list:
+    """[(kernel name, ms)] of the last timed ssd_prefill call, after waiting for it."""
+    cap = 16
+    ms = (ctypes.c_float * cap)()
+    n = _i(0)
+    _check("ssd_stage_times", lib().ssd_stage_times(ms, cap, ctypes.byref(n)))
+    return [(lib().ssd_stage_name(i).decode(), float(ms[i])) for i in range(min(n.value, cap))]

@@ -668,19 +668,17 @@ long prefill_mfma_bt_elems_per_chunk() { return kBTChunk; }
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     const long nitems = (long)a.B * a.nchunks * a.H;
     if (nitems > 0x7fffffffL || (long)a.G * kK0Blocks > 65535 || a.nchunks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chunk_pack_mfma, dim3(a.nchunks, kK0Blocks * a.G, a.B), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    stage_begin();
+    hipError_t e = launch_stage("chunk_pack_mfma", chunk_pack_mfma, dim3(a.nchunks, kK0Blocks * a.G, a.B),
+                                dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_state_mfma, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
-    e = hipGetLastError();
+    e = launch_stage("chunk_state_mfma", chunk_state_mfma, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
-    hipLaunchKernelGGL(state_pass_bf16, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       a, total);
-    e = hipGetLastError();
+    e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, a, total);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_out_mfma, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
-    return hipGetLastError();
+    return launch_stage("chunk_out_mfma", chunk_out_mfma, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
 }
 
 }  // namespace ssd

@@ -87,11 +87,10 @@ hipError_t launch_state_pass(const PrefillArgs &a, hipStream_t s) {
     const long blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (blocks == 0) return hipSuccess;
-    if (vec4)
-        hipLaunchKernelGGL(state_pass_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, total);
-    else
-        hipLaunchKernelGGL(state_pass_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, total);
-    return hipGetLastError();
+    return vec4 ? launch_stage("state_pass", state_pass_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a,
+                               total)
+                : launch_stage("state_pass", state_pass_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a,
+                               total);
 }
 
 // dst[i] = src ? src[i] : 0 (the L = 0 case of a prefill; src == dst allowed).

@@ -186,22 +186,18 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
 
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s) {
     if (a.B > 65535 || a.H > 65535) return hipErrorInvalidConfiguration;
+    stage_begin();
     dim3 g1(a.nchunks, a.H, a.B);
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(chunk_state_vec<bf16_t>, g1, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(chunk_state_vec<float>, g1, dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = dtype == DT_BF16
+                       ? launch_stage("chunk_state_vec", chunk_state_vec<bf16_t>, g1, dim3(kThreads), 0, s, a)
+                       : launch_stage("chunk_state_vec", chunk_state_vec<float>, g1, dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
     e = launch_state_pass(a, s);
     if (e != hipSuccess) return e;
     const long nlt = (a.Q + LT - 1) / LT;
     dim3 g3((unsigned)(a.nchunks * nlt), a.H, a.B);
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(chunk_out_vec<bf16_t>, g3, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(chunk_out_vec<float>, g3, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    return dtype == DT_BF16 ? launch_stage("chunk_out_vec", chunk_out_vec<bf16_t>, g3, dim3(kThreads), 0, s, a)
+                            : launch_stage("chunk_out_vec", chunk_out_vec<float>, g3, dim3(kThreads), 0, s, a);
 }
 
 }  // namespace ssd

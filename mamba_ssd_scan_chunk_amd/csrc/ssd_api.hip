@@ -241,6 +241,64 @@ SSD_API int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_
     return hip_status(ssd::launch_conv_update(a, dtype, stream));
 }
 
+// ---- stage timing (per host thread)
+namespace {
+constexpr int kMaxStages = 8;
+struct StageTimer {
+    bool on = false, have_events = false;
+    int n = 0;  // kernels recorded for the last call
+    hipEvent_t start[kMaxStages], stop[kMaxStages];
+    const char *name[kMaxStages];
+};
+thread_local StageTimer g_timer;
+}  // namespace
+
+void ssd::stage_begin() { g_timer.n = 0; }
+
+bool ssd::stage_events(const char *kernel, hipEvent_t *start, hipEvent_t *stop) {
+    if (!g_timer.on || g_timer.n >= kMaxStages) return false;
+    *start = g_timer.start[g_timer.n];
+    *stop = g_timer.stop[g_timer.n];
+    g_timer.name[g_timer.n++] = kernel;
+    return true;
+}
+
+SSD_API int ssd_stage_timing(int enable) {
+    if (enable && !g_timer.have_events) {
+        int made = 0;
+        hipError_t e = hipSuccess;
+        for (; made < 2 * kMaxStages; ++made) {
+            e = hipEventCreate(made < kMaxStages ? &g_timer.start[made] : &g_timer.stop[made - kMaxStages]);
+            if (e != hipSuccess) break;
+        }
+        if (e != hipSuccess) {
+            for (int j = 0; j < made; ++j)
+                (void)hipEventDestroy(j < kMaxStages ? g_timer.start[j] : g_timer.stop[j - kMaxStages]);
+            return hip_status(e);
+        }
+        g_timer.have_events = true;
+    }
+    g_timer.on = enable != 0;
+    g_timer.n = 0;
+    return SSD_OK;
+}
+
+SSD_API int ssd_stage_times(float *ms, int capacity, int *count) {
+    if (!count || capacity < 0 || (capacity > 0 && !ms)) return SSD_ERR_INVALID_ARG;
+    const int n = g_timer.n;
+    *count = n;
+    for (int i = 0; i < n && i < capacity; ++i) {
+        hipError_t e = hipEventSynchronize(g_timer.stop[i]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_timer.start[i], g_timer.stop[i]);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return SSD_OK;
+}
+
+SSD_API const char *ssd_stage_name(int index) {
+    return (index >= 0 && index < g_timer.n) ? g_timer.name[index] : nullptr;
+}
+
 SSD_API const char *ssd_status_string(int status) {
     switch (status) {
         case SSD_OK: return "success";

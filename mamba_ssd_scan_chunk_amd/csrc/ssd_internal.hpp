@@ -2,6 +2,7 @@
 // Arguments reaching these launchers have already been validated.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -34,6 +35,25 @@ long prefill_mfma_gt_elems_per_chunk();
 long prefill_mfma_bt_elems_per_chunk();
 WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, int G, bool mfma);
 bool prefill_uses_mfma(int P, int N, int Q, int dtype);
+
+// Stage timing (profiling aid, per host thread).  stage_begin starts a new
+// record for one ssd_prefill call; stage_events hands out the start/stop
+// events of its next kernel (false when timing is off or the record is
+// full), which launch_stage passes to hipExtLaunchKernelGGL so that they
+// are stamped when that kernel's dispatch starts and ends.
+void stage_begin();
+bool stage_events(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
+
+template <typename Kernel, typename... Args>
+hipError_t launch_stage(const char *name, Kernel kernel, dim3 grid, dim3 block, size_t shm, hipStream_t s,
+                        Args... args) {
+    hipEvent_t e0, e1;
+    if (stage_events(name, &e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);

@@ -192,3 +192,14 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "ssd_oracle" not in text, f
+
+
+def test_stage_timing_queries_without_a_timed_call(lib):
+    """Before any timed ssd_prefill call there is nothing to report, and the
+    query rejects a missing count pointer; neither touches the device."""
+    n = ctypes.c_int(-1)
+    assert lib.ssd_stage_times(None, 0, ctypes.byref(n)) == bd.SSD_OK
+    assert n.value == 0
+    assert lib.ssd_stage_times(None, 0, None) == bd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_stage_times(None, 4, ctypes.byref(n)) == bd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_stage_name(0) is None and lib.ssd_stage_name(-1) is None

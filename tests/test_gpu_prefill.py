@@ -158,3 +158,22 @@ def test_long_context_prefill_sampled_heads(oracle):
         y_ref, fs_ref = oracle.ssd_scan(**sub)
         assert rel_err(y[b:b + 1, :, h:h + 1], y_ref) <= TOL_BF16, (b, h)
         assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
+
+
+@pytest.mark.parametrize("dtype,P,N,Q,kernels", [
+    ("bf16", 64, 128, 256, ["chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]),
+    ("f32", 16, 16, 64, ["chunk_state_vec", "state_pass", "chunk_out_vec"]),
+])
+def test_stage_timing_reports_each_kernel(dtype, P, N, Q, kernels):
+    d = synth.make_prefill(1, 700, 4, P, 1, N, dtype, seed=12)
+    announce("stage timing", dtype)
+    y0, f0 = _run(d, Q)
+    bd.stage_timing(True)
+    try:
+        y1, f1 = _run(d, Q)
+        st = bd.stage_times()
+    finally:
+        bd.stage_timing(False)
+    assert [name for name, _ in st] == kernels
+    assert all(ms > 0.0 for _, ms in st)
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)  # timing changes no result
