@@ -77,6 +77,10 @@ def stage_work(kernel, B, L, H, P, G, N, Q, esize=2):
     elif kernel == "chunk_state_mfma":
         nbytes = B * L * H * (P * esize + 4) + groups * Q * N * 2 + items * (P * N * 4 + 4)
         flops = B * H * sum(2 * q * N * P for q in qs)
+    elif kernel == "chunk_scan_mfma":
+        nbytes = (B * L * H * (P * esize + 4) + groups * Q * N * 2 + items * P * N * 2
+                  + B * H * P * N * 4)
+        flops = B * H * sum(2 * q * N * P + 2 * P * N for q in qs)
     elif kernel == "state_pass_bf16":
         nbytes = items * (P * N * 4 + 4 + P * N * 2) + B * H * P * N * 4
         flops = items * 2 * P * N

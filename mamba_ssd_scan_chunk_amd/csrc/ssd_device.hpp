@@ -34,14 +34,23 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 // ---------------------------------------------------------------- wave ops
 
-// Inclusive prefix sum across the 64 lanes of a wavefront.
+// Inclusive prefix sum across the 64 lanes of a wavefront, with DPP moves:
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes (lanes shifted in from
+// outside the row read 0), then row_bcast 15 adds the last lane of rows 0
+// and 2 to rows 1 and 3, and row_bcast 31 the last lane of row 1 to rows
+// 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift_add(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+    return v + __int_as_float(moved);
+}
 __device__ __forceinline__ float wave_inclusive_sum(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
+    v = dpp_shift_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_shift_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_shift_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_shift_add<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_shift_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_shift_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
