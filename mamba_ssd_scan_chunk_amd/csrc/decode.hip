@@ -8,15 +8,29 @@
 //
 // The step is bound by HBM bandwidth: the fp32 state (P*N*4 bytes per head)
 // is read and written once, everything else is tiny.  A workgroup owns one
-// (batch, head, block of PBLK state rows).  Each state row of N floats is
-// covered by N/4 consecutive lanes with one float4 each, so a wavefront
-// reads and writes 1 KiB contiguous per row pass; the readout sum over n is
-// a butterfly over those N/4 lanes.  The convolution of the PBLK x-channels
-// of the block and of the 2N B/C channels of its group is recomputed per
-// workgroup (a few hundred FMAs) so that no second kernel or grid-wide sync
-// is needed; the shifted windows go to a separate output buffer, written for
-// the x-channels by their owner and for the B/C channels by the first
-// block of the group's first head.
+// (batch, group, block of PBLK consecutive state rows); the rows of a group
+// are the flattened (head, p) pairs, contiguous in the state, x and y.  Each
+// state row of N floats is covered by N/4 consecutive lanes with one float4
+// each, so a wavefront reads and writes 1 KiB contiguous per row pass.
+//
+// Order of work in a workgroup:
+//  1. the small operands are loaded: per-row step constants and the conv
+//     operands (cached window, taps, bias, new input) of the PBLK x-channels
+//     of the block and the 2N B/C channels of its group;
+//  2. the state rows are loaded.  Vector-memory loads retire in issue
+//     order, so step 3 waits only for the loads of step 1 while the state
+//     is still on its way from HBM;
+//  3. the convolution is finished and its results go to LDS (the B/C
+//     channels are recomputed by every block of the group, a few hundred
+//     FMAs, so that no second kernel or grid-wide sync is needed); the
+//     shifted windows go to the separate output buffer, for the x-channels
+//     by their owner and for the B/C channels by the group's first block;
+//  4. each state row is updated and stored as soon as it arrives, and its
+//     partial readout sum kept; the RPT partial sums of a lane are reduced
+//     over the N/4 lanes of the row with a transposing butterfly (half of
+//     the rows move at each lane bit while more than one row is left), so a
+//     lane moves RPT - 1 + log2(N/4 / RPT) values instead of
+//     RPT * log2(N/4).
 #include "ssd_device.hpp"
 #include "ssd_internal.hpp"
 
@@ -31,44 +45,193 @@ struct DecodeShape {
     static constexpr int LPR = N / 4;                  // lanes per state row
     static constexpr int ROWS_PER_PASS = kThreads / LPR;
     static constexpr int PBLK = ROWS_PER_PASS * RPT;   // state rows per workgroup
+    static constexpr int NCH = PBLK + 2 * N;           // conv channels per workgroup (at most)
+    static constexpr int CH_ROUNDS = (NCH + kThreads - 1) / kThreads;
 };
 
-// Convolved value of conv channel `cidx` at this step (raw input `raw`); the
-// shifted window goes to conv_out when `write_out`.
-template <typename T, bool CONV>
-__device__ __forceinline__ float conv_channel(const DecodeArgs &a, long C, int b, long cidx, float raw, bool write_out) {
-    if (!CONV) return raw;
-    const int K = a.K;
+// ---- convolution of one channel, split into its loads and its arithmetic
+
+// The loads of step 1 must not be waited for before the state loads are
+// issued.  Any arithmetic on a loaded value placed above them (the compiler
+// is free to: a bf16 widening, a half-word extraction from a merged load, a
+// packing of two window values for one store) makes them wait.  So
+//  - window elements are loaded and stored one by one (no_merge keeps the
+//    compiler from fusing neighbours into one access that then needs
+//    extraction or packing), as raw bits;
+//  - after the state loads every loaded register passes through `settle`,
+//    which the compiler must treat as producing it there, so all the
+//    arithmetic comes after.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw bits of one element (bf16 zero-extended, fp32 as is) and their value.
+template <typename T> __device__ __forceinline__ uint32_t ld_bits(const T *p);
+template <> __device__ __forceinline__ uint32_t ld_bits<float>(const float *p) { return __float_as_uint(*p); }
+template <> __device__ __forceinline__ uint32_t ld_bits<bf16_t>(const bf16_t *p) { return *p; }
+// An empty statement that may touch memory: accesses are not merged across it.
+__device__ __forceinline__ void no_merge() { asm volatile("" ::: "memory"); }
+template <typename T> __device__ __forceinline__ float widen(uint32_t v);
+template <> __device__ __forceinline__ float widen<float>(uint32_t v) { return __uint_as_float(v); }
+template <> __device__ __forceinline__ float widen<bf16_t>(uint32_t v) { return __uint_as_float(v << 16); }
+template <typename T> __device__ __forceinline__ void st_bits(T *p, uint32_t v);
+template <> __device__ __forceinline__ void st_bits<float>(float *p, uint32_t v) { *p = __uint_as_float(v); }
+template <> __device__ __forceinline__ void st_bits<bf16_t>(bf16_t *p, uint32_t v) { *p = (bf16_t)v; }
+
+// Operands of one conv channel at this step, as loaded: the K-1 cached
+// inputs and the new input (win[K-1]), the K taps and the bias.
+template <int KM>
+struct ConvIn {
+    uint32_t win[KM];
+    uint32_t w[KM];
+    uint32_t bias;
+};
+
+// KT is the kernel width when fixed at compile time, 0 when it is taken from
+// the arguments (up to kMaxK).  With KT = 4 the taps of a channel are one
+// 8-byte (bf16) or 16-byte (fp32) load, in w[0..1] as bf16 pairs or in
+// w[0..3]; the launcher takes this path only for taps aligned to that size.
+// Loads are unconditional (the caller clamps the channel index): a load
+// under a branch is waited for at the end of the branch.
+template <typename T, bool CONV, int KT, int KM>
+__device__ __forceinline__ void conv_load(const DecodeArgs &a, long C, int b, long cidx, const T *raw,
+                                          ConvIn<KM> &in) {
+    if (!CONV) {
+        in.win[0] = ld_bits(raw);
+        return;
+    }
+    const int K = KT ? KT : a.K;
     const T *cin = (const T *)a.conv_in + ((long)b * C + cidx) * (K - 1);
     const T *w = (const T *)a.conv_w + cidx * K;
-    float win[kMaxK];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) win[k] = (k < K - 1) ? ld(cin + k) : (k == K - 1 ? raw : 0.0f);
-    float acc = a.conv_b ? ld((const T *)a.conv_b + cidx) : 0.0f;
+    for (int k = 0; k < KM; ++k) {
+        in.win[k] = (k < K - 1) ? ld_bits(cin + k) : (k == K - 1 ? ld_bits(raw) : 0u);
+        no_merge();
+    }
+    if constexpr (KT == 4 && sizeof(T) == 2) {
+        const u32x2 p = *(const u32x2 *)w;
+        in.w[0] = p.x;
+        in.w[1] = p.y;
+    } else if constexpr (KT == 4) {
+        const u32x4 p = *(const u32x4 *)w;
+        in.w[0] = p.x; in.w[1] = p.y; in.w[2] = p.z; in.w[3] = p.w;
+    } else {
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
-        if (k < K) acc = fmaf(ld(w + k), win[k], acc);
+        for (int k = 0; k < KM; ++k) in.w[k] = k < K ? ld_bits(w + k) : 0u;
+    }
+    // the bias is read from the taps when there is none, and not used
+    in.bias = ld_bits(a.conv_b ? (const T *)a.conv_b + cidx : w);
+}
+
+// The registers of the first nwin window values and nw tap words become the
+// outputs of an empty statement placed here.
+template <int KM>
+__device__ __forceinline__ void settle(ConvIn<KM> &in, int nwin, int nw) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+        if (k < nwin) asm volatile("" : "+v"(in.win[k]));
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+        if (k < nw) asm volatile("" : "+v"(in.w[k]));
+    asm volatile("" : "+v"(in.bias));
+}
+
+// Convolved value of the channel; its shifted window goes to conv_out when
+// `write_out`.
+template <typename T, bool CONV, int KT, int KM>
+__device__ __forceinline__ float conv_finish(const DecodeArgs &a, long C, int b, long cidx, const ConvIn<KM> &in,
+                                             bool write_out) {
+    if (!CONV) return widen<T>(in.win[0]);
+    const int K = KT ? KT : a.K;
+    float acc = a.conv_b ? widen<T>(in.bias) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        float wk;
+        if constexpr (KT == 4 && sizeof(T) == 2)
+            wk = __uint_as_float((k & 1) ? (in.w[k / 2] & 0xffff0000u) : (in.w[k / 2] << 16));
+        else
+            wk = widen<T>(in.w[k]);
+        if (k < K) acc = fmaf(wk, widen<T>(in.win[k]), acc);
+    }
     if (write_out) {
+        // the window moves by one token: raw bits, no rounding
         T *cout = (T *)a.conv_out + ((long)b * C + cidx) * (K - 1);
 #pragma unroll
-        for (int k = 0; k < kMaxK - 1; ++k)
-            if (k < K - 1) st(cout + k, win[k + 1]);
+        for (int k = 0; k < KM - 1; ++k)
+            if (k < K - 1) {
+                st_bits(cout + k, in.win[k + 1]);
+                no_merge();
+            }
     }
     return a.activation ? silu(acc) : acc;
 }
 
-// One workgroup per block of PBLK consecutive state rows of one (batch,
-// group): rows are the flattened (head, p) pairs of the group, contiguous in
-// the state, x and y, so a block may cover several heads and the 2N B/C
-// channels of the group are convolved once per block.  The state loads are
-// issued first so their HBM latency overlaps the convolution stage.
-template <typename T, int N, bool CONV, int RPT>
+// ---- readout reduction
+
+// The value that lane l receives from its partner across lane bit BIT, the
+// partner being l ^ 1, l ^ 2 (quad permutations), l ^ 7, l ^ 15 (the
+// half-row and row mirrors), l ^ 16, l ^ 32 (the permlane swaps).  The
+// mirrors also flip the lower bits; the reduction below only needs a
+// partner whose bit BIT differs and whose higher bits agree, and the masks
+// 1, 2, 7, 15, 16, 32 are independent, so every lane of a group is summed
+// exactly once.
+template <int BIT>
+__device__ __forceinline__ float lane_partner(float v, int lane) {
+    const int u = __float_as_int(v);
+    if constexpr (BIT == 0) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0xb1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+    } else if constexpr (BIT == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x4e, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+    } else if constexpr (BIT == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    } else if constexpr (BIT == 3) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x140, 0xf, 0xf, false));  // row_mirror
+    } else if constexpr (BIT == 4) {
+        // element 0: rows 0 and 2 in both rows of each pair; element 1: rows 1 and 3
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __int_as_float((lane & 16) ? r[0] : r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __int_as_float((lane & 32) ? r[0] : r[1]);
+    }
+}
+
+// Sums v[j] (row pass j of this lane) over the lanes that share bits above
+// BIT + 1 of the lane index, from lane bit BIT down to 0.  While M > 1 rows
+// are live, each step keeps the half of them selected by the lane's bit and
+// adds the partner's values of the same rows; `first` accumulates the first
+// live row.  On return v[0..M_end) hold totals of rows first .. first+M_end-1.
+template <int BIT, int M, int RPT>
+__device__ __forceinline__ void reduce_rows(float (&v)[RPT], int &first, int lane) {
+    if constexpr (BIT >= 0) {
+        if constexpr (M > 1) {
+            constexpr int HALF = M / 2;
+            const bool upper = (lane >> BIT) & 1;
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) {
+                const float keep = upper ? v[j + HALF] : v[j];
+                const float send = upper ? v[j] : v[j + HALF];
+                v[j] = keep + lane_partner<BIT>(send, lane);
+            }
+            first += upper ? HALF : 0;
+            reduce_rows<BIT - 1, HALF, RPT>(v, first, lane);
+        } else {
+            v[0] += lane_partner<BIT>(v[0], lane);
+            reduce_rows<BIT - 1, 1, RPT>(v, first, lane);
+        }
+    }
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+template <typename T, int N, bool CONV, int RPT, int KT>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     using S = DecodeShape<N, RPT>;
-    __shared__ float xs[S::PBLK];
+    static_assert(S::PBLK <= kThreads, "one thread per row of the block for the row constants");
+    constexpr int KM = KT ? KT : kMaxK;
+    __shared__ float2 rowc[S::PBLK];  // per row: dt * x, expm1(dt * A)
+    __shared__ float rowdx[S::PBLK];  // per row: D * x
     __shared__ float Bs[N];
     __shared__ float Cs[N];
-    __shared__ float hdt[S::PBLK], hdm1[S::PBLK], hD[S::PBLK];  // per head of the block
 
     const int P = a.P, H = a.H;
     const int hpg = H / a.G;
@@ -84,48 +247,80 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     const long xstride = a.in_stride ? a.in_stride : HP;
     const long bcstride = a.in_stride ? a.in_stride : GN;
     const long row_base = (long)b * HP + (long)g * GR + r0;  // row index in [B*H*P)
-    const int lr = threadIdx.x % S::LPR;
-    const int row0 = threadIdx.x / S::LPR;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int lr = tid % S::LPR;
+    const int row0 = tid / S::LPR;
     const int n0 = lr * 4;
 
-    float *sbase = a.state + row_base * N + n0;
-    float4 hv[RPT];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        const int pr = row0 + r * S::ROWS_PER_PASS;
-        hv[r] = pr < prows ? *(const float4 *)(sbase + (long)pr * N) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    // ---- per-head step constants, this block's x channels and the 2N B/C
-    //      channels of its group
-    const int hfirst = g * hpg + r0 / P;  // first head of the block
-    const int nheads = (r0 + prows - 1) / P - r0 / P + 1;
-    for (int i = threadIdx.x; i < nheads; i += kThreads) {
-        const int h = hfirst + i;
-        const float dtv = a.dt_t[(long)b * H + h];
-        hdt[i] = dtv;
-        hdm1[i] = expm1f(dtv * -expf(a.A_log[h]));
-        hD[i] = a.D ? a.D[h] : 0.0f;
-    }
+    // ---- 1. small operands
+    // row constants: thread t for row t of the block (clamped)
+    const int trow = min(tid, prows - 1);
+    const int th = g * hpg + (r0 + trow) / P;
+    const float t_dt = a.dt_t[(long)b * H + th];
+    const float t_alog = a.A_log[th];
+    const float t_Dv = a.D ? a.D[th] : 0.0f;
+    // conv channels: the block's x rows, then B, then C; thread tid takes
+    // channels tid + k * kThreads (clamped, the duplicates write nothing)
     const bool bc_writer = pb == 0;
     const long xch0 = (long)g * GR + r0;  // conv channel of the block's first row
     const T *xin = (const T *)a.x_t + b * xstride + xch0;
     const T *Bin = (const T *)a.B_t + b * bcstride + (long)g * N;
     const T *Cin = (const T *)a.C_t + b * bcstride + (long)g * N;
-    for (int i = threadIdx.x; i < prows + 2 * N; i += kThreads) {
+    const int nch = prows + 2 * N;
+    ConvIn<KM> cin[S::CH_ROUNDS];
+    long cidx[S::CH_ROUNDS];
+#pragma unroll
+    for (int k = 0; k < S::CH_ROUNDS; ++k) {
+        const int i = min(tid + k * kThreads, nch - 1);
+        const T *raw;
         if (i < prows) {
-            xs[i] = conv_channel<T, CONV>(a, C, b, xch0 + i, ld(xin + i), true);
+            cidx[k] = xch0 + i;
+            raw = xin + i;
         } else if (i < prows + N) {
-            const int n = i - prows;
-            Bs[n] = conv_channel<T, CONV>(a, C, b, HP + (long)g * N + n, ld(Bin + n), bc_writer);
+            cidx[k] = HP + (long)g * N + (i - prows);
+            raw = Bin + (i - prows);
         } else {
-            const int n = i - prows - N;
-            Cs[n] = conv_channel<T, CONV>(a, C, b, HP + GN + (long)g * N + n, ld(Cin + n), bc_writer);
+            cidx[k] = HP + GN + (long)g * N + (i - prows - N);
+            raw = Cin + (i - prows - N);
+        }
+        conv_load<T, CONV, KT, KM>(a, C, b, cidx[k], raw, cin[k]);
+    }
+
+    // ---- 2. state rows (clamped; rows past the block are not stored)
+    float *sbase = a.state + row_base * N + n0;
+    float4 hv[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int pr = min(row0 + r * S::ROWS_PER_PASS, prows - 1);
+        hv[r] = *(const float4 *)(sbase + (long)pr * N);
+    }
+    // nothing may be scheduled above this point that uses a step-1 value
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kWinRegs = CONV ? KM : 1;
+    constexpr int kTapRegs = !CONV ? 0 : (KT == 4 && sizeof(T) == 2) ? 2 : KM;
+#pragma unroll
+    for (int k = 0; k < S::CH_ROUNDS; ++k) settle(cin[k], kWinRegs, kTapRegs);
+
+    // ---- 3. convolution results and row constants to LDS
+#pragma unroll
+    for (int k = 0; k < S::CH_ROUNDS; ++k) {
+        const int i = tid + k * kThreads;
+        const bool valid = i < nch;
+        const bool is_x = i < prows;
+        const float v = conv_finish<T, CONV, KT, KM>(a, C, b, cidx[k], cin[k], valid && (is_x || bc_writer));
+        if (k == 0 && is_x) {
+            // thread t = row t: the channel just finished is x of row t
+            rowc[i] = make_float2(t_dt * v, expm1f(t_dt * -expf(t_alog)));
+            rowdx[i] = t_Dv * v;
+        } else if (valid && !is_x) {
+            if (i < prows + N) Bs[i - prows] = v;
+            else Cs[i - prows - N] = v;
         }
     }
     __syncthreads();
 
-    // ---- state update and readout
+    // ---- 4. state update, stores and readout
     // The update is evaluated as h + (expm1(dt*A) * h + dt*x*B), rounding the
     // state once per step.  Two forms that look equivalent drift over long
     // runs when the decay is within a few ulp of 1: exp(dt*A) * h (the fp32
@@ -135,30 +330,38 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     // state-sized rounding is of h plus a random increment.
     const float4 Bv = make_float4(Bs[n0], Bs[n0 + 1], Bs[n0 + 2], Bs[n0 + 3]);
     const float4 Cv = make_float4(Cs[n0], Cs[n0 + 1], Cs[n0 + 2], Cs[n0 + 3]);
-    T *yout = (T *)a.y_t + row_base;
+    float part[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int pr = row0 + r * S::ROWS_PER_PASS;
-        const bool valid = pr < prows;
-        const int hi = (r0 + (valid ? pr : 0)) / P - r0 / P;  // head of this row within the block
-        const float dtv = hdt[hi];
-        const float dm1 = hdm1[hi];
-        const float Dh = hD[hi];
-        const float xv = valid ? xs[pr] : 0.0f;
-        const float coef = dtv * xv;
+        const float2 rc = rowc[min(pr, prows - 1)];
+        const float coef = rc.x, dm1 = rc.y;
         float4 v = hv[r];
         v.x += fmaf(dm1, v.x, coef * Bv.x);
         v.y += fmaf(dm1, v.y, coef * Bv.y);
         v.z += fmaf(dm1, v.z, coef * Bv.z);
         v.w += fmaf(dm1, v.w, coef * Bv.w);
-        float part = Cv.x * v.x;
-        part = fmaf(Cv.y, v.y, part);
-        part = fmaf(Cv.z, v.z, part);
-        part = fmaf(Cv.w, v.w, part);
-        part = group_sum<S::LPR>(part);
-        if (valid) {
-            *(float4 *)(sbase + (long)pr * N) = v;
-            if (lr == 0) st(yout + pr, fmaf(Dh, xv, part));
+        float p = Cv.x * v.x;
+        p = fmaf(Cv.y, v.y, p);
+        p = fmaf(Cv.z, v.z, p);
+        p = fmaf(Cv.w, v.w, p);
+        part[r] = p;
+        if (pr < prows) *(float4 *)(sbase + (long)pr * N) = v;
+    }
+    constexpr int LB = ilog2(S::LPR);
+    constexpr int HALVINGS = ilog2(RPT) < LB ? ilog2(RPT) : LB;
+    constexpr int M_END = RPT >> HALVINGS;
+    int first = 0;
+    reduce_rows<LB - 1, RPT, RPT>(part, first, lane);
+    // lanes that differ only in the fully reduced low bits hold the same
+    // totals; the one with those bits zero writes
+    constexpr int LOW = LB - HALVINGS;
+    if ((lr & ((1 << LOW) - 1)) == 0) {
+        T *yout = (T *)a.y_t + row_base;
+#pragma unroll
+        for (int j = 0; j < M_END; ++j) {
+            const int pr = row0 + (first + j) * S::ROWS_PER_PASS;
+            if (pr < prows) st(yout + pr, part[j] + rowdx[pr]);
         }
     }
 }
@@ -170,10 +373,13 @@ hipError_t launch_nr(const DecodeArgs &a, hipStream_t s) {
     const long npb = (GR + S::PBLK - 1) / S::PBLK;
     const long blocks = (long)a.B * a.G * npb;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (a.conv_in)
-        hipLaunchKernelGGL((decode_step_kernel<T, N, true, RPT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    const bool taps_aligned = ((uintptr_t)a.conv_w & (4 * sizeof(T) - 1)) == 0;
+    if (a.conv_in && a.K == 4 && taps_aligned)
+        hipLaunchKernelGGL((decode_step_kernel<T, N, true, RPT, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else if (a.conv_in)
+        hipLaunchKernelGGL((decode_step_kernel<T, N, true, RPT, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_step_kernel<T, N, false, RPT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((decode_step_kernel<T, N, false, RPT, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -27,14 +27,9 @@ def _setup(B, H, P, G, N, K, dtype, steps, seed, variant="spec", with_bias=False
                 state0=state0, conv0=conv0)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("conv", [False, True])
-def test_decode_steps_match_oracle(oracle, dtype, N, conv):
-    B, H, P, G, K, steps = 2, 4, 20, 2, 4, 5
-    s = _setup(B, H, P, G, N, K, dtype, steps, seed=N + (100 if conv else 0), with_bias=conv)
+def _run_steps(oracle, B, H, P, G, N, K, dtype, steps, seed, conv):
+    s = _setup(B, H, P, G, N, K, dtype, steps, seed=seed, with_bias=conv)
     C = s["C"]
-    announce("decode", dtype, f"N={N}", f"conv={conv}")
     state = s["state0"].cuda()
     cin, cout = s["conv0"].cuda(), torch.empty_like(s["conv0"]).cuda()
     w = s["w"].cuda()
@@ -60,6 +55,33 @@ def test_decode_steps_match_oracle(oracle, dtype, N, conv):
             np.testing.assert_array_equal(f64(cout), new_conv)  # raw values, shifted exactly
             ref_conv = new_conv
             cin, cout = cout, cin
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("conv", [False, True])
+def test_decode_steps_match_oracle(oracle, dtype, N, conv):
+    """Small grid: blocks of 16-64 rows, ragged, heads of P=20 rows crossing
+    block boundaries, two groups."""
+    announce("decode", dtype, f"N={N}", f"conv={conv}")
+    _run_steps(oracle, 2, 4, 20, 2, N, 4, dtype, 5, N + (100 if conv else 0), conv)
+
+
+@pytest.mark.parametrize("K", [2, 3, 8])
+def test_decode_conv_widths(oracle, K):
+    """Conv widths other than 4 (the width taken from the arguments)."""
+    announce("decode conv width", K)
+    _run_steps(oracle, 2, 4, 20, 2, 128, K, "bf16", 3, 50 + K, True)
+
+
+@pytest.mark.parametrize("dtype,N,K", [("bf16", 16, 4), ("bf16", 32, 4), ("bf16", 64, 4), ("bf16", 128, 4),
+                                       ("f32", 128, 4), ("bf16", 128, 3), ("bf16", 256, 4)])
+def test_decode_large_grid(oracle, dtype, N, K):
+    """Enough blocks for the large-block launch (>= 1024 blocks of 4x the
+    small-grid rows), with P=20 so that heads cross blocks and the last
+    block of each group is ragged."""
+    announce("decode large grid", dtype, f"N={N}", f"K={K}")
+    _run_steps(oracle, 64, 16, 20, 2, N, K, dtype, 2, 200 + N + K, True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
