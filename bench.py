@@ -104,7 +104,7 @@ def measured_traffic(kernel):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != source_hash(rec.get("sources", [])):
+    if not rec.get("sources") or rec.get("source_hash") != source_hash(rec["sources"]):
         return None
     return rec.get("bytes_per_launch")
 
