@@ -77,15 +77,12 @@ def stage_work(kernel, B, L, H, P, G, N, Q, esize=2):
     elif kernel == "chunk_state_mfma":
         nbytes = B * L * H * (P * esize + 4) + groups * Q * N * 2 + items * (P * N * 4 + 4)
         flops = B * H * sum(2 * q * N * P for q in qs)
-    elif kernel == "chunk_scan_mfma":
-        nbytes = (B * L * H * (P * esize + 4) + groups * Q * N * 2 + items * P * N * 2
-                  + B * H * P * N * 4)
-        flops = B * H * sum(2 * q * N * P + 2 * P * N for q in qs)
     elif kernel == "state_pass_bf16":
-        nbytes = items * (P * N * 4 + 4 + P * N * 2) + B * H * P * N * 4
+        # plus C repacked into K3's operand order (read once, written once)
+        nbytes = items * (P * N * 4 + 4 + P * N * 2) + B * H * P * N * 4 + B * L * G * N * esize + groups * Q * N * 2
         flops = items * 2 * P * N
     elif kernel == "chunk_out_mfma":
-        nbytes = (B * L * H * (2 * P * esize + 4) + B * L * G * N * esize + items * P * N * 2
+        nbytes = (B * L * H * (2 * P * esize + 4) + groups * Q * N * 2 + items * P * N * 2
                   + groups * tile_bytes)
         flops = B * H * sum(P * q * (q + 1) + 2 * q * N * P for q in qs)
     else:

@@ -17,9 +17,12 @@
 // part of the masked product that does not depend on the head, shared by all
 // heads of the group), applies the causal mask, and stores it as bf16 in the
 // exact register order of the 32x32x16 MFMA accumulator; it also stores B in
-// the order of the MFMA B operand for the token contraction of K1.  K1 and K3
-// then run one workgroup per (batch, chunk, head) with small LDS footprints,
-// several per CU, and read those packed operands straight from L2.
+// the order of the MFMA B operand for the token contraction of K1 (the state
+// pass K2, a streaming kernel with spare issue slots, stores C in the order
+// of the B operand of h C^T in K3).  K1 and K3 then run one
+// workgroup per (batch, chunk, head) with small LDS footprints, several per
+// CU, and read those packed operands straight from L2, 1 KiB contiguous per
+// load instruction.
 //
 // Contractions over tokens need 8 consecutive tokens per lane in an operand,
 // while x is stored token-major: K1 and K3 transpose their x chunk through
@@ -204,9 +207,11 @@ __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a) {
             o0[e] = pack_bf16(acc[e * 2], acc[e * 2 + 1]);
             o1[e] = pack_bf16(acc[8 + e * 2], acc[8 + e * 2 + 1]);
         }
-        u32x4 *dst = (u32x4 *)(a.ws_gt + cg * kGTChunk) + ((long)tix * 64 + lane) * 2;
+        // [tile][half][lane]: each half of a tile is 1 KiB contiguous, one
+        // load instruction of K3
+        u32x4 *dst = (u32x4 *)(a.ws_gt + cg * kGTChunk) + (long)tix * 128 + lane;
         dst[0] = o0;
-        dst[1] = o1;
+        dst[64] = o1;
         return;
     }
 
@@ -408,18 +413,16 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) hv[k] = *(const u32x4 *)(hg + (tid + k * kThreads) * 8);
     }
-    const unsigned rs_c = (unsigned)a.G * kN * 2;  // C row stride in bytes
-    const __amdgpu_buffer_rsrc_t crs =
-        make_rsrc((const bf16_t *)a.Cm + (((long)b * a.L + t0) * a.G + g) * kN, (unsigned)(Qc - 1) * rs_c + kN * 2);
+    // C operands as K0 packed them: 1 KiB contiguous per load instruction
+    const u32x4 *ctp = (const u32x4 *)(a.ws_ct + cg * kBTChunk) + lane;
     auto load_c = [&](int lt, u32x4 (&cop)[8]) {
-        const unsigned off = (unsigned)(lt * 32 + li) * rs_c + 16 * lh;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) cop[kk] = buf_load16(crs, off + 32 * kk);
+        for (int kk = 0; kk < 8; ++kk) cop[kk] = ctp[(lt * 8 + kk) * 64];
     };
     u32x4 cop[8];
     load_c(ltA, cop);
-    const u32x4 *gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane * 2;
-    auto tile_ptr = [&](int si, int lt) { return gtp + gt_index(si, lt) * 128; };
+    const u32x4 *gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
+    auto tile_ptr = [&](int si, int lt) { return gtp + gt_index(si, lt) * 128; };  // halves at [0] and [64]
     // G^T tiles of steps k and k+1 (ring of 2), for both column tiles
     u32x4 gA[2][2], gB[2][2];
 #pragma unroll
@@ -427,9 +430,9 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
         const u32x4 *pa = tile_ptr(0, ltA);
         const u32x4 *pb = tile_ptr(k, ltB);
         gA[k][0] = pa[0];
-        gA[k][1] = pa[1];
+        gA[k][1] = pa[64];
         gB[k][0] = pb[0];
-        gB[k][1] = pb[1];
+        gB[k][1] = pb[64];
     }
 
     // ---- cumsum of dt*A within each 64-token wave (fp32), per-token factors
@@ -558,11 +561,11 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
             if (k + 1 <= ltB) {
                 const u32x4 *pb = tile_ptr(k + 1, ltB);
                 gB[(k + 1) & 1][0] = pb[0];
-                gB[(k + 1) & 1][1] = pb[1];
+                gB[(k + 1) & 1][1] = pb[64];
                 if (k + 1 <= ltA) {
                     const u32x4 *pa = tile_ptr(k + 1, ltA);
                     gA[(k + 1) & 1][0] = pa[0];
-                    gA[(k + 1) & 1][1] = pa[1];
+                    gA[(k + 1) & 1][1] = pa[64];
                 }
             }
             u32x4 xa[2][2];
@@ -619,7 +622,36 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
 // carried-in state h_{c-1} as bf16 (the MFMA operand of C h) and the final
 // state in fp32.  h + (dm1 * h + S) rounds the state once per chunk.
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long total) {
+// Blocks past the state blocks pack C for K3: block (b, c, g, q) writes token
+// tiles 2q, 2q+1 as [lt][kk][lane] 16 bytes = C[32 lt + li][16 kk + 8 lh ..
+// + 8] (tokens past the end as zero).
+__device__ __forceinline__ void pack_c(const PrefillArgs &a, long blk) {
+    const int q = (int)(blk % (kTiles / 2));
+    const long cg = blk / (kTiles / 2);  // (b * nchunks + c) * G + g
+    const int g = (int)(cg % a.G);
+    const long bc = cg / a.G;
+    const int c = (int)(bc % a.nchunks), b = (int)(bc / a.nchunks);
+    const int t0 = c * kQ, Qc = min(kQ, a.L - t0);
+    const unsigned rs = (unsigned)a.G * kN * 2;
+    const __amdgpu_buffer_rsrc_t crs =
+        make_rsrc((const bf16_t *)a.Cm + (((long)b * a.L + t0) * a.G + g) * kN, (unsigned)(Qc - 1) * rs + kN * 2);
+    u32x4 *ct = (u32x4 *)(a.ws_ct + cg * kBTChunk);
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = threadIdx.x + k * kThreads;
+        const int lt = 2 * q + (idx >> 9), kk = (idx >> 6) & 7, ln = idx & 63;
+        v[k] = buf_load16(crs, (unsigned)(lt * 32 + (ln & 31)) * rs + 32 * kk + 16 * (ln >> 5));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ct[2 * q * 8 * 64 + threadIdx.x + k * kThreads] = v[k];
+}
+
+__global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long total, long state_blocks) {
+    if ((long)blockIdx.x >= state_blocks) {
+        pack_c(a, (long)blockIdx.x - state_blocks);
+        return;
+    }
     const long e = (long)blockIdx.x * kThreads + threadIdx.x;  // float4 index
     if (e >= total) return;
     const long PN4 = (long)kP * kN / 4;
@@ -675,8 +707,11 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     e = launch_stage("chunk_state_mfma", chunk_state_mfma, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
-    e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, a, total);
+    const long state_blocks = (total + kThreads - 1) / kThreads;
+    const long pack_blocks = (long)a.B * a.nchunks * a.G * (kTiles / 2);
+    if (state_blocks + pack_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)(state_blocks + pack_blocks)),
+                     dim3(kThreads), 0, s, a, total, state_blocks);
     if (e != hipSuccess) return e;
     return launch_stage("chunk_out_mfma", chunk_out_mfma, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
 }

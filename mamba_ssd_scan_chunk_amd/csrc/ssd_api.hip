@@ -66,7 +66,7 @@ bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
 }
 
 WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, int G, bool mfma) {
-    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0};
+    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0};
     if (L <= 0) return w;
     const size_t nch = ((size_t)L + Q - 1) / Q;
     const size_t heads = (size_t)B * nch * H;
@@ -81,7 +81,8 @@ WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int 
     const size_t gt_bytes = mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t) : 0;
     w.off_bt = align_up(w.off_gt + gt_bytes, 256);
     const size_t bt_bytes = mfma ? groups * prefill_mfma_bt_elems_per_chunk() * sizeof(uint16_t) : 0;
-    w.total = align_up(w.off_bt + bt_bytes, 256);
+    w.off_ct = align_up(w.off_bt + bt_bytes, 256);
+    w.total = align_up(w.off_ct + bt_bytes, 256);  // C packed like B
     return w;
 }
 
@@ -156,6 +157,7 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
     a.ws_hb = mfma ? (uint16_t *)(ws + wl.off_hb) : nullptr;
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
+    a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
     hipError_t e = mfma ? ssd::launch_prefill_mfma(a, stream) : ssd::launch_prefill_vector(a, dtype, stream);
     return hip_status(e);
 }

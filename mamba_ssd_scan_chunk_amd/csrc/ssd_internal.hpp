@@ -24,12 +24,13 @@ struct PrefillArgs {
     float *ws_dec;  // [B, nchunks, H]: exp(sum of dt*A over the chunk) - 1
     double *ws_cs;  // [B, nchunks, H, Q]: in-chunk inclusive cumsum of dt*A (vector path)
     uint16_t *ws_hb;  // [B, nchunks, H, P, N] bf16: carried-in states (MFMA path)
-    uint16_t *ws_gt;  // [B, nchunks, G, tiles, lanes, 16] bf16: masked C B^T (MFMA path)
+    uint16_t *ws_gt;  // [B, nchunks, G, tiles, 2, lanes, 8] bf16: masked C B^T (MFMA path)
     uint16_t *ws_bt;  // [B, nchunks, G, Q*N] bf16: B in MFMA operand order (MFMA path)
+    uint16_t *ws_ct;  // [B, nchunks, G, Q*N] bf16: C in MFMA operand order (MFMA path)
 };
 
 struct WorkspaceLayout {
-    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, total;
+    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, total;
 };
 long prefill_mfma_gt_elems_per_chunk();
 long prefill_mfma_bt_elems_per_chunk();
