@@ -273,10 +273,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     const int g = h / (a.H / a.G);
     const long cg = (long)bc * a.G + g;
 
-    // every global load of this workgroup is issued before the cumsum
+    // every global load of this workgroup is issued before the cumsum, dt
+    // first: loads retire in issue order, so the cumsum waits for dt only
+    const float dtv = load_dt(a, b, t0, Qc, h, tid);
     u32x4 raw[8];
     load_x_raw(a, b, t0, Qc, h, raw, tid);
-    const float dtv = load_dt(a, b, t0, Qc, h, tid);
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[kQ / 16];
 #pragma unroll
@@ -403,11 +404,12 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
     const int g = h / (a.H / a.G);
     const long cg = (long)bc * a.G + g;
 
-    // ---- global loads, all issued before the cumsum: x, dt, h_{c-1}, the C
+    // ---- global loads, all issued before the cumsum: dt, x, h_{c-1}, the C
     // operands of column tile ltA and the first G^T tiles
+    // dt first: loads retire in issue order, so the cumsum waits for dt only
+    const float dtv = load_dt(a, b, t0, Qc, h, tid);
     u32x4 raw[8], hv[4];
     load_x_raw(a, b, t0, Qc, h, raw, tid);
-    const float dtv = load_dt(a, b, t0, Qc, h, tid);
     {
         const bf16_t *hg = a.ws_hb + (long)item * kP * kN;
 #pragma unroll
