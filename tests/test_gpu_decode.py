@@ -145,8 +145,11 @@ def test_decode_4096_steps_2p7b_shape(oracle, variant):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K", [2, 3, 4, 8])
 @pytest.mark.parametrize("T", [1, 2, 5, 17, 100])
-def test_conv_state_update_matches_oracle(oracle, dtype, K, T):
-    B, C = 2, 300
+@pytest.mark.parametrize("C", [300, 304])
+def test_conv_state_update_matches_oracle(oracle, dtype, K, T, C):
+    """C = 304: 16-byte channel groups for both dtypes; C = 300: one channel
+    per thread for bf16 (300 % 8 != 0), channel groups for fp32."""
+    B = 2
     xbc = synth.make_tokens(B, T, C, dtype, seed=T * 10 + K)
     w, bias = synth.make_conv(C, K, dtype, seed=K, with_bias=(T % 2 == 1))
     st0 = synth.make_tokens(B, K - 1, C, dtype, seed=K + 50).transpose(1, 2).contiguous()
@@ -158,6 +161,31 @@ def test_conv_state_update_matches_oracle(oracle, dtype, K, T):
     st_ref, out_ref = oracle.conv_update(st0, xbc, w, bias, T != 5)
     np.testing.assert_array_equal(f64(st), st_ref)
     assert rel_err(out, out_ref) <= (1e-6 if dtype == "f32" else 8e-3)
+
+
+@pytest.mark.parametrize("K", [3, 4])
+def test_conv_unaligned_tensors(oracle, K):
+    """Tensors at 2-byte offsets take the one-channel-per-thread form; same
+    result as the oracle."""
+    B, C, T = 2, 304, 37
+    xbc = synth.make_tokens(B, T, C, "bf16", seed=90 + K)
+    w, bias = synth.make_conv(C, K, "bf16", seed=91 + K, with_bias=True)
+    st0 = synth.make_tokens(B, K - 1, C, "bf16", seed=92 + K).transpose(1, 2).contiguous()
+    announce("conv unaligned", K)
+    # views one element into larger buffers: every pointer is 2 mod 16
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        v = buf[1:].view(t.shape)
+        v.copy_(t.cuda())
+        return v
+    st, xd, wd, bd_ = shifted(st0), shifted(xbc), shifted(w), shifted(bias)
+    outbuf = torch.empty(xbc.numel() + 1, dtype=xbc.dtype, device="cuda")
+    out = outbuf[1:].view(xbc.shape)
+    bd.conv_state_update(st, xd, wd, bd_, activation=1, out=out)
+    torch.cuda.synchronize()
+    st_ref, out_ref = oracle.conv_update(st0, xbc, w, bias, True)
+    np.testing.assert_array_equal(f64(st), st_ref)
+    assert rel_err(out, out_ref) <= 8e-3
 
 
 def test_conv_prompt_then_steps_equals_one_pass(oracle):
