@@ -160,6 +160,37 @@ def test_long_context_prefill_sampled_heads(oracle):
         assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
 
 
+@pytest.mark.slow
+def test_long_context_prefill_then_decode_sampled_heads(oracle):
+    """B=8, L=16384 2.7B-shaped layer, then 1024 cached decode steps: the
+    decode outputs and final state equal those of one prefill over all
+    L + 1024 tokens, checked against the oracle's full scan on sampled
+    (batch, head) pairs."""
+    w = synth.WORKLOADS["mamba2-2.7b-longctx"]
+    B, L, k, H, P, G, N = w.B, w.L, w.decode_steps, w.H, w.P, w.G, w.N
+    d = synth.make_prefill(B, L + k, H, P, G, N, w.dtype, seed=5)
+    announce("longctx prefill + decode", B, L, k)
+    dd = dev(d)
+    head = {kk: (v[:, :L].contiguous() if v.dim() > 1 else v) for kk, v in dd.items()}
+    _, state = bd.ssd_prefill(head["x"], head["dt"], head["A_log"], head["Bm"], head["Cm"], head["D"], Q=w.Q)
+    del head
+    xs = dd["x"][:, L:].reshape(B, k, H * P).transpose(0, 1).contiguous()
+    dts = dd["dt"][:, L:].transpose(0, 1).contiguous()
+    Bs = dd["Bm"][:, L:].reshape(B, k, G * N).transpose(0, 1).contiguous()
+    Cs = dd["Cm"][:, L:].reshape(B, k, G * N).transpose(0, 1).contiguous()
+    y_dec = torch.empty((k, B, H, P), dtype=dd["x"].dtype, device="cuda")
+    for t in range(k):
+        bd.ssd_decode_step(xs[t], dts[t], dd["A_log"], Bs[t], Cs[t], dd["D"], state, y_t=y_dec[t], G=G)
+    torch.cuda.synchronize()
+    del dd
+    for b, h in [(0, 3), (4, 40), (7, 77)]:
+        sub = dict(x=d["x"][b:b + 1, :, h:h + 1], dt=d["dt"][b:b + 1, :, h:h + 1], A_log=d["A_log"][h:h + 1],
+                   Bm=d["Bm"][b:b + 1], Cm=d["Cm"][b:b + 1], D=d["D"][h:h + 1])
+        y_ref, fs_ref = oracle.ssd_scan(**sub)
+        assert rel_err(y_dec[:, b, h], y_ref[0, L:, 0]) <= TOL_BF16, (b, h)
+        assert rel_err(state[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
+
+
 @pytest.mark.parametrize("dtype,P,N,Q,kernels", [
     ("bf16", 64, 128, 256, ["chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]),
     ("f32", 16, 16, 64, ["chunk_state_vec", "state_pass", "chunk_out_vec"]),
