@@ -416,7 +416,10 @@ def decode_record(args):
                                "graph_gbs": round(gbs(rgms), 1), "hbm_peak_frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
                                "eager_us_per_step": round(rms * 1e3, 3)}},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs(rgms), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_step_kernel"),
+                            "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
+                            # the committed counters were taken on the default (B = 16) workload
+                            "traffic": measured_traffic("decode_step_kernel")
+                            if args.decode_workload == "mamba2-2.7b-decode-b16" else None,
                             "kernel": "ssd_decode_step, rotated states, 4096 steps in one HIP graph"},
     }
 
