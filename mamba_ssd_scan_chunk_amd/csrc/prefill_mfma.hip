@@ -425,16 +425,20 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
     load_c(ltA, cop);
     const u32x4 *gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
     auto tile_ptr = [&](int si, int lt) { return gtp + gt_index(si, lt) * 128; };  // halves at [0] and [64]
-    // G^T tiles of steps k and k+1 (ring of 2), for both column tiles
-    u32x4 gA[2][2], gB[2][2];
-#pragma unroll
-    for (int k = 0; k < 1; ++k) {
+    // G^T tiles in flight: steps k, k+1 for column tile ltA (at most 4 steps),
+    // k .. k+2 for ltB (5 to 8 steps; one step ahead leaves the L2 latency
+    // exposed on the longer chain)
+    u32x4 gA[2][2], gB[3][2];
+    {
         const u32x4 *pa = tile_ptr(0, ltA);
-        const u32x4 *pb = tile_ptr(k, ltB);
-        gA[k][0] = pa[0];
-        gA[k][1] = pa[64];
-        gB[k][0] = pb[0];
-        gB[k][1] = pb[64];
+        const u32x4 *pb = tile_ptr(0, ltB);
+        gA[0][0] = pa[0];
+        gA[0][1] = pa[64];
+        gB[0][0] = pb[0];
+        gB[0][1] = pb[64];
+        const u32x4 *pb1 = tile_ptr(1, ltB);  // ltB >= 4
+        gB[1][0] = pb1[0];
+        gB[1][1] = pb1[64];
     }
 
     // ---- cumsum of dt*A within each 64-token wave (fp32), per-token factors
@@ -560,15 +564,15 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
 #pragma unroll
     for (int k = 0; k < kTiles; ++k) {
         if (k <= ltB) {
-            if (k + 1 <= ltB) {
-                const u32x4 *pb = tile_ptr(k + 1, ltB);
-                gB[(k + 1) & 1][0] = pb[0];
-                gB[(k + 1) & 1][1] = pb[64];
-                if (k + 1 <= ltA) {
-                    const u32x4 *pa = tile_ptr(k + 1, ltA);
-                    gA[(k + 1) & 1][0] = pa[0];
-                    gA[(k + 1) & 1][1] = pa[64];
-                }
+            if (k + 2 <= ltB) {
+                const u32x4 *pb = tile_ptr(k + 2, ltB);
+                gB[(k + 2) % 3][0] = pb[0];
+                gB[(k + 2) % 3][1] = pb[64];
+            }
+            if (k + 1 <= ltA) {
+                const u32x4 *pa = tile_ptr(k + 1, ltA);
+                gA[(k + 1) & 1][0] = pa[0];
+                gA[(k + 1) & 1][1] = pa[64];
             }
             u32x4 xa[2][2];
 #pragma unroll
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
                 }
             }
             {
-                u32x4 g2[2] = {gB[k & 1][0], gB[k & 1][1]};
+                u32x4 g2[2] = {gB[k % 3][0], gB[k % 3][1]};
                 if (exact) scale_tile_exact(g2, cst, dtt, cslB, k, lh);
                 if (k == ltB) add_diagonal(g2, dlB, li, lh);
 #pragma unroll
