@@ -166,6 +166,9 @@ def bench_prefill(args):
                        final_state=fs, workspace=ws)
 
     ms = _timed(step, args.steps, args.warmup, "prefill")
+    # the same calls captured in one HIP graph (as a serving loop would run
+    # them): the kernels are the same, the dispatch gaps between them may not be
+    graph_ms = _graph_timed(step, min(args.steps, 20))
     flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
     nbytes = prefill_bytes(w.B, w.L, w.H, w.P, w.G, w.N, 2 if w.dtype == "bf16" else 4)
     # per-kernel durations: HIP events the library records between its
@@ -182,7 +185,7 @@ def bench_prefill(args):
     finally:
         bd.stage_timing(False)
     stages = {k: sum(v) / len(v) for k, v in stages.items()}
-    return w, ms, flops, nbytes, stages
+    return w, ms, flops, nbytes, stages, graph_ms
 
 
 def bench_decode(args, rotate):
@@ -346,7 +349,7 @@ def main():
 
 
 def prefill_record(args):
-    w, ms, flops, nbytes, stages = bench_prefill(args)
+    w, ms, flops, nbytes, stages, graph_ms = bench_prefill(args)
     tflops = flops / (ms * 1e-3) / 1e12
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/B
     stage_rec = {}
@@ -384,6 +387,8 @@ def prefill_record(args):
                     "algorithmic_gflop": round(flops / 1e9, 3), "compulsory_mb": round(nbytes / 1e6, 2),
                     "gbs_compulsory": round(nbytes / (ms * 1e-3) / 1e9, 1),
                     "attainable_frac": round(tflops / min(PEAK_BF16_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3), 4),
+                    "graph": {"us_per_call": round(graph_ms * 1e3, 2),
+                              "tokens_per_s": round(w.B * w.L / (graph_ms * 1e-3), 1)},
                     "kernels": stage_rec},
         "roofline": roof,
     }
