@@ -74,6 +74,17 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(unsigned, v);
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (workgroup i to XCD i % 8),
+// each XCD with its own L2.  This maps workgroup i to an item so that every
+// XCD gets one contiguous range of items: the heads of a chunk then share one
+// L2 for the chunk's packed operands (B for K1; C and the G^T tiles for K3)
+// instead of each of the 8 L2s fetching them.
+__device__ __forceinline__ int xcd_item(int i, int total) {
+    const int x = i & 7, j = i >> 3;
+    const int q = total >> 3, r = total & 7;
+    return x * q + min(x, r) + j;
+}
+
 // index of causal tile (token tile si, column tile lt), si <= lt
 __device__ __forceinline__ int gt_index(int si, int lt) { return lt * (lt + 1) / 2 + si; }
 
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
-    const int item = blockIdx.x;
+    const int item = xcd_item(blockIdx.x, gridDim.x);  // grid = one workgroup per item
     const int h = item % a.H, bc = item / a.H;
     const int c = bc % a.nchunks, b = bc / a.nchunks;
     const int t0 = c * kQ;
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
     const int ltA = wave, ltB = kTiles - 1 - wave;
-    const int item = blockIdx.x;
+    const int item = xcd_item(blockIdx.x, gridDim.x);  // grid = one workgroup per item
     const int h = item % a.H, bc = item / a.H;
     const int c = bc % a.nchunks, b = bc / a.nchunks;
     const int t0 = c * kQ;
