@@ -35,6 +35,10 @@ CASES = [
     ("bf16-q256-ragged", 1, 700, 2, 64, 1, 128, 256, "bf16"),
     ("bf16-q128", 2, 384, 3, 64, 1, 128, 128, "bf16"),
     ("bf16-q64-groups", 1, 333, 4, 64, 2, 128, 64, "bf16"),
+    # MFMA path (P=64, N=128, Q=256): several groups and batch elements, an
+    # item count that is not a multiple of 8 (the XCD-aware item order)
+    ("bf16-mfma-groups", 2, 600, 4, 64, 2, 128, 256, "bf16"),
+    ("bf16-mfma-b3g3", 3, 513, 6, 64, 3, 128, 256, "bf16"),
 ]
 
 
