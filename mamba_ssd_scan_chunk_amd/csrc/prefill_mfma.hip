@@ -26,18 +26,15 @@
 //
 // Contractions over tokens need 8 consecutive tokens per lane in an operand,
 // while x is stored token-major: K1 and K3 transpose their x chunk through
-// registers into LDS once, folding in a per-token scale.  The decay of K3 is
-// factored per 32x32 tile (si, lt) of G^T as
-//     exp(cs_l - cs_s) dt_s = exp(cs_l - cs_end(si)) * [exp(cs_end(si) - cs_s) dt_s]
-// with cs_end(si) the cumsum at the end of token tile si: the bracket depends
-// on s only and is folded into x; the first factor is one value per lane
-// (its column l).  Off the diagonal tile both factors are <= 1; on it the
-// first is at most exp(32 max|dt*A|), finite in fp32, and the product is <= 1.
-// The accumulator order of a 32x32 tile (lane i: column i%32, rows
-// 8q + 4(i/32) + r) is a valid K order of 16 tokens for each pair of q, so G^T
-// tiles feed the A operand directly and x is read from LDS in that order.
+// registers into LDS once, folding in a per-token scale.  K3 factors the
+// decay exp(cs_l - cs_s) dt_s through a reference cumsum R_k per 32-token
+// tile (a Horner scheme over token tiles, described at K3), so the masked
+// C B^T tiles enter the MFMA exactly as K0 stored them.  The accumulator
+// order of a 32x32 tile (lane i: column i%32, rows 8q + 4(i/32) + r) is a
+// valid K order of 16 tokens for each pair of q, so a G^T tile is the B
+// operand of K3's MFMA as it stands and x'^T is read from LDS in that order.
 // D x is added through the diagonal of the masked product: with x' = v x and
-// M = u G^T, adding D / dt_l to G^T[l,l] before the scale by u_l adds
+// the output scaled by u, adding D / dt_l to G^T[l,l] adds
 // u_l v_l D/dt_l x_l = D x_l (u_l v_l = dt_l).
 #include <algorithm>
 
@@ -257,7 +254,8 @@ __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------------
-// K1: chunk states.  Grid (B * nchunks * H), workgroup = item (b, c, h):
+// K1: chunk states.  Grid (B * nchunks * H), workgroup = item (b, c, h) in
+// the XCD-aware order:
 //   S_c[p, n] = sum_s exp(cs_last - cs_s) dt_s x_s[p] B_s[n]
 // with x'' = exp(cs_last - cs_s) dt_s x_s <= dt_s folded into x in LDS.
 // Wave w computes the 64 x 32 slice of S for columns n in [32w, 32w + 32).
@@ -334,9 +332,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------------
-// K3: outputs.  Grid (nchunks * H, 1, B), one workgroup per (batch, chunk,
-// head).  The output is formed transposed, Y^T [P x Q]; wave w owns the
-// column (token) tiles w and 7-w and both 32-row feature tiles.
+// K3: outputs.  Grid (B * nchunks * H), one workgroup per item (batch,
+// chunk, head), in the XCD-aware order.  The output is formed transposed,
+// Y^T [P x Q]; wave w owns the column (token) tiles w and 7-w and both
+// 32-row feature tiles.
 //
 // Decay bookkeeping.  R_k is the cumsum at the 16th token of token tile k.
 // With
@@ -389,8 +388,8 @@ __device__ __forceinline__ void add_diagonal(u32x4 (&gt)[2], float dl, int li, i
     for (int k = 0; k < 8; ++k) gt[k >> 2][k & 3] = (widx == k) ? w2 : gt[k >> 2][k & 3];
 }
 
-// Grid (B * nchunks * H): workgroup = item (b, c, h), h fastest.  Wave w
-// owns column tiles ltA = w and ltB = 7 - w and processes them side by side:
+// Item (b, c, h), h fastest, from xcd_item.  Wave w owns column tiles
+// ltA = w and ltB = 7 - w and processes them side by side:
 // step k applies token tile k to both (while k <= lt), so the two Horner
 // chains of a wave (four accumulators) hide each other's MFMA -> VALU -> MFMA
 // latency, and the x'^T operands of token tile k are read once for both.

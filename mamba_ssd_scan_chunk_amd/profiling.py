@@ -19,6 +19,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -28,11 +29,39 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 4 * 64 * 2**20  # bench.py copy leg: bytes read and bytes written per dispatch
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that an edit of comments alone keeps a measurement valid.  String and
+    character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_hash(files) -> str:
+    """Hash of the code (not the comments) of `files`, relative to the
+    repository root."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
