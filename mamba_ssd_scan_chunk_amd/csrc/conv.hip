@@ -19,7 +19,8 @@
 namespace ssd {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // one-channel form
+constexpr int kVThreads = 64;  // channel-group form: one wave per workgroup (fewer idle lanes at the ragged end)
 constexpr int kMaxK = 8;
 constexpr int kTB = 16;  // tokens per thread, one-channel form (>= kMaxK - 1)
 constexpr int kTBV = 8;  // tokens per thread, channel-group form
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void conv_update_kernel(ConvArgs a) {
 }
 
 // Vector form, for C a multiple of V = 16 / sizeof(T) and 16-byte aligned
-// tensors: a thread owns V consecutive channels, so every token load and
+// tensors (workgroups of one wave): a thread owns V consecutive channels, so every token load and
 // output store is 16 bytes per lane (1 KiB per wave instruction) and the
 // taps, bias and cache of its channels are a few 16-byte loads.  K is a
 // template argument, so the window lives in registers.  The SiLU of the bf16
@@ -128,11 +129,11 @@ template <> struct Vec16<float> {
 };
 
 template <typename T, int K>
-__global__ __launch_bounds__(kThreads) void conv_update_vec(ConvArgs a) {
+__global__ __launch_bounds__(kVThreads) void conv_update_vec(ConvArgs a) {
     using VT = Vec16<T>;
     constexpr int V = VT::V;
     const long ngrp = a.C / V;
-    const long grp = (long)blockIdx.x * kThreads + threadIdx.x;
+    const long grp = (long)blockIdx.x * kVThreads + threadIdx.x;
     if (grp >= ngrp) return;
     const int tb = blockIdx.y, b = blockIdx.z;
     const int T_ = a.T;
@@ -235,13 +236,13 @@ __global__ __launch_bounds__(kThreads) void conv_update_vec(ConvArgs a) {
 template <typename T>
 hipError_t launch_vec(const ConvArgs &a, dim3 grid, hipStream_t s) {
     switch (a.K) {
-        case 2: hipLaunchKernelGGL((conv_update_vec<T, 2>), grid, dim3(kThreads), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((conv_update_vec<T, 3>), grid, dim3(kThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((conv_update_vec<T, 4>), grid, dim3(kThreads), 0, s, a); break;
-        case 5: hipLaunchKernelGGL((conv_update_vec<T, 5>), grid, dim3(kThreads), 0, s, a); break;
-        case 6: hipLaunchKernelGGL((conv_update_vec<T, 6>), grid, dim3(kThreads), 0, s, a); break;
-        case 7: hipLaunchKernelGGL((conv_update_vec<T, 7>), grid, dim3(kThreads), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((conv_update_vec<T, 8>), grid, dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((conv_update_vec<T, 2>), grid, dim3(kVThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((conv_update_vec<T, 3>), grid, dim3(kVThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((conv_update_vec<T, 4>), grid, dim3(kVThreads), 0, s, a); break;
+        case 5: hipLaunchKernelGGL((conv_update_vec<T, 5>), grid, dim3(kVThreads), 0, s, a); break;
+        case 6: hipLaunchKernelGGL((conv_update_vec<T, 6>), grid, dim3(kVThreads), 0, s, a); break;
+        case 7: hipLaunchKernelGGL((conv_update_vec<T, 7>), grid, dim3(kVThreads), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((conv_update_vec<T, 8>), grid, dim3(kVThreads), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -260,7 +261,9 @@ hipError_t launch_conv_update(const ConvArgs &a, int dtype, hipStream_t s) {
         aligned16(a.bias) && aligned16(a.out)) {
         const long tblocks = vblocks;
         const long ngrp = a.C / V;
-        const dim3 grid((unsigned)((ngrp + kThreads - 1) / kThreads), (unsigned)tblocks, a.B);
+        const long gblocks = (ngrp + kVThreads - 1) / kVThreads;
+        if (gblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)gblocks, (unsigned)tblocks, a.B);
         return dtype == DT_BF16 ? launch_vec<bf16_t>(a, grid, s) : launch_vec<float>(a, grid, s);
     }
     const long tblocks = (a.T + kTB - 1) / kTB;
