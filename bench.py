@@ -412,6 +412,18 @@ def decode_record(args):
     dw, dms, gms, dbytes, _ = bench_decode(args, rotate=False)
     _, rms, rgms, _, nrot = bench_decode(args, rotate=True)
     gbs = lambda ms: dbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    # the other batch size of the stated decode workload, in one HIP graph
+    other = {"mamba2-2.7b-decode-b16": "mamba2-2.7b-decode-b1",
+             "mamba2-2.7b-decode-b1": "mamba2-2.7b-decode-b16"}.get(args.decode_workload)
+    extra = {}
+    if other is not None:
+        oargs = argparse.Namespace(**vars(args))
+        oargs.decode_workload = other
+        oargs.decode_steps = min(args.decode_steps, 1024)
+        ow, _, ogms, obytes, _ = bench_decode(oargs, rotate=False)
+        extra = {"other_batch": {"workload": ow.name, "batch": ow.B, "steps": oargs.decode_steps,
+                                 "graph_us_per_step": round(ogms * 1e3, 3),
+                                 "gbs": round(obytes / (ogms * 1e-3) / 1e9, 1)}}
     return {
         "decode": {"workload": dw.name, "batch": dw.B, "steps": args.decode_steps, "bytes_per_step": dbytes,
                    "graph": {"us_per_step": round(gms * 1e3, 3), "steps_per_s": round(1e3 / gms, 1),
@@ -419,7 +431,7 @@ def decode_record(args):
                    "eager": {"us_per_step": round(dms * 1e3, 3), "gbs": round(gbs(dms), 1)},
                    "rotated": {"states": nrot, "graph_us_per_step": round(rgms * 1e3, 3),
                                "graph_gbs": round(gbs(rgms), 1), "hbm_peak_frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
-                               "eager_us_per_step": round(rms * 1e3, 3)}},
+                               "eager_us_per_step": round(rms * 1e3, 3)}, **extra},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs(rgms), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
                             # the committed counters were taken on the default (B = 16) workload
