@@ -67,6 +67,13 @@ def test_decode_steps_match_oracle(oracle, dtype, N, conv):
     _run_steps(oracle, 2, 4, 20, 2, N, 4, dtype, 5, N + (100 if conv else 0), conv)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_largest_head(oracle, dtype):
+    """The largest shape the decode step takes: P = 1024, N = 256, K = 8."""
+    announce("decode largest head", dtype)
+    _run_steps(oracle, 2, 2, 1024, 1, 256, 8, dtype, 3, 77, True)
+
+
 @pytest.mark.parametrize("K", [2, 3, 8])
 def test_decode_conv_widths(oracle, K):
     """Conv widths other than 4 (the width taken from the arguments)."""

@@ -39,6 +39,10 @@ CASES = [
     # item count that is not a multiple of 8 (the XCD-aware item order)
     ("bf16-mfma-groups", 2, 600, 4, 64, 2, 128, 256, "bf16"),
     ("bf16-mfma-b3g3", 3, 513, 6, 64, 3, 128, 256, "bf16"),
+    # the largest P, N, Q the vector path takes, and the smallest Q
+    ("f32-max-dims", 1, 300, 1, 256, 1, 256, 256, "f32"),
+    ("bf16-max-dims", 1, 270, 1, 256, 1, 256, 256, "bf16"),
+    ("f32-min-q", 1, 50, 2, 1, 1, 1, 16, "f32"),
 ]
 
 
