@@ -408,6 +408,39 @@ def copy_record(args):
                      "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}}
 
 
+def cached_vs_recompute(args, cached_step_ms):
+    """The cached decode step against recomputing the sequence: conv over the
+    L + 1 tokens plus the SSD prefill of L + 1 tokens, for the same B = 1
+    layer (the comparison behind the pages' cached-decode speedup)."""
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS["mamba2-2.7b-decode-b1"]
+    L1 = w.L + 1
+    C, K = w.conv_channels, w.K
+    d = {k: v.cuda() for k, v in synth.make_prefill(w.B, L1, w.H, w.P, w.G, w.N, w.dtype, seed=8).items()}
+    xbc = synth.make_tokens(w.B, L1, C, w.dtype, seed=9).cuda()
+    cw, _ = synth.make_conv(C, K, w.dtype, seed=10)
+    cw = cw.cuda()
+    st = torch.zeros((w.B, C, K - 1), dtype=xbc.dtype, device="cuda")
+    out = torch.empty_like(xbc)
+    y = torch.empty_like(d["x"])
+    code = bd.SSD_BF16 if w.dtype == "bf16" else bd.SSD_F32
+    ws = torch.empty(bd.ssd_prefill_workspace_bytes(w.B, L1, w.H, w.P, w.G, w.N, w.Q, code),
+                     dtype=torch.uint8, device="cuda")
+
+    def recompute(_):
+        st.zero_()
+        bd.conv_state_update(st, xbc, cw, activation=1, out=out)
+        bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], None, Q=w.Q, y=y, workspace=ws)
+
+    ms = _graph_timed(recompute, 10)
+    return {"workload": w.name, "tokens": L1, "recompute_us": round(ms * 1e3, 2),
+            "cached_step_us": round(cached_step_ms * 1e3, 3), "speedup": round(ms / cached_step_ms, 1)}
+
+
 def decode_record(args):
     dw, dms, gms, dbytes, _ = bench_decode(args, rotate=False)
     _, rms, rgms, _, nrot = bench_decode(args, rotate=True)
@@ -424,6 +457,9 @@ def decode_record(args):
         extra = {"other_batch": {"workload": ow.name, "batch": ow.B, "steps": oargs.decode_steps,
                                  "graph_us_per_step": round(ogms * 1e3, 3),
                                  "gbs": round(obytes / (ogms * 1e-3) / 1e9, 1)}}
+    b1_ms = gms if dw.B == 1 else (ogms if other is not None else None)
+    if b1_ms is not None:
+        extra["cached_vs_recompute"] = cached_vs_recompute(args, b1_ms)
     return {
         "decode": {"workload": dw.name, "batch": dw.B, "steps": args.decode_steps, "bytes_per_step": dbytes,
                    "graph": {"us_per_step": round(gms * 1e3, 3), "steps_per_s": round(1e3 / gms, 1),
