@@ -13,6 +13,7 @@ Distributions (``N(mu, v)`` has variance ``v``):
     Bm, Cm ~ N(0, 1/N)
     D      ~ N(0, 1)
     conv_w ~ N(0, 0.02),  raw conv inputs ~ N(0, 1)
+    dt_raw ~ N(0, 1), dt_bias ~ U(ln 1e-3, ln 0.1)   (raw step-size projection)
 Variants: "spec" (as above), "d0" (D = 0, so the output is the SSM term
 alone), "slow" (A_log ~ U(-7, -4) and dt = 1e-3, so state survives across
 thousands of tokens and every chunk hand-off matters), "steep" (A_log ~
@@ -120,6 +121,17 @@ def make_prefill(B, L, H, P, G, N, dtype="f32", seed=0, variant="spec"):
         x=_store(x, dtype), dt=torch.from_numpy(dt), A_log=torch.from_numpy(A_log),
         Bm=_store(Bm, dtype), Cm=_store(Cm, dtype), D=torch.from_numpy(D),
     )
+
+
+def make_dt_raw(shape, H, seed=0):
+    """A raw step-size projection dt_raw [*shape, H] ~ N(0, 1) and a per-head
+    bias dt_bias [H] ~ U(ln 1e-3, ln 0.1), both fp32.  With bounds 1e-3 and
+    0.1 the preprocessed step lands below, inside and above that range.
+    Draw order: dt_raw, dt_bias."""
+    rng = np.random.default_rng(seed)
+    raw = _normal(rng, tuple(shape) + (H,))
+    bias = rng.uniform(math.log(1e-3), math.log(0.1), size=H).astype(np.float32)
+    return torch.from_numpy(raw), torch.from_numpy(bias)
 
 
 def make_state(B, H, P, N, seed=0, scale=1.0):

@@ -13,8 +13,10 @@ bqwf.cn article on the compiler-first Mamba-2 implementation §1.1, §2.1,
     y_t = h_t . C_t + D_h * x_t                                      [P]
 
 with A_h = -exp(A_log[h]), plus the depthwise causal convolution over a
-(K-1)-token window cache.  ``ssd_scan`` is the prefill, ``decode_step`` is one
-step of the same recurrence after one step of the convolution cache.
+(K-1)-token window cache and the step-size chain dt = clip(softplus(dt_raw +
+dt_bias), dt_min, dt_max) of §1.2 (``dt_from_raw``).  ``ssd_scan`` is the
+prefill, ``decode_step`` is one step of the same recurrence after one step of
+the convolution cache.
 
 All arithmetic is in C (``ssd_oracle.c``), double precision, token by token.
 Every function here only marshals arrays.  Pins that tie this oracle to the
@@ -59,6 +61,9 @@ def _load():
         lib.oracle_ssd_scan.argtypes = [ctypes.c_int] * 6 + [_dp] * 9 + [ctypes.c_int]
         lib.oracle_conv_update.restype = ctypes.c_int
         lib.oracle_conv_update.argtypes = [ctypes.c_int] * 4 + [_dp] * 4 + [ctypes.c_int, _dp]
+        lib.oracle_dt_from_raw.restype = ctypes.c_int
+        lib.oracle_dt_from_raw.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _dp, ctypes.c_double,
+                                           ctypes.c_double, _dp]
         _lib = lib
     return _lib
 
@@ -114,6 +119,25 @@ def ssd_scan(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, want_y=True,
     if rc != 0:
         raise ValueError(f"oracle_ssd_scan failed ({rc})")
     return y, fs
+
+
+def dt_from_raw(dt_raw, dt_bias=None, dt_min=0.0, dt_max=float("inf")):
+    """Step size from a raw projection: clip(softplus(dt_raw + dt_bias[h]),
+    dt_min, dt_max), the softplus -> clip chain of bqwf.cn §1.2.
+
+    dt_raw [..., H] (any leading shape), dt_bias [H] or None (0).  Returns a
+    float64 array of dt_raw's shape.
+    """
+    raw = _f64(dt_raw)
+    H = raw.shape[-1]
+    bias = _f64(dt_bias)
+    assert bias is None or bias.shape == (H,)
+    out = np.empty_like(raw)
+    rc = _load().oracle_dt_from_raw(raw.size // H, H, _ptr(raw), _ptr(bias), float(dt_min), float(dt_max),
+                                    _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_dt_from_raw failed ({rc})")
+    return out
 
 
 def conv_update(conv_state, xBC, w, bias=None, activation=False):

@@ -193,3 +193,28 @@ int oracle_conv_update(int B, int T, int C, int K, double *conv_state,
     free(win);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Step-size preprocessing                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The chain that bqwf.cn §1.2 names before the decay (softplus, then clip,
+ * then exp), as the step size is formed from a raw projection:
+ *   u        = dt_raw[i] + dt_bias[h]          (bias 0 when absent)
+ *   dt[i]    = min(max(softplus(u), dt_min), dt_max)
+ *   softplus(u) = log(1 + exp(u)), written max(u, 0) + log1p(exp(-|u|)) so
+ *   that it neither overflows nor loses the small tail for large |u|.
+ * dt_raw and dt are [n, H] (h = i % H).  dt_max may be +inf.
+ */
+int oracle_dt_from_raw(long n, int H, const double *dt_raw, const double *dt_bias,
+                       double dt_min, double dt_max, double *dt)
+{
+    if (n < 0 || H <= 0 || !dt_raw || !dt || !(dt_min <= dt_max)) return -1;
+    for (long i = 0; i < n * H; ++i) {
+        const double u = dt_raw[i] + (dt_bias ? dt_bias[i % H] : 0.0);
+        const double sp = (u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u)));
+        dt[i] = fmin(fmax(sp, dt_min), dt_max);
+    }
+    return 0;
+}

@@ -12,8 +12,11 @@ fails at least one of them:
   * chunk-size invariance (segmented runs, and the numpy chunked form);
   * prefill-then-decode equals one longer prefill;
   * linearity, causality, independence of heads/batch, group broadcasting;
-  * convolution: one-hot taps, numpy.convolve, torch SiLU.
+  * convolution: one-hot taps, numpy.convolve, torch SiLU;
+  * step-size chain: softplus(0) = ln 2, softplus(u) - softplus(-u) = u,
+    400-digit decimal log(1 + e^u), the per-head bias index, clip bounds.
 """
+import decimal
 import json
 import math
 import os
@@ -348,3 +351,53 @@ def test_oracle_rejects_bad_groups(oracle):
     d = _inputs(B=1, L=4, H=3, P=2, G=2, N=2, seed=44)  # G does not divide H
     with pytest.raises(ValueError):
         oracle.ssd_scan(**d)
+
+
+# ---------------------------------------------------------------------------
+# Step-size chain dt = clip(softplus(dt_raw + dt_bias[h]), dt_min, dt_max)
+# ---------------------------------------------------------------------------
+
+def _softplus_decimal(u):
+    """log(1 + e^u) in 400-digit decimal arithmetic (independent of libm; enough
+    digits that 1 + e^u keeps e^u down to u = -700)."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 400
+        return float((decimal.Decimal(u).exp() + 1).ln())
+
+
+def test_dt_softplus_at_zero_is_ln2(oracle):
+    assert oracle.dt_from_raw(np.zeros((1, 1)))[0, 0] == pytest.approx(math.log(2.0), rel=1e-15)
+
+
+def test_dt_softplus_matches_decimal_and_odd_part_identity(oracle):
+    u = np.concatenate([np.linspace(-40.0, 40.0, 161), [-700.0, -1e-8, 1e-8, 700.0]])
+    sp = oracle.dt_from_raw(u[:, None])[:, 0]
+    ref = np.array([_softplus_decimal(v) for v in u])
+    np.testing.assert_allclose(sp, ref, rtol=2e-15, atol=0.0)
+    sp_neg = oracle.dt_from_raw(-u[:, None])[:, 0]
+    np.testing.assert_allclose(sp - sp_neg, u, rtol=1e-14, atol=1e-15)   # softplus(u) - softplus(-u) = u
+    assert np.all(sp > 0.0) and np.all(np.diff(sp[:161]) > 0.0)           # positive, increasing
+
+
+def test_dt_bias_is_per_head_on_the_last_axis(oracle):
+    H = 5
+    bias = np.array([-3.0, -1.0, 0.0, 0.5, 2.0])
+    raw = np.zeros((2, 3, H))
+    raw[1, 2, :] = 1.0
+    dt = oracle.dt_from_raw(raw, bias)
+    for h in range(H):
+        np.testing.assert_allclose(dt[0, 0, h], _softplus_decimal(bias[h]), rtol=2e-15)
+        np.testing.assert_allclose(dt[1, 2, h], _softplus_decimal(bias[h] + 1.0), rtol=2e-15)
+
+
+def test_dt_clip_bounds(oracle):
+    u = np.array([[-800.0, -8.0, -4.0, -2.0, 0.0, 3.0, 800.0]])
+    lo, hi = 1e-3, 0.1
+    dt = oracle.dt_from_raw(u, None, lo, hi)[0]
+    ref = np.clip([_softplus_decimal(v) if abs(v) < 100 else max(v, 0.0) for v in u[0]], lo, hi)
+    np.testing.assert_allclose(dt, ref, rtol=2e-15, atol=0.0)
+    assert dt[0] == lo and dt[-1] == hi and lo < dt[2] < hi
+    # equal bounds pin every value; an inverted range is rejected
+    np.testing.assert_array_equal(oracle.dt_from_raw(u, None, 0.05, 0.05), np.full_like(u, 0.05))
+    with pytest.raises(ValueError):
+        oracle.dt_from_raw(u, None, 0.2, 0.1)
