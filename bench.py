@@ -169,6 +169,15 @@ def bench_prefill(args):
     # the same calls captured in one HIP graph (as a serving loop would run
     # them): the kernels are the same, the dispatch gaps between them may not be
     graph_ms = _graph_timed(step, min(args.steps, 20))
+    # the same calls with the step passed raw: softplus(dt + bias) clipped to
+    # [1e-3, 0.1] inside the kernels
+    raw, dt_bias = (t.cuda() for t in synth.make_dt_raw((w.B, w.L), w.H, seed=3))
+
+    def step_raw(_):
+        bd.ssd_prefill(d["x"], raw, d["A_log"], d["Bm"], d["Cm"], d["D"], None, Q=w.Q, y=y, final_state=fs,
+                       workspace=ws, dt_raw=True, dt_bias=dt_bias, dt_min=1e-3, dt_max=0.1)
+
+    raw_ms = _timed(step_raw, args.steps, args.warmup, "prefill_dt_raw")
     flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
     nbytes = prefill_bytes(w.B, w.L, w.H, w.P, w.G, w.N, 2 if w.dtype == "bf16" else 4)
     # per-kernel durations: HIP events the library records between its
@@ -185,10 +194,10 @@ def bench_prefill(args):
     finally:
         bd.stage_timing(False)
     stages = {k: sum(v) / len(v) for k, v in stages.items()}
-    return w, ms, flops, nbytes, stages, graph_ms
+    return w, ms, flops, nbytes, stages, graph_ms, raw_ms
 
 
-def bench_decode(args, rotate):
+def bench_decode(args, rotate, raw_dt=False):
     import torch
 
     from mamba_ssd_scan_chunk_amd import binding as bd
@@ -205,6 +214,10 @@ def bench_decode(args, rotate):
     del pre
     xbc, dts = synth.make_decode_stream(steps, B, H, P, G, N, w.dtype, seed=4)
     xbc, dts = xbc.cuda(), dts.cuda()
+    kw = {}
+    if raw_dt:  # the step passed raw, preprocessed inside the kernel
+        dts, dt_bias = (t.cuda() for t in synth.make_dt_raw((steps, B), H, seed=6))
+        kw = dict(dt_raw=True, dt_bias=dt_bias, dt_min=1e-3, dt_max=0.1)
     cw, _ = synth.make_conv(C, K, w.dtype, seed=5)
     cw = cw.cuda()
     conv = [torch.zeros((B, C, K - 1), dtype=tdt, device="cuda") for _ in range(2)]
@@ -221,7 +234,7 @@ def bench_decode(args, rotate):
         row = xbc[i % steps]
         bd.ssd_decode_step(row[:, :HP], dts[i % steps], A_log, row[:, HP:HP + GN], row[:, HP + GN:], D,
                            states[i % nrot], y_t=y, in_stride=C, G=G, conv_state_in=conv[i & 1],
-                           conv_state_out=conv[(i + 1) & 1], conv_w=cw, K=K, activation=1)
+                           conv_state_out=conv[(i + 1) & 1], conv_w=cw, K=K, activation=1, **kw)
 
     eager_ms = _timed(step, steps, min(args.warmup, 8), "decode")
     graph_ms = _graph_timed(step, steps)
@@ -313,6 +326,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode and conv legs")
     ap.add_argument("--legs", default="prefill,decode,conv",
                     help="comma-separated subset of prefill,decode,conv,copy (for profiling runs)")
+    ap.add_argument("--no-decode-extras", action="store_true",
+                    help="decode leg: only the stated workload's one-state and rotated-state runs (no other batch, "
+                         "raw-step or recompute legs), so that every decode dispatch has the same size")
     ap.add_argument("--stage-runs", type=int, default=20, help="timed calls for the per-kernel durations")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -349,7 +365,7 @@ def main():
 
 
 def prefill_record(args):
-    w, ms, flops, nbytes, stages, graph_ms = bench_prefill(args)
+    w, ms, flops, nbytes, stages, graph_ms, raw_ms = bench_prefill(args)
     tflops = flops / (ms * 1e-3) / 1e12
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/B
     stage_rec = {}
@@ -389,6 +405,8 @@ def prefill_record(args):
                     "attainable_frac": round(tflops / min(PEAK_BF16_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3), 4),
                     "graph": {"us_per_call": round(graph_ms * 1e3, 2),
                               "tokens_per_s": round(w.B * w.L / (graph_ms * 1e-3), 1)},
+                    "dt_raw": {"us_per_call": round(raw_ms * 1e3, 2),
+                               "tokens_per_s": round(w.B * w.L / (raw_ms * 1e-3), 1)},
                     "kernels": stage_rec},
         "roofline": roof,
     }
@@ -445,21 +463,27 @@ def decode_record(args):
     dw, dms, gms, dbytes, _ = bench_decode(args, rotate=False)
     _, rms, rgms, _, nrot = bench_decode(args, rotate=True)
     gbs = lambda ms: dbytes / (ms * 1e-3) / 1e9  # noqa: E731
-    # the other batch size of the stated decode workload, in one HIP graph
-    other = {"mamba2-2.7b-decode-b16": "mamba2-2.7b-decode-b1",
-             "mamba2-2.7b-decode-b1": "mamba2-2.7b-decode-b16"}.get(args.decode_workload)
     extra = {}
-    if other is not None:
-        oargs = argparse.Namespace(**vars(args))
-        oargs.decode_workload = other
-        oargs.decode_steps = min(args.decode_steps, 1024)
-        ow, _, ogms, obytes, _ = bench_decode(oargs, rotate=False)
-        extra = {"other_batch": {"workload": ow.name, "batch": ow.B, "steps": oargs.decode_steps,
-                                 "graph_us_per_step": round(ogms * 1e3, 3),
-                                 "gbs": round(obytes / (ogms * 1e-3) / 1e9, 1)}}
-    b1_ms = gms if dw.B == 1 else (ogms if other is not None else None)
-    if b1_ms is not None:
-        extra["cached_vs_recompute"] = cached_vs_recompute(args, b1_ms)
+    b1_ms = gms if dw.B == 1 else None
+    if not args.no_decode_extras:
+        # the step passed raw and preprocessed in the kernel
+        _, _, raw_gms, _, _ = bench_decode(args, rotate=False, raw_dt=True)
+        extra["dt_raw"] = {"graph_us_per_step": round(raw_gms * 1e3, 3), "gbs": round(gbs(raw_gms), 1)}
+        # the other batch size of the stated decode workload, in one HIP graph
+        other = {"mamba2-2.7b-decode-b16": "mamba2-2.7b-decode-b1",
+                 "mamba2-2.7b-decode-b1": "mamba2-2.7b-decode-b16"}.get(args.decode_workload)
+        if other is not None:
+            oargs = argparse.Namespace(**vars(args))
+            oargs.decode_workload = other
+            oargs.decode_steps = min(args.decode_steps, 1024)
+            ow, _, ogms, obytes, _ = bench_decode(oargs, rotate=False)
+            extra["other_batch"] = {"workload": ow.name, "batch": ow.B, "steps": oargs.decode_steps,
+                                    "graph_us_per_step": round(ogms * 1e3, 3),
+                                    "gbs": round(obytes / (ogms * 1e-3) / 1e9, 1)}
+            if ow.B == 1:
+                b1_ms = ogms
+        if b1_ms is not None:
+            extra["cached_vs_recompute"] = cached_vs_recompute(args, b1_ms)
     return {
         "decode": {"workload": dw.name, "batch": dw.B, "steps": args.decode_steps, "bytes_per_step": dbytes,
                    "graph": {"us_per_step": round(gms * 1e3, 3), "steps_per_s": round(1e3 / gms, 1),
@@ -467,7 +491,8 @@ def decode_record(args):
                    "eager": {"us_per_step": round(dms * 1e3, 3), "gbs": round(gbs(dms), 1)},
                    "rotated": {"states": nrot, "graph_us_per_step": round(rgms * 1e3, 3),
                                "graph_gbs": round(gbs(rgms), 1), "hbm_peak_frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
-                               "eager_us_per_step": round(rms * 1e3, 3)}, **extra},
+                               "eager_us_per_step": round(rms * 1e3, 3)},
+                   **extra},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs(rgms), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs(rgms) / PEAK_HBM_GBS, 4),
                             # the committed counters were taken on the default (B = 16) workload

@@ -106,6 +106,28 @@ int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
                 const float *init_state, void *y, float *final_state,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * ssd_prefill_dt_raw -- ssd_prefill with the step computed from its raw
+ * value inside the kernels, dt = clamp(softplus(dt_raw + dt_bias[h]),
+ * dt_min, dt_max) with softplus(u) = log(1 + exp(u)), in fp32.
+ * Source: bqwf.cn article §1.2 (the softplus and clipping of the step fused
+ * into the kernels that consume it instead of a separate elementwise pass).
+ *
+ *   dt_raw [B,L,H]  fp32   raw step (any real value)
+ *   dt_bias [H]     fp32   added before softplus; NULL means 0
+ *   dt_min, dt_max         0 <= dt_min <= dt_max (dt_max may be +inf); NaN is
+ *                          rejected (SSD_ERR_INVALID_ARG); an unaligned
+ *                          dt_bias gives SSD_ERR_ALIGNMENT
+ * Every other argument, limit and error is as for ssd_prefill, and the
+ * workspace size is the same.
+ */
+int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                       const void *x, const float *dt_raw, const float *dt_bias,
+                       float dt_min, float dt_max, const float *A_log,
+                       const void *Bm, const void *Cm, const float *D,
+                       const float *init_state, void *y, float *final_state,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace ssd_prefill needs for these arguments (0 if none).
  * Returns (size_t)-1 for arguments ssd_prefill would reject. */
 size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N,
@@ -154,6 +176,21 @@ int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
                     const void *conv_state_in, void *conv_state_out,
                     const void *conv_w, const void *conv_b, int K,
                     int activation, hipStream_t stream);
+
+/*
+ * ssd_decode_step_dt_raw -- ssd_decode_step with dt = clamp(softplus(
+ * dt_raw[b,h] + dt_bias[h]), dt_min, dt_max) computed in the kernel, as in
+ * ssd_prefill_dt_raw (same source, same argument rules for dt_raw [B,H],
+ * dt_bias, dt_min and dt_max); everything else as for ssd_decode_step.
+ */
+int ssd_decode_step_dt_raw(int B, int H, int P, int G, int N, int dtype,
+                           const void *x_t, const float *dt_raw, const float *dt_bias,
+                           float dt_min, float dt_max, const float *A_log,
+                           const void *B_t, const void *C_t, const float *D,
+                           float *ssm_state, void *y_t, long in_stride,
+                           const void *conv_state_in, void *conv_state_out,
+                           const void *conv_w, const void *conv_b, int K,
+                           int activation, hipStream_t stream);
 
 /*
  * conv_state_update -- depthwise causal convolution over T new tokens with

@@ -26,11 +26,13 @@ SSD_ERR_WORKSPACE = -4
 SSD_ERR_HIP = -5
 
 # (name, restype, argtypes) of every entry point in include/ssd.h
-_i, _p, _l, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_long, ctypes.c_size_t
+_i, _p, _l, _sz, _f = ctypes.c_int, ctypes.c_void_p, ctypes.c_long, ctypes.c_size_t, ctypes.c_float
 SIGNATURES = {
     "ssd_prefill": (_i, [_i] * 8 + [_p] * 10 + [_sz, _p]),
+    "ssd_prefill_dt_raw": (_i, [_i] * 8 + [_p] * 3 + [_f, _f] + [_p] * 8 + [_sz, _p]),
     "ssd_prefill_workspace_bytes": (_sz, [_i] * 8),
     "ssd_decode_step": (_i, [_i] * 6 + [_p] * 8 + [_l] + [_p] * 4 + [_i, _i, _p]),
+    "ssd_decode_step_dt_raw": (_i, [_i] * 6 + [_p] * 3 + [_f, _f] + [_p] * 6 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "conv_state_update": (_i, [_i] * 5 + [_p] * 4 + [_i, _p, _p]),
     "ssd_stage_timing": (_i, [_i]),
     "ssd_stage_times": (_i, [ctypes.POINTER(ctypes.c_float), _i, ctypes.POINTER(_i)]),
@@ -110,12 +112,14 @@ def ssd_prefill_workspace_bytes(B, L, H, P, G, N, Q, dtype) -> int:
 
 
 def ssd_prefill(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y=None,
-                final_state=None, want_final_state=True, workspace=None, stream=None):
+                final_state=None, want_final_state=True, workspace=None, stream=None,
+                dt_raw=False, dt_bias=None, dt_min=0.0, dt_max=float("inf")):
     """Chunked SSD prefill.  x [B,L,H,P], dt [B,L,H] f32, A_log [H] f32,
     Bm/Cm [B,L,G,N], D [H] f32 or None, init_state [B,H,P,N] f32 or None.
-    Returns (y, final_state)."""
+    With ``dt_raw`` the kernels use clamp(softplus(dt + dt_bias), dt_min,
+    dt_max) as the step (ssd_prefill_dt_raw).  Returns (y, final_state)."""
     for t, n in ((x, "x"), (dt, "dt"), (A_log, "A_log"), (Bm, "Bm"), (Cm, "Cm"), (D, "D"),
-                 (init_state, "init_state"), (y, "y"), (final_state, "final_state")):
+                 (init_state, "init_state"), (y, "y"), (final_state, "final_state"), (dt_bias, "dt_bias")):
         _dense(t, n)
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
@@ -128,20 +132,30 @@ def ssd_prefill(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y=None,
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().ssd_prefill(B, L, H, P, G, N, Q, code, _ptr(x), _ptr(dt), _ptr(A_log), _ptr(Bm),
-                           _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
-                           _ptr(workspace), ws_bytes, _stream(stream))
-    _check("ssd_prefill", rc)
+    if dt_raw:
+        rc = lib().ssd_prefill_dt_raw(B, L, H, P, G, N, Q, code, _ptr(x), _ptr(dt), _ptr(dt_bias), float(dt_min),
+                                      float(dt_max), _ptr(A_log), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state),
+                                      _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes, _stream(stream))
+        _check("ssd_prefill_dt_raw", rc)
+    else:
+        if dt_bias is not None:
+            raise ValueError("dt_bias is used only with dt_raw=True")
+        rc = lib().ssd_prefill(B, L, H, P, G, N, Q, code, _ptr(x), _ptr(dt), _ptr(A_log), _ptr(Bm),
+                               _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                               _ptr(workspace), ws_bytes, _stream(stream))
+        _check("ssd_prefill", rc)
     return y, final_state
 
 
 def ssd_decode_step(x_t, dt_t, A_log, B_t, C_t, D, ssm_state, *, y_t=None, in_stride=0,
                     conv_state_in=None, conv_state_out=None, conv_w=None, conv_b=None,
-                    K=4, activation=0, H=None, P=None, G=None, N=None, stream=None):
+                    K=4, activation=0, H=None, P=None, G=None, N=None, stream=None,
+                    dt_raw=False, dt_bias=None, dt_min=0.0, dt_max=float("inf")):
     """One decode step, in place on ssm_state [B,H,P,N] (and conv_state_out).
 
     x_t [B,H*P], dt_t [B,H], B_t/C_t [B,G*N] (or views into one [B,C] row with
-    ``in_stride`` = C).  Returns y_t [B,H,P]."""
+    ``in_stride`` = C).  With ``dt_raw`` the step is clamp(softplus(dt_t +
+    dt_bias), dt_min, dt_max) (ssd_decode_step_dt_raw).  Returns y_t [B,H,P]."""
     Bsz, H_, P_, N_ = ssm_state.shape
     H, P, N = H or H_, P or P_, N or N_
     G = G or (B_t.shape[-1] // N if in_stride == 0 else None)
@@ -151,11 +165,22 @@ def ssd_decode_step(x_t, dt_t, A_log, B_t, C_t, D, ssm_state, *, y_t=None, in_st
     code = _dtype_code(x_t)
     if y_t is None:
         y_t = torch.empty((Bsz, H, P), dtype=x_t.dtype, device=x_t.device)
-    rc = lib().ssd_decode_step(Bsz, H, P, G, N, code, _ptr(x_t), _ptr(dt_t), _ptr(A_log), _ptr(B_t),
-                               _ptr(C_t), _ptr(D), _ptr(ssm_state), _ptr(y_t), int(in_stride),
-                               _ptr(conv_state_in), _ptr(conv_state_out), _ptr(conv_w), _ptr(conv_b),
-                               int(K), int(activation), _stream(stream))
-    _check("ssd_decode_step", rc)
+    if dt_raw:
+        _dense(dt_bias, "dt_bias")
+        rc = lib().ssd_decode_step_dt_raw(Bsz, H, P, G, N, code, _ptr(x_t), _ptr(dt_t), _ptr(dt_bias),
+                                          float(dt_min), float(dt_max), _ptr(A_log), _ptr(B_t), _ptr(C_t),
+                                          _ptr(D), _ptr(ssm_state), _ptr(y_t), int(in_stride),
+                                          _ptr(conv_state_in), _ptr(conv_state_out), _ptr(conv_w),
+                                          _ptr(conv_b), int(K), int(activation), _stream(stream))
+        _check("ssd_decode_step_dt_raw", rc)
+    else:
+        if dt_bias is not None:
+            raise ValueError("dt_bias is used only with dt_raw=True")
+        rc = lib().ssd_decode_step(Bsz, H, P, G, N, code, _ptr(x_t), _ptr(dt_t), _ptr(A_log), _ptr(B_t),
+                                   _ptr(C_t), _ptr(D), _ptr(ssm_state), _ptr(y_t), int(in_stride),
+                                   _ptr(conv_state_in), _ptr(conv_state_out), _ptr(conv_w), _ptr(conv_b),
+                                   int(K), int(activation), _stream(stream))
+        _check("ssd_decode_step", rc)
     return y_t
 
 

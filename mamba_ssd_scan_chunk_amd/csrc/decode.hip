@@ -257,7 +257,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     // row constants: thread t for row t of the block (clamped)
     const int trow = min(tid, prows - 1);
     const int th = g * hpg + (r0 + trow) / P;
-    const float t_dt = a.dt_t[(long)b * H + th];
+    const float t_dtv = a.dt_t[(long)b * H + th];  // raw value when dt is preprocessed here (below)
+    const float t_bias = a.dtp.dt_bias ? a.dtp.dt_bias[th] : 0.0f;
     const float t_alog = a.A_log[th];
     const float t_Dv = a.D ? a.D[th] : 0.0f;
     // conv channels: the block's x rows, then B, then C; thread tid takes
@@ -301,6 +302,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     constexpr int kTapRegs = !CONV ? 0 : (KT == 4 && sizeof(T) == 2) ? 2 : KM;
 #pragma unroll
     for (int k = 0; k < S::CH_ROUNDS; ++k) settle(cin[k], kWinRegs, kTapRegs);
+    float t_dtv_s = t_dtv, t_bias_s = t_bias, t_alog_s = t_alog, t_Dv_s = t_Dv;
+    asm volatile("" : "+v"(t_dtv_s), "+v"(t_bias_s), "+v"(t_alog_s), "+v"(t_Dv_s));
 
     // ---- 3. convolution results and row constants to LDS
 #pragma unroll
@@ -311,8 +314,10 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
         const float v = conv_finish<T, CONV, KT, KM>(a, C, b, cidx[k], cin[k], valid && (is_x || bc_writer));
         if (k == 0 && is_x) {
             // thread t = row t: the channel just finished is x of row t
-            rowc[i] = make_float2(t_dt * v, expm1f(t_dt * -expf(t_alog)));
-            rowdx[i] = t_Dv * v;
+            const float t_dt =
+                a.dtp.dt_raw ? dt_softplus_clamp(t_dtv_s + t_bias_s, a.dtp.dt_min, a.dtp.dt_max) : t_dtv_s;
+            rowc[i] = make_float2(t_dt * v, expm1f(t_dt * -expf(t_alog_s)));
+            rowdx[i] = t_Dv_s * v;
         } else if (valid && !is_x) {
             if (i < prows + N) Bs[i - prows] = v;
             else Cs[i - prows - N] = v;

@@ -110,11 +110,14 @@ __device__ __forceinline__ void load_x_raw(const PrefillArgs &a, int b, int t0, 
     for (int k = 0; k < 8; ++k) raw[k] = buf_load16(r, (unsigned)(sb * 8 + k) * rs + pb * 16);
 }
 
-// dt of token tid of the chunk (0 at or past Qc).
+// dt of token tid of the chunk (0 at or past Qc), after the optional
+// preprocessing of the raw value.
 __device__ __forceinline__ float load_dt(const PrefillArgs &a, int b, int t0, int Qc, int h, int t) {
     const float *d0 = a.dt + ((long)b * a.L + t0) * a.H + h;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(d0, (unsigned)((Qc - 1) * a.H + 1) * 4);
-    return buf_load_f32(r, (unsigned)t * a.H * 4);
+    const float v = buf_load_f32(r, (unsigned)t * a.H * 4);
+    if (!a.dtp.dt_raw) return v;
+    return t < Qc ? dt_value(v, 1, a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max) : 0.0f;
 }
 
 constexpr int kXRow = kQ * 2 + 16;        // x'^T row stride in LDS (bytes), padded against bank conflicts

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_vec(PrefillArgs a) {
     float dtv = 0.0f;
     double v = 0.0;
     if (tid < Qc) {
-        dtv = a.dt[((long)b * a.L + t0 + tid) * a.H + h];
+        dtv = dt_value(a.dt[((long)b * a.L + t0 + tid) * a.H + h], a.dtp.dt_raw, a.dtp.dt_bias, h, a.dtp.dt_min,
+                       a.dtp.dt_max);
         v = (double)(dtv * Af);
     }
     double inc = wave_inclusive_sum_f64(v);
@@ -136,7 +137,9 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
         }
         if (tid < ST) {
             css[tid] = tid < srows ? cs[s0 + tid] : 0.0;
-            dts[tid] = tid < srows ? a.dt[((long)b * a.L + t0 + s0 + tid) * a.H + h] : 0.0f;
+            dts[tid] = tid < srows ? dt_value(a.dt[((long)b * a.L + t0 + s0 + tid) * a.H + h], a.dtp.dt_raw,
+                                              a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max)
+                                   : 0.0f;
         }
         __syncthreads();
         {

@@ -94,11 +94,20 @@ SSD_API size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, in
     return ssd::prefill_workspace_layout(B, L, H, P, N, Q, G, ssd::prefill_uses_mfma(P, N, Q, dtype)).total;
 }
 
-SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
-                        const void *x, const float *dt, const float *A_log,
-                        const void *Bm, const void *Cm, const float *D,
-                        const float *init_state, void *y, float *final_state,
-                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// dt preprocessing arguments: dt_bias may be null; 0 <= dt_min <= dt_max
+// (dt_max may be +inf); no NaN.
+bool valid_dt_prep(float dt_min, float dt_max, const float *dt_bias) {
+    if (!(dt_min >= 0.0f) || !(dt_max >= dt_min)) return false;  // also rejects NaN
+    return aligned(dt_bias, 4);
+}
+
+int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                 const void *x, const float *dt, const float *A_log,
+                 const void *Bm, const void *Cm, const float *D,
+                 const float *init_state, void *y, float *final_state,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream, const ssd::DtPrep &dtp) {
     const PrefillShape s{B, L, H, P, G, N, Q, dtype};
     int rc = check_prefill_shape(s);
     if (rc != SSD_OK) return rc;
@@ -122,7 +131,8 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
     // outputs may not overlap inputs, workspace or each other
     // (final_state == init_state exactly is allowed)
     struct R { const void *p; size_t n; };
-    const R ins[] = {{x, b_x}, {dt, b_dt}, {A_log, (size_t)H * 4}, {Bm, b_bc}, {Cm, b_bc}, {D, D ? (size_t)H * 4 : 0}};
+    const R ins[] = {{x, b_x}, {dt, b_dt}, {A_log, (size_t)H * 4}, {Bm, b_bc}, {Cm, b_bc}, {D, D ? (size_t)H * 4 : 0},
+                     {dtp.dt_bias, dtp.dt_bias ? (size_t)H * 4 : 0}};
     if (L > 0) {
         for (const R &r : ins) if (overlap(y, b_x, r.p, r.n)) return SSD_ERR_INVALID_ARG;
         if (overlap(y, b_x, init_state, b_state) || overlap(y, b_x, final_state, b_state) ||
@@ -149,6 +159,7 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
     a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.Q = Q;
     a.nchunks = (L + Q - 1) / Q;
     a.x = x; a.dt = dt; a.A_log = A_log; a.Bm = Bm; a.Cm = Cm; a.D = D;
+    a.dtp = dtp;
     a.init_state = init_state; a.y = y; a.final_state = final_state;
     char *ws = (char *)workspace;
     a.ws_S = (float *)(ws + wl.off_S);
@@ -162,13 +173,13 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
     return hip_status(e);
 }
 
-SSD_API int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
-                            const void *x_t, const float *dt_t, const float *A_log,
-                            const void *B_t, const void *C_t, const float *D,
-                            float *ssm_state, void *y_t, long in_stride,
-                            const void *conv_state_in, void *conv_state_out,
-                            const void *conv_w, const void *conv_b, int K,
-                            int activation, hipStream_t stream) {
+int decode_impl(int B, int H, int P, int G, int N, int dtype,
+                const void *x_t, const float *dt_t, const float *A_log,
+                const void *B_t, const void *C_t, const float *D,
+                float *ssm_state, void *y_t, long in_stride,
+                const void *conv_state_in, void *conv_state_out,
+                const void *conv_w, const void *conv_b, int K,
+                int activation, hipStream_t stream, const ssd::DtPrep &dtp) {
     if (!valid_dtype(dtype)) return SSD_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || P < 1 || G < 1 || N < 1 || H % G != 0 || in_stride < 0) return SSD_ERR_INVALID_ARG;
     if (!x_t || !dt_t || !A_log || !B_t || !C_t || !ssm_state || !y_t) return SSD_ERR_INVALID_ARG;
@@ -194,7 +205,7 @@ SSD_API int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
     const size_t b_conv = conv ? (size_t)B * C * (K - 1) * es : 0;
     struct R { const void *p; size_t n; };
     const R ins[] = {{x_t, b_x}, {B_t, b_bc}, {C_t, b_bc}, {dt_t, (size_t)B * H * 4}, {A_log, (size_t)H * 4},
-                     {D, D ? (size_t)H * 4 : 0}, {conv_state_in, b_conv},
+                     {D, D ? (size_t)H * 4 : 0}, {dtp.dt_bias, dtp.dt_bias ? (size_t)H * 4 : 0}, {conv_state_in, b_conv},
                      {conv ? conv_w : nullptr, conv ? (size_t)C * K * es : 0},
                      {conv ? conv_b : nullptr, (conv && conv_b) ? (size_t)C * es : 0}};
     for (const R &r : ins) {
@@ -209,12 +220,59 @@ SSD_API int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
     a.B = B; a.H = H; a.P = P; a.G = G; a.N = N; a.K = K; a.activation = activation;
     a.in_stride = in_stride;
     a.x_t = x_t; a.dt_t = dt_t; a.A_log = A_log; a.B_t = B_t; a.C_t = C_t; a.D = D;
+    a.dtp = dtp;
     a.state = ssm_state; a.y_t = y_t;
     a.conv_in = conv ? conv_state_in : nullptr;
     a.conv_out = conv ? conv_state_out : nullptr;
     a.conv_w = conv ? conv_w : nullptr;
     a.conv_b = conv ? conv_b : nullptr;
     return hip_status(ssd::launch_decode(a, dtype, stream));
+}
+
+}  // namespace
+
+SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                        const void *x, const float *dt, const float *A_log,
+                        const void *Bm, const void *Cm, const float *D,
+                        const float *init_state, void *y, float *final_state,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return prefill_impl(B, L, H, P, G, N, Q, dtype, x, dt, A_log, Bm, Cm, D, init_state, y, final_state,
+                        workspace, workspace_bytes, stream, ssd::DtPrep{0, nullptr, 0.0f, 0.0f});
+}
+
+SSD_API int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                               const void *x, const float *dt_raw, const float *dt_bias, float dt_min,
+                               float dt_max, const float *A_log, const void *Bm, const void *Cm,
+                               const float *D, const float *init_state, void *y, float *final_state,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dt_prep(dt_min, dt_max, dt_bias)) return aligned(dt_bias, 4) ? SSD_ERR_INVALID_ARG : SSD_ERR_ALIGNMENT;
+    return prefill_impl(B, L, H, P, G, N, Q, dtype, x, dt_raw, A_log, Bm, Cm, D, init_state, y, final_state,
+                        workspace, workspace_bytes, stream, ssd::DtPrep{1, dt_bias, dt_min, dt_max});
+}
+
+SSD_API int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,
+                            const void *x_t, const float *dt_t, const float *A_log,
+                            const void *B_t, const void *C_t, const float *D,
+                            float *ssm_state, void *y_t, long in_stride,
+                            const void *conv_state_in, void *conv_state_out,
+                            const void *conv_w, const void *conv_b, int K,
+                            int activation, hipStream_t stream) {
+    return decode_impl(B, H, P, G, N, dtype, x_t, dt_t, A_log, B_t, C_t, D, ssm_state, y_t, in_stride,
+                       conv_state_in, conv_state_out, conv_w, conv_b, K, activation, stream,
+                       ssd::DtPrep{0, nullptr, 0.0f, 0.0f});
+}
+
+SSD_API int ssd_decode_step_dt_raw(int B, int H, int P, int G, int N, int dtype,
+                                   const void *x_t, const float *dt_raw, const float *dt_bias, float dt_min,
+                                   float dt_max, const float *A_log, const void *B_t, const void *C_t,
+                                   const float *D, float *ssm_state, void *y_t, long in_stride,
+                                   const void *conv_state_in, void *conv_state_out,
+                                   const void *conv_w, const void *conv_b, int K,
+                                   int activation, hipStream_t stream) {
+    if (!valid_dt_prep(dt_min, dt_max, dt_bias)) return aligned(dt_bias, 4) ? SSD_ERR_INVALID_ARG : SSD_ERR_ALIGNMENT;
+    return decode_impl(B, H, P, G, N, dtype, x_t, dt_raw, A_log, B_t, C_t, D, ssm_state, y_t, in_stride,
+                       conv_state_in, conv_state_out, conv_w, conv_b, K, activation, stream,
+                       ssd::DtPrep{1, dt_bias, dt_min, dt_max});
 }
 
 SSD_API int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_state,

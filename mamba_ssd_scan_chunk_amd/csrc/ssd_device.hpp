@@ -32,6 +32,20 @@ template <> __device__ __forceinline__ void st<bf16_t>(bf16_t *p, float v) { *p 
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
+// clamp(softplus(u), lo, hi), softplus(u) = log(1 + exp(u)) (u itself above
+// 20, where the difference is below fp32 resolution).
+__device__ __forceinline__ float dt_softplus_clamp(float u, float lo, float hi) {
+    const float sp = u > 20.0f ? u : log1pf(expf(u));
+    return fminf(fmaxf(sp, lo), hi);
+}
+
+// dt of head h from the value read: itself, or clamp(softplus(v + bias[h]),
+// lo, hi).
+__device__ __forceinline__ float dt_value(float v, int raw, const float *bias, int h, float lo, float hi) {
+    if (!raw) return v;
+    return dt_softplus_clamp(v + (bias ? bias[h] : 0.0f), lo, hi);
+}
+
 // ---------------------------------------------------------------- wave ops
 
 // Inclusive prefix sum across the 64 lanes of a wavefront, with DPP moves:

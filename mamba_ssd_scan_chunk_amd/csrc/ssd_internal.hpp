@@ -11,10 +11,19 @@ namespace ssd {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
+// dt preprocessing: dt as given (dt_raw = 0), or dt = clamp(softplus(dt +
+// dt_bias[h]), dt_min, dt_max) computed where dt is read (dt_raw = 1).
+struct DtPrep {
+    int dt_raw;
+    const float *dt_bias;  // [H] or null (0)
+    float dt_min, dt_max;
+};
+
 struct PrefillArgs {
     int B, L, H, P, G, N, Q, nchunks;
     const void *x;
     const float *dt, *A_log;
+    DtPrep dtp;
     const void *Bm, *Cm;
     const float *D, *init_state;
     void *y;
@@ -66,6 +75,7 @@ struct DecodeArgs {
     long in_stride;
     const void *x_t;
     const float *dt_t, *A_log;
+    DtPrep dtp;
     const void *B_t, *C_t;
     const float *D;
     float *state;

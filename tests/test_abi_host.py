@@ -98,6 +98,34 @@ def test_prefill_rejects(lib, kw, code):
     assert _prefill(lib, **kw) == code
 
 
+def _prefill_raw(lib, B=1, L=64, H=2, P=16, G=1, N=16, Q=32, dtype=0, dt_min=0.001, dt_max=0.1, **over):
+    ptrs = dict(x=_addr(0), dt=_addr(1), bias=_addr(10), A_log=_addr(2), Bm=_addr(3), Cm=_addr(4), D=_addr(5),
+                init=_addr(6), y=_addr(7), final=_addr(8), ws=_addr(9))
+    ptrs.update(over)
+    return lib.ssd_prefill_dt_raw(B, L, H, P, G, N, Q, dtype, ptrs["x"], ptrs["dt"], ptrs["bias"], dt_min, dt_max,
+                                  ptrs["A_log"], ptrs["Bm"], ptrs["Cm"], ptrs["D"], ptrs["init"], ptrs["y"],
+                                  ptrs["final"], ptrs["ws"], 1 << 40, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt_min=-0.1), bd.SSD_ERR_INVALID_ARG),
+    (dict(dt_min=0.2, dt_max=0.1), bd.SSD_ERR_INVALID_ARG),
+    (dict(dt_min=float("nan")), bd.SSD_ERR_INVALID_ARG),
+    (dict(dt_max=float("nan")), bd.SSD_ERR_INVALID_ARG),
+    (dict(bias=_addr(10, 2)), bd.SSD_ERR_ALIGNMENT),
+    (dict(y=_addr(10, 0)), bd.SSD_ERR_INVALID_ARG),     # y overlaps dt_bias
+    (dict(G=3, H=4), bd.SSD_ERR_INVALID_ARG),          # the checks of ssd_prefill apply
+    (dict(dt=None), bd.SSD_ERR_INVALID_ARG),
+])
+def test_prefill_dt_raw_rejects(lib, kw, code):
+    assert _prefill_raw(lib, **kw) == code
+
+
+def test_prefill_dt_raw_accepts_open_limits(lib):
+    # no bias, dt_max = +inf: valid; L = 0 without outputs returns before any HIP call
+    assert _prefill_raw(lib, L=0, bias=None, dt_min=0.0, dt_max=float("inf"), final=None, x=None, y=None) == bd.SSD_OK
+
+
 def test_prefill_empty_sequence_without_outputs_is_a_no_op(lib):
     # L = 0 and no final_state: nothing to do, returns before any HIP call
     assert _prefill(lib, L=0, final=None, x=None, y=None) == bd.SSD_OK
@@ -143,6 +171,26 @@ def _decode(lib, B=2, H=2, P=16, G=1, N=16, dtype=0, K=4, act=1, stride=0, **ove
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def _decode_raw(lib, B=2, H=2, P=16, G=1, N=16, dtype=0, K=4, act=1, dt_min=0.0, dt_max=1.0, **over):
+    p = dict(x=_addr(0), dt=_addr(1), bias=_addr(12), A_log=_addr(2), Bt=_addr(3), Ct=_addr(4), D=_addr(5),
+             state=_addr(6), y=_addr(7), cin=_addr(8), cout=_addr(9), w=_addr(10), b=_addr(11))
+    p.update(over)
+    return lib.ssd_decode_step_dt_raw(B, H, P, G, N, dtype, p["x"], p["dt"], p["bias"], dt_min, dt_max, p["A_log"],
+                                      p["Bt"], p["Ct"], p["D"], p["state"], p["y"], 0, p["cin"], p["cout"], p["w"],
+                                      p["b"], K, act, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt_max=-1.0), bd.SSD_ERR_INVALID_ARG),
+    (dict(dt_min=float("nan")), bd.SSD_ERR_INVALID_ARG),
+    (dict(bias=_addr(12, 1)), bd.SSD_ERR_ALIGNMENT),
+    (dict(state=_addr(12, 0)), bd.SSD_ERR_INVALID_ARG),  # state overlaps dt_bias
+    (dict(K=1), bd.SSD_ERR_INVALID_ARG),                 # the checks of ssd_decode_step apply
+])
+def test_decode_dt_raw_rejects(lib, kw, code):
+    assert _decode_raw(lib, **kw) == code
 
 
 def _conv(lib, B=2, T=8, C=40, K=4, dtype=1, act=1, **over):

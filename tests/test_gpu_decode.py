@@ -27,8 +27,18 @@ def _setup(B, H, P, G, N, K, dtype, steps, seed, variant="spec", with_bias=False
                 state0=state0, conv0=conv0)
 
 
-def _run_steps(oracle, B, H, P, G, N, K, dtype, steps, seed, conv):
+def _run_steps(oracle, B, H, P, G, N, K, dtype, steps, seed, conv, raw_dt=None):
+    """``raw_dt`` = (with_bias, dt_min, dt_max): the step is passed raw and
+    preprocessed inside the kernel; the oracle gets dt_from_raw of it."""
     s = _setup(B, H, P, G, N, K, dtype, steps, seed=seed, with_bias=conv)
+    kw, ref_dts = {}, s["dts"]
+    if raw_dt is not None:
+        with_bias, lo, hi = raw_dt
+        raw, dt_bias = synth.make_dt_raw((steps, B), H, seed + 5)
+        dt_bias = dt_bias if with_bias else None
+        s["dts"] = raw
+        ref_dts = oracle.dt_from_raw(raw, dt_bias, lo, hi)
+        kw = dict(dt_raw=True, dt_bias=None if dt_bias is None else dt_bias.cuda(), dt_min=lo, dt_max=hi)
     C = s["C"]
     state = s["state0"].cuda()
     cin, cout = s["conv0"].cuda(), torch.empty_like(s["conv0"]).cuda()
@@ -42,11 +52,11 @@ def _run_steps(oracle, B, H, P, G, N, K, dtype, steps, seed, conv):
         x_t, B_t, C_t = row[:, :H * P], row[:, H * P:H * P + G * N], row[:, H * P + G * N:]
         y = bd.ssd_decode_step(x_t, dt, A_log, B_t, C_t, D, state, in_stride=C, G=G,
                                conv_state_in=cin if conv else None, conv_state_out=cout if conv else None,
-                               conv_w=w, conv_b=bias, K=K, activation=1)
+                               conv_w=w, conv_b=bias, K=K, activation=1, **kw)
         torch.cuda.synchronize()
         r = s["xbc"][t]
         y_ref, ref_state, new_conv = oracle.decode_step(
-            r[:, :H * P], s["dts"][t], s["A_log"], r[:, H * P:H * P + G * N], r[:, H * P + G * N:],
+            r[:, :H * P], ref_dts[t], s["A_log"], r[:, H * P:H * P + G * N], r[:, H * P + G * N:],
             s["D"], ref_state, conv_state=ref_conv if conv else None, conv_w=s["w"], conv_b=s["bias"],
             activation=True)
         assert rel_err(y, y_ref) <= _tol(dtype), t
@@ -65,6 +75,18 @@ def test_decode_steps_match_oracle(oracle, dtype, N, conv):
     block boundaries, two groups."""
     announce("decode", dtype, f"N={N}", f"conv={conv}")
     _run_steps(oracle, 2, 4, 20, 2, N, 4, dtype, 5, N + (100 if conv else 0), conv)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("conv", [False, True])
+@pytest.mark.parametrize("raw_dt", [(True, 1e-3, 0.1), (False, 0.0, float("inf"))], ids=["bias-clip", "plain"])
+def test_decode_dt_raw_matches_oracle(oracle, dtype, conv, raw_dt):
+    """dt preprocessing fused into the decode step: softplus of the raw step
+    plus a per-head bias, clipped (both bounds reached by the inputs), or
+    softplus alone."""
+    announce("decode dt_raw", dtype, f"conv={conv}", raw_dt)
+    _run_steps(oracle, 2, 4, 20, 2, 128, 4, dtype, 4, 300 + conv, conv, raw_dt)
+    _run_steps(oracle, 64, 16, 20, 2, 128, 4, dtype, 2, 310 + conv, conv, raw_dt)  # large-block launch
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -60,6 +60,32 @@ def test_prefill_matches_oracle(oracle, case, variant, with_init):
     assert rel_err(fs, fs_ref) <= _tol(dtype)
 
 
+RAW_DT_CASES = ["ragged", "q32-groups", "one-token", "odd-dims", "bf16-small", "bf16-q256-ragged",
+                "bf16-mfma-b3g3"]
+
+
+@pytest.mark.parametrize("name", RAW_DT_CASES)
+@pytest.mark.parametrize("raw_dt", [(True, 1e-3, 0.1), (False, 0.0, float("inf"))], ids=["bias-clip", "plain"])
+def test_prefill_dt_raw_matches_oracle(oracle, name, raw_dt):
+    """dt preprocessing fused into the prefill kernels (vector and MFMA
+    paths, ragged last chunk): the oracle scans dt_from_raw of the same raw
+    step."""
+    case = next(c for c in CASES if c[0] == name)
+    _, B, L, H, P, G, N, Q, dtype = case
+    with_bias, lo, hi = raw_dt
+    d = synth.make_prefill(B, L, H, P, G, N, dtype, seed=400 + RAW_DT_CASES.index(name))
+    raw, dt_bias = synth.make_dt_raw((B, L), H, seed=450 + RAW_DT_CASES.index(name))
+    dt_bias = dt_bias if with_bias else None
+    init = synth.make_state(B, H, P, N, seed=6, scale=0.5)
+    announce("prefill dt_raw", name, raw_dt)
+    d["dt"] = raw
+    y, fs = _run(d, Q, init, dt_raw=True, dt_bias=None if dt_bias is None else dt_bias.cuda(), dt_min=lo, dt_max=hi)
+    dt_ref = oracle.dt_from_raw(raw, dt_bias, lo, hi)
+    y_ref, fs_ref = oracle.ssd_scan(d["x"], dt_ref, d["A_log"], d["Bm"], d["Cm"], d["D"], init)
+    assert rel_err(y, y_ref) <= _tol(dtype)
+    assert rel_err(fs, fs_ref) <= _tol(dtype)
+
+
 @pytest.mark.parametrize("with_init", [False, True])
 def test_prefill_empty_sequence(with_init):
     B, H, P, N = 2, 3, 16, 16
@@ -148,6 +174,22 @@ def test_full_size_prefill_matches_oracle(oracle, name, variant):
     announce("full prefill", name, variant)
     y, fs = _run(d, w.Q)
     y_ref, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"])
+    assert rel_err(y, y_ref) <= TOL_BF16
+    assert rel_err(fs, fs_ref) <= TOL_BF16
+
+
+@pytest.mark.slow
+def test_full_size_prefill_dt_raw(oracle):
+    """2.7B-shaped layer (L=4096, Q=256) with the step preprocessed in the
+    kernels from a raw projection, a per-head bias and the bounds 1e-3, 0.1."""
+    w = synth.WORKLOADS["mamba2-2.7b-prefill"]
+    d = synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, w.dtype, seed=2)
+    raw, dt_bias = synth.make_dt_raw((w.B, w.L), w.H, seed=3)
+    announce("full prefill dt_raw")
+    d["dt"] = raw
+    y, fs = _run(d, w.Q, dt_raw=True, dt_bias=dt_bias.cuda(), dt_min=1e-3, dt_max=0.1)
+    dt_ref = oracle.dt_from_raw(raw, dt_bias, 1e-3, 0.1)
+    y_ref, fs_ref = oracle.ssd_scan(d["x"], dt_ref, d["A_log"], d["Bm"], d["Cm"], d["D"])
     assert rel_err(y, y_ref) <= TOL_BF16
     assert rel_err(fs, fs_ref) <= TOL_BF16
 
