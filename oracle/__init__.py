@@ -14,7 +14,8 @@ bqwf.cn article on the compiler-first Mamba-2 implementation §1.1, §2.1,
 
 with A_h = -exp(A_log[h]), plus the depthwise causal convolution over a
 (K-1)-token window cache and the step-size chain dt = clip(softplus(dt_raw +
-dt_bias), dt_min, dt_max) of §1.2 (``dt_from_raw``).  ``ssd_scan`` is the
+dt_bias), dt_min, dt_max) of §1.2 (``dt_from_raw``), and the layer's closing
+gated RMS normalisation of §3.2 and §4.1 (``gated_rmsnorm``).  ``ssd_scan`` is the
 prefill, ``decode_step`` is one step of the same recurrence after one step of
 the convolution cache.
 
@@ -64,6 +65,9 @@ def _load():
         lib.oracle_dt_from_raw.restype = ctypes.c_int
         lib.oracle_dt_from_raw.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _dp, ctypes.c_double,
                                            ctypes.c_double, _dp]
+        lib.oracle_gated_rmsnorm.restype = ctypes.c_int
+        lib.oracle_gated_rmsnorm.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _dp, _dp, ctypes.c_long,
+                                             _dp, ctypes.c_double, _dp]
         _lib = lib
     return _lib
 
@@ -137,6 +141,27 @@ def dt_from_raw(dt_raw, dt_bias=None, dt_min=0.0, dt_max=float("inf")):
                                     _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_dt_from_raw failed ({rc})")
+    return out
+
+
+def gated_rmsnorm(y, z=None, w=None, *, group, eps=1e-5):
+    """The layer's closing normalisation, gated RMS form (bqwf.cn §3.2,
+    §4.1): g = y * silu(z), then each group of ``group`` consecutive channels
+    of the last axis is divided by sqrt(mean(g^2) + eps) and multiplied by w.
+
+    y [..., D], z [..., D] or None (no gate), w [D] or None (1).  Returns a
+    float64 array of y's shape.
+    """
+    y = _f64(y)
+    D = y.shape[-1]
+    z, w = _f64(z), _f64(w)
+    assert z is None or z.shape == y.shape
+    assert w is None or w.shape == (D,)
+    out = np.empty_like(y)
+    rc = _load().oracle_gated_rmsnorm(y.size // D, D, int(group), _ptr(y), _ptr(z), D, _ptr(w), float(eps),
+                                      _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_gated_rmsnorm failed ({rc})")
     return out
 
 

@@ -218,3 +218,46 @@ int oracle_dt_from_raw(long n, int H, const double *dt_raw, const double *dt_bia
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Output side of the mixer: gated RMS normalisation                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The normalisation that closes the layer (bqwf.cn §3.2 fuses it into its
+ * neighbours; §4.1 asks for its variance in at least fp32), in the gated
+ * RMS form of the Mamba-2 mixer: the scan output is gated by the z branch,
+ * then each group of `group` consecutive channels is scaled to unit RMS and
+ * by a per-channel weight.  For row r and channel c of group k:
+ *   g[c]     = y[r,c] * silu(z[r,c])        (g = y when z is NULL)
+ *   ms_k     = (1/group) * sum over the group of g[c]^2
+ *   out[r,c] = g[c] / sqrt(ms_k + eps) * w[c]        (w = 1 when NULL)
+ * y, z, out: [rows, D] (z with row stride z_stride); w: [D].
+ */
+int oracle_gated_rmsnorm(long rows, int D, int group, const double *y, const double *z, long z_stride,
+                         const double *w, double eps, double *out)
+{
+    if (rows < 0 || D <= 0 || group <= 0 || D % group != 0 || !y || !out || !(eps >= 0.0)) return -1;
+    double *g = (double *)malloc(sizeof(double) * group);
+    if (!g) return -1;
+    for (long r = 0; r < rows; ++r) {
+        for (int k0 = 0; k0 < D; k0 += group) {
+            double ss = 0.0;
+            for (int j = 0; j < group; ++j) {
+                const int c = k0 + j;
+                double v = y[r * D + c];
+                if (z) {
+                    const double zz = z[r * z_stride + c];
+                    v *= zz / (1.0 + exp(-zz));
+                }
+                g[j] = v;
+                ss += v * v;
+            }
+            const double inv = 1.0 / sqrt(ss / group + eps);
+            for (int j = 0; j < group; ++j)
+                out[r * D + k0 + j] = g[j] * inv * (w ? w[k0 + j] : 1.0);
+        }
+    }
+    free(g);
+    return 0;
+}

@@ -14,7 +14,10 @@ fails at least one of them:
   * linearity, causality, independence of heads/batch, group broadcasting;
   * convolution: one-hot taps, numpy.convolve, torch SiLU;
   * step-size chain: softplus(0) = ln 2, softplus(u) - softplus(-u) = u,
-    400-digit decimal log(1 + e^u), the per-head bias index, clip bounds.
+    400-digit decimal log(1 + e^u), the per-head bias index, clip bounds;
+  * gated RMS normalisation: torch's rms_norm and silu on the gated values,
+    unit RMS per group, scale invariance, group independence, a constant
+    group's closed form, a saturated gate.
 """
 import decimal
 import json
@@ -401,3 +404,74 @@ def test_dt_clip_bounds(oracle):
     np.testing.assert_array_equal(oracle.dt_from_raw(u, None, 0.05, 0.05), np.full_like(u, 0.05))
     with pytest.raises(ValueError):
         oracle.dt_from_raw(u, None, 0.2, 0.1)
+
+
+# ---------------------------------------------------------------------------
+# Gated RMS normalisation out = rmsnorm_group(y * silu(z)) * w
+# ---------------------------------------------------------------------------
+
+def _norm_inputs(rows=5, D=48, seed=0):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((rows, D)), rng.standard_normal((rows, D)), rng.uniform(0.5, 1.5, D)
+
+
+@pytest.mark.parametrize("group", [1, 8, 16, 48])
+def test_gated_rmsnorm_matches_torch_rms_norm(oracle, group):
+    y, z, w = _norm_inputs(seed=group)
+    got = oracle.gated_rmsnorm(y, z, w, group=group, eps=1e-5)
+    g = torch.from_numpy(y) * torch.nn.functional.silu(torch.from_numpy(z))
+    rows, D = y.shape
+    ref = torch.nn.functional.rms_norm(g.reshape(rows, D // group, group), (group,), eps=1e-5).reshape(rows, D)
+    ref = (ref * torch.from_numpy(w)).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_gated_rmsnorm_unit_rms_and_scale_invariance(oracle):
+    y, _, _ = _norm_inputs(seed=3)
+    out = oracle.gated_rmsnorm(y, group=16, eps=0.0)
+    blocks = out.reshape(5, 3, 16)
+    np.testing.assert_allclose((blocks ** 2).mean(-1), 1.0, rtol=1e-14)
+    ratio = blocks / y.reshape(5, 3, 16)                    # one positive factor per group
+    np.testing.assert_allclose(ratio, ratio[..., :1] * np.ones(16), rtol=1e-13)
+    assert np.all(ratio > 0)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * y, group=16, eps=0.0), out, rtol=1e-13)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(-2.0 * y, group=16, eps=0.0), -out, rtol=1e-13)
+
+
+def test_gated_rmsnorm_groups_are_independent(oracle):
+    y, z, w = _norm_inputs(seed=4)
+    out = oracle.gated_rmsnorm(y, z, w, group=16)
+    y2 = y.copy()
+    y2[:, 16:32] *= 3.0
+    y2[:, 20] += 1.0
+    out2 = oracle.gated_rmsnorm(y2, z, w, group=16)
+    np.testing.assert_array_equal(out2[:, :16], out[:, :16])
+    np.testing.assert_array_equal(out2[:, 32:], out[:, 32:])
+    assert not np.allclose(out2[:, 16:32], out[:, 16:32])
+
+
+def test_gated_rmsnorm_constant_group_closed_form(oracle):
+    a, eps = 0.3, 0.01
+    y = np.full((1, 8), a)
+    w = np.arange(1.0, 9.0)
+    out = oracle.gated_rmsnorm(y, None, w, group=8, eps=eps)
+    np.testing.assert_allclose(out[0], a / math.sqrt(a * a + eps) * w, rtol=1e-15)
+
+
+def test_gated_rmsnorm_gate(oracle):
+    y, _, _ = _norm_inputs(seed=5)
+    # z = 0 closes the gate: silu(0) = 0, so the output is 0 (eps > 0)
+    np.testing.assert_array_equal(oracle.gated_rmsnorm(y, np.zeros_like(y), group=8), 0.0)
+    # a saturated gate (silu(z) = z for large z) scales y by a constant, which
+    # the normalisation removes
+    np.testing.assert_allclose(oracle.gated_rmsnorm(y, np.full_like(y, 40.0), group=8, eps=0.0),
+                               oracle.gated_rmsnorm(y, group=8, eps=0.0), rtol=1e-13)
+    # the gate multiplies channel by channel: a gate of 2 on one channel only
+    z = np.full_like(y, 40.0)
+    z[:, 3] = 80.0
+    y2 = y.copy()
+    y2[:, 3] *= 2.0
+    np.testing.assert_allclose(oracle.gated_rmsnorm(y, z, group=8, eps=0.0),
+                               oracle.gated_rmsnorm(y2, group=8, eps=0.0), rtol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.gated_rmsnorm(y, group=7)                      # groups must tile the channels
