@@ -293,6 +293,48 @@ def bench_conv(args):
     return ms, nbytes
 
 
+def bench_norm(args):
+    """The layer's closing gated RMS normalisation over the prefill's output
+    [B*L, H*P] (one group over all H*P channels, as in the 2.7B layer),
+    eager back-to-back calls; and over a decode step's [B, H*P] in a HIP graph."""
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    D = w.H * w.P
+    y = synth.make_tokens(1, w.B * w.L, D, w.dtype, seed=8)[0].cuda()
+    z, nw = synth.make_gate((w.B * w.L,), D, w.dtype, seed=9)
+    z, nw = z.cuda(), nw.cuda()
+    out = torch.empty_like(y)
+
+    def step(_):
+        bd.ssd_gated_rmsnorm(y, z, nw, group=D, eps=1e-5, out=out)
+
+    ms = _timed(step, args.steps, args.warmup, "norm")
+    es = y.element_size()
+    nbytes = 3 * w.B * w.L * D * es + D * 4
+
+    dw = synth.WORKLOADS[args.decode_workload]
+    yd, zd, od = y[:dw.B], z[:dw.B], out[:dw.B]
+
+    def dstep(_):
+        bd.ssd_gated_rmsnorm(yd, zd, nw, group=D, eps=1e-5, out=od)
+
+    dms = _graph_timed(dstep, 100)
+    return w, D, ms, nbytes, dw, dms
+
+
+def norm_record(args):
+    w, D, ms, nbytes, dw, dms = bench_norm(args)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"norm": {"workload": w.name, "rows": w.B * w.L, "channels": D, "group": D, "us": round(ms * 1e3, 2),
+                     "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
+                     "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "decode_rows": {"workload": dw.name, "rows": dw.B, "graph_us": round(dms * 1e3, 2)}}}
+
+
 def cpu_baseline(args):
     import oracle
     from mamba_ssd_scan_chunk_amd import synth
@@ -323,9 +365,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-only", action="store_true", help="skip the decode and conv legs")
-    ap.add_argument("--legs", default="prefill,decode,conv",
-                    help="comma-separated subset of prefill,decode,conv,copy (for profiling runs)")
+    ap.add_argument("--prefill-only", action="store_true", help="skip the decode, conv and norm legs")
+    ap.add_argument("--legs", default="prefill,decode,conv,norm",
+                    help="comma-separated subset of prefill,decode,conv,norm,copy (for profiling runs)")
     ap.add_argument("--no-decode-extras", action="store_true",
                     help="decode leg: only the stated workload's one-state and rotated-state runs (no other batch, "
                          "raw-step or recompute legs), so that every decode dispatch has the same size")
@@ -354,6 +396,8 @@ def main():
         out.update(decode_record(args))
     if "conv" in legs:
         out.update(conv_record(args))
+    if "norm" in legs:
+        out.update(norm_record(args))
     if "copy" in legs:
         out.update(copy_record(args))
     if HOST_BOUND:

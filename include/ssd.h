@@ -211,6 +211,36 @@ int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_state,
                       int activation, void *out, hipStream_t stream);
 
 /*
+ * ssd_gated_rmsnorm -- the normalisation that closes the layer, in the gated
+ * RMS form of the Mamba-2 mixer (bqwf.cn article §3.2: normalisation fused
+ * with its neighbours; §4.1: its variance in fp32 even for bf16 inputs).
+ * For each of `rows` rows and each group of `group` consecutive channels:
+ *
+ *   g   = y * silu(z)                           (g = y when z is NULL)
+ *   out = g / sqrt(mean over the group of g^2 + eps) * norm_w
+ *
+ * Sums, the gate and the scaling are fp32; out is rounded once to dtype.
+ *
+ *   y     [rows, D] dtype       the scan output (ssd_prefill's y as
+ *                               [B*L, H*P], ssd_decode_step's y_t as [B, H*P])
+ *   z     [rows, D] dtype or NULL, row stride z_stride elements (>= D), so z
+ *                               may be a column slice of a wider projection
+ *   norm_w [D] fp32 or NULL (weight 1)
+ *   out   [rows, D] dtype       may be y itself (in place); otherwise it must
+ *                               not overlap y, z or norm_w
+ * group divides D; with V = 16 / sizeof(dtype) (8 for bf16, 4 for fp32),
+ * group / V must be a power of two up to 64 or a multiple of 64 (for bf16:
+ * group = 8, 16, ..., 512 or a multiple of 512 -- one head of P = 64, or
+ * d_inner / ngroups of the Mamba-2 sizes), and D <= 2048 * V, else
+ * SSD_ERR_UNSUPPORTED.  y, z, out and norm_w must be 16-byte aligned and
+ * z_stride a multiple of V (SSD_ERR_ALIGNMENT).  eps >= 0.  rows = 0 is a
+ * no-op.  Errors: SSD_ERR_INVALID_ARG for bad sizes, eps, null y/out or
+ * overlapping buffers.
+ */
+int ssd_gated_rmsnorm(long rows, int D, int group, int dtype, const void *y, const void *z, long z_stride,
+                      const float *norm_w, float eps, void *out, hipStream_t stream);
+
+/*
  * Stage timing -- a profiling aid, kept per host thread.
  * ssd_stage_timing(1) makes the following ssd_prefill calls of the calling
  * thread launch each kernel with a pair of HIP events stamped when that

@@ -34,6 +34,7 @@ SIGNATURES = {
     "ssd_decode_step": (_i, [_i] * 6 + [_p] * 8 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "ssd_decode_step_dt_raw": (_i, [_i] * 6 + [_p] * 3 + [_f, _f] + [_p] * 6 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "conv_state_update": (_i, [_i] * 5 + [_p] * 4 + [_i, _p, _p]),
+    "ssd_gated_rmsnorm": (_i, [_l, _i, _i, _i, _p, _p, _l, _p, _f, _p, _p]),
     "ssd_stage_timing": (_i, [_i]),
     "ssd_stage_times": (_i, [ctypes.POINTER(ctypes.c_float), _i, ctypes.POINTER(_i)]),
     "ssd_stage_name": (ctypes.c_char_p, [_i]),
@@ -198,6 +199,47 @@ def conv_state_update(conv_state, xBC, conv_w, conv_b=None, *, activation=0, out
     rc = lib().conv_state_update(B, T, C, Km1 + 1, code, _ptr(conv_state), _ptr(xBC), _ptr(conv_w),
                                  _ptr(conv_b), int(activation), _ptr(out), _stream(stream))
     _check("conv_state_update", rc)
+    return out
+
+
+def _row_stride(t, D, name):
+    """Element stride between consecutive rows of t viewed as [rows, D]
+    (channels contiguous, rows evenly spaced)."""
+    if t.stride(-1) != 1 or t.shape[-1] != D:
+        raise ValueError(f"{name} must have {D} contiguous channels on its last axis")
+    if t.dim() == 1:
+        return D
+    stride = t.stride(-2)
+    expect = stride
+    for k in range(t.dim() - 2, 0, -1):
+        expect *= t.shape[k]
+        if t.shape[k - 1] > 1 and t.stride(k - 1) != expect:
+            raise ValueError(f"{name}: rows must be evenly spaced")
+    return stride
+
+
+def ssd_gated_rmsnorm(y, z=None, norm_w=None, *, group, eps=1e-5, out=None, stream=None):
+    """out = y * silu(z) scaled per group of ``group`` channels to unit RMS
+    (plus eps) and by norm_w (fp32 [D]).  y [..., D] contiguous; z of y's
+    shape with contiguous channels and evenly spaced rows (a column slice of
+    a wider projection is fine) or None; out may be y (in place)."""
+    _dense(y, "y")
+    _dense(norm_w, "norm_w")
+    D = y.shape[-1]
+    rows = y.numel() // D if D else 0
+    z_stride = 0
+    if z is not None:
+        if tuple(z.shape) != tuple(y.shape) or z.dtype != y.dtype:
+            raise ValueError("z must match y's shape and dtype")
+        z_stride = _row_stride(z, D, "z")
+    if norm_w is not None and (norm_w.dtype != torch.float32 or tuple(norm_w.shape) != (D,)):
+        raise ValueError("norm_w must be fp32 [D]")
+    if out is None:
+        out = torch.empty_like(y)
+    _dense(out, "out")
+    rc = lib().ssd_gated_rmsnorm(rows, D, int(group), _dtype_code(y), _ptr(y), _ptr(z), z_stride, _ptr(norm_w),
+                                 float(eps), _ptr(out), _stream(stream))
+    _check("ssd_gated_rmsnorm", rc)
     return out
 
 

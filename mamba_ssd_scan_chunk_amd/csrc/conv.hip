@@ -95,39 +95,6 @@ __global__ __launch_bounds__(kThreads) void conv_update_kernel(ConvArgs a) {
 // template argument, so the window lives in registers.  The SiLU of the bf16
 // output uses the hardware exp2 and reciprocal (relative error ~1e-7, far
 // below the output's bf16 rounding); fp32 keeps expf and IEEE division.
-template <typename T> struct Vec16;
-template <> struct Vec16<bf16_t> {
-    static constexpr int V = 8;
-    __device__ static void unpack(const uint4 &r, float (&f)[8]) {
-        const unsigned w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-    __device__ static uint4 pack(const float (&f)[8]) {
-        unsigned w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-        return make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    __device__ static float act(float v) {
-        return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * 1.44269504088896341f));
-    }
-};
-template <> struct Vec16<float> {
-    static constexpr int V = 4;
-    __device__ static void unpack(const uint4 &r, float (&f)[4]) {
-        f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
-        f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
-    }
-    __device__ static uint4 pack(const float (&f)[4]) {
-        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
-    }
-    __device__ static float act(float v) { return silu(v); }
-};
-
 template <typename T, int K>
 __global__ __launch_bounds__(kVThreads) void conv_update_vec(ConvArgs a) {
     using VT = Vec16<T>;

@@ -301,6 +301,31 @@ SSD_API int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_
     return hip_status(ssd::launch_conv_update(a, dtype, stream));
 }
 
+SSD_API int ssd_gated_rmsnorm(long rows, int D, int group, int dtype, const void *y, const void *z, long z_stride,
+                              const float *norm_w, float eps, void *out, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSD_ERR_INVALID_ARG;
+    if (rows < 0 || D < 1 || group < 1 || D % group != 0 || !(eps >= 0.0f && eps < 1e30f)) return SSD_ERR_INVALID_ARG;
+    if (rows > 0 && (!y || !out)) return SSD_ERR_INVALID_ARG;
+    if (z && z_stride < D) return SSD_ERR_INVALID_ARG;
+    const size_t es = esize(dtype);
+    const int V = (int)(16 / es), gv = group / V;
+    if (group % V != 0 || D / V > ssd::kNormMaxVecs || rows > 0x7fffffffL) return SSD_ERR_UNSUPPORTED;
+    if (gv <= 64 ? (gv & (gv - 1)) != 0 : gv % 64 != 0) return SSD_ERR_UNSUPPORTED;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(z, 16) || !aligned(norm_w, 16) || (z && z_stride % V != 0))
+        return SSD_ERR_ALIGNMENT;
+    // out is y itself or disjoint from every input
+    const size_t b_y = mul(mul((size_t)rows, (size_t)D), es);
+    const size_t b_z = z && rows > 0 ? mul(mul((size_t)(rows - 1), (size_t)z_stride) + (size_t)D, es) : 0;
+    const size_t b_w = norm_w ? (size_t)D * sizeof(float) : 0;
+    if ((out != y && overlap(out, b_y, y, b_y)) || overlap(out, b_y, z, b_z) || overlap(out, b_y, norm_w, b_w))
+        return SSD_ERR_INVALID_ARG;
+    if (rows == 0) return SSD_OK;
+    ssd::NormArgs a;
+    a.rows = rows; a.D = D; a.group = group; a.z_stride = z_stride;
+    a.y = y; a.z = z; a.w = norm_w; a.eps = eps; a.out = out;
+    return hip_status(ssd::launch_gated_rmsnorm(a, dtype, stream));
+}
+
 // ---- stage timing (per host thread)
 namespace {
 constexpr int kMaxStages = 8;

@@ -94,4 +94,17 @@ struct ConvArgs {
 };
 hipError_t launch_conv_update(const ConvArgs &a, int dtype, hipStream_t s);
 
+struct NormArgs {
+    long rows;
+    int D, group;
+    long z_stride;
+    const void *y, *z;  // z null: no gate
+    const float *w;     // null: weight 1
+    float eps;
+    void *out;
+};
+// Largest row the one-wave-per-row kernel takes, in 16-byte vectors.
+constexpr int kNormMaxVecs = 64 * 32;
+hipError_t launch_gated_rmsnorm(const NormArgs &a, int dtype, hipStream_t s);
+
 }  // namespace ssd

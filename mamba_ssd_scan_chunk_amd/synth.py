@@ -14,6 +14,7 @@ Distributions (``N(mu, v)`` has variance ``v``):
     D      ~ N(0, 1)
     conv_w ~ N(0, 0.02),  raw conv inputs ~ N(0, 1)
     dt_raw ~ N(0, 1), dt_bias ~ U(ln 1e-3, ln 0.1)   (raw step-size projection)
+    z ~ N(0, 1), norm_w ~ U(0.5, 1.5)   (gate branch and normalisation weight)
 Variants: "spec" (as above), "d0" (D = 0, so the output is the SSM term
 alone), "slow" (A_log ~ U(-7, -4) and dt = 1e-3, so state survives across
 thousands of tokens and every chunk hand-off matters), "steep" (A_log ~
@@ -132,6 +133,16 @@ def make_dt_raw(shape, H, seed=0):
     raw = _normal(rng, tuple(shape) + (H,))
     bias = rng.uniform(math.log(1e-3), math.log(0.1), size=H).astype(np.float32)
     return torch.from_numpy(raw), torch.from_numpy(bias)
+
+
+def make_gate(shape, D, dtype="f32", seed=0):
+    """The gate branch z [*shape, D] ~ N(0, 1) in ``dtype`` and the
+    normalisation weight norm_w [D] ~ U(0.5, 1.5) in fp32.
+    Draw order: z, norm_w."""
+    rng = np.random.default_rng(seed)
+    z = _normal(rng, tuple(shape) + (D,))
+    w = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    return _store(z, dtype), torch.from_numpy(w)
 
 
 def make_state(B, H, P, N, seed=0, scale=1.0):

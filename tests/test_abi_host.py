@@ -222,6 +222,48 @@ def test_conv_zero_tokens_is_a_no_op(lib):
     assert _conv(lib, T=0, x=None) == bd.SSD_OK
 
 
+def _norm(lib, rows=4, D=5120, group=5120, dtype=1, eps=1e-5, z_stride=None, **over):
+    p = dict(y=_addr(0), z=_addr(1), w=_addr(2), out=_addr(3))
+    p.update(over)
+    zs = D if z_stride is None else z_stride
+    return lib.ssd_gated_rmsnorm(rows, D, group, dtype, p["y"], p["z"], zs, p["w"], eps, p["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), bd.SSD_ERR_INVALID_ARG),
+    (dict(D=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(group=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(group=1000), bd.SSD_ERR_INVALID_ARG),            # does not divide D
+    (dict(dtype=2), bd.SSD_ERR_INVALID_ARG),
+    (dict(eps=-1e-6), bd.SSD_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), bd.SSD_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), bd.SSD_ERR_INVALID_ARG),
+    (dict(y=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(out=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(z_stride=5000), bd.SSD_ERR_INVALID_ARG),         # rows of z shorter than D
+    (dict(out=_addr(0, 1024)), bd.SSD_ERR_INVALID_ARG),    # out partly overlaps y
+    (dict(out=_addr(1, 0)), bd.SSD_ERR_INVALID_ARG),       # out overlaps z
+    (dict(out=_addr(2, 16)), bd.SSD_ERR_INVALID_ARG),      # out overlaps norm_w
+    (dict(D=20, group=20), bd.SSD_ERR_UNSUPPORTED),         # group not a multiple of 8 bf16
+    (dict(D=960, group=96), bd.SSD_ERR_UNSUPPORTED),       # 12 vectors: neither 2^k <= 64 nor 64m
+    (dict(D=5120, group=640), bd.SSD_ERR_UNSUPPORTED),     # 80 vectors
+    (dict(D=16384 + 512, group=512), bd.SSD_ERR_UNSUPPORTED),  # row longer than 2048 vectors
+    (dict(dtype=0, D=8192 + 256, group=256), bd.SSD_ERR_UNSUPPORTED),
+    (dict(y=_addr(0, 8)), bd.SSD_ERR_ALIGNMENT),
+    (dict(z=_addr(1, 8)), bd.SSD_ERR_ALIGNMENT),
+    (dict(w=_addr(2, 4)), bd.SSD_ERR_ALIGNMENT),
+    (dict(z_stride=5124), bd.SSD_ERR_ALIGNMENT),            # row stride not a multiple of 8 bf16
+])
+def test_gated_rmsnorm_rejects(lib, kw, code):
+    assert _norm(lib, **kw) == code
+
+
+def test_gated_rmsnorm_accepts_in_place_and_empty(lib):
+    # rows = 0 returns before any HIP call; out == y (in place) is allowed
+    assert _norm(lib, rows=0, out=_addr(0)) == bd.SSD_OK
+    assert _norm(lib, rows=0, y=None, out=None, z=None, w=None) == bd.SSD_OK
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
 
