@@ -16,8 +16,8 @@ with A_h = -exp(A_log[h]), plus the depthwise causal convolution over a
 (K-1)-token window cache and the step-size chain dt = clip(softplus(dt_raw +
 dt_bias), dt_min, dt_max) of §1.2 (``dt_from_raw``), and the layer's closing
 gated RMS normalisation of §3.2 and §4.1 (``gated_rmsnorm``).  ``ssd_scan`` is the
-prefill, ``decode_step`` is one step of the same recurrence after one step of
-the convolution cache.
+prefill (``ssd_scan_varlen`` the same per packed sequence), ``decode_step`` is
+one step of the same recurrence after one step of the convolution cache.
 
 All arithmetic is in C (``ssd_oracle.c``), double precision, token by token.
 Every function here only marshals arrays.  Pins that tie this oracle to the
@@ -122,6 +122,30 @@ def ssd_scan(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, want_y=True,
     )
     if rc != 0:
         raise ValueError(f"oracle_ssd_scan failed ({rc})")
+    return y, fs
+
+
+def ssd_scan_varlen(x, dt, A_log, Bm, Cm, cu_seqlens, D=None, init_state=None, *, nthreads=None):
+    """The prefill of sequences packed without padding: sequence b is rows
+    cu_seqlens[b] .. cu_seqlens[b+1] of x [T,H,P], dt [T,H], Bm/Cm [T,G,N],
+    scanned on its own from init_state[b] (or 0) by ``ssd_scan``.
+
+    Returns (y [T,H,P], final_state [B,H,P,N]) as float64 arrays.
+    """
+    x, dt, Bm, Cm = map(_f64, (x, dt, Bm, Cm))
+    cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+    T, H, P = x.shape
+    N = Bm.shape[2]
+    nseq = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and all(a <= b for a, b in zip(cu, cu[1:]))
+    init = _f64(init_state)
+    y = np.empty((T, H, P), np.float64)
+    fs = np.empty((nseq, H, P, N), np.float64)
+    for b in range(nseq):
+        lo, hi = cu[b], cu[b + 1]
+        yb, fs[b:b + 1] = ssd_scan(x[None, lo:hi], dt[None, lo:hi], A_log, Bm[None, lo:hi], Cm[None, lo:hi], D,
+                                   None if init is None else init[b:b + 1], nthreads=nthreads)
+        y[lo:hi] = yb[0]
     return y, fs
 
 

@@ -15,6 +15,8 @@ fails at least one of them:
   * convolution: one-hot taps, numpy.convolve, torch SiLU;
   * step-size chain: softplus(0) = ln 2, softplus(u) - softplus(-u) = u,
     400-digit decimal log(1 + e^u), the per-head bias index, clip bounds;
+  * packed sequences: equal lengths reproduce the batched layout, an empty
+    sequence keeps its state, sequences do not see each other;
   * gated RMS normalisation: torch's rms_norm and silu on the gated values,
     unit RMS per group, scale invariance, group independence, a constant
     group's closed form, a saturated gate.
@@ -475,3 +477,45 @@ def test_gated_rmsnorm_gate(oracle):
                                oracle.gated_rmsnorm(y2, group=8, eps=0.0), rtol=1e-13)
     with pytest.raises(ValueError):
         oracle.gated_rmsnorm(y, group=7)                      # groups must tile the channels
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences (varlen)
+# ---------------------------------------------------------------------------
+
+def test_varlen_equal_lengths_is_the_batched_layout(oracle):
+    B, L, H, P, G, N = 3, 20, 2, 3, 1, 4
+    d = _inputs(B=B, L=L, H=H, P=P, G=G, N=N, seed=70)
+    h0 = np.random.default_rng(71).standard_normal((B, H, P, N))
+    y_ref, fs_ref = oracle.ssd_scan(**d, init_state=h0)
+    packed = {k: (v.reshape((B * L,) + v.shape[2:]) if k in ("x", "dt", "Bm", "Cm") else v) for k, v in d.items()}
+    y, fs = oracle.ssd_scan_varlen(cu_seqlens=[0, L, 2 * L, 3 * L], init_state=h0, **packed)
+    np.testing.assert_array_equal(y, y_ref.reshape(B * L, H, P))
+    np.testing.assert_array_equal(fs, fs_ref)
+
+
+def test_varlen_sequences_are_independent_and_empty_ones_keep_state(oracle):
+    H, P, G, N = 2, 3, 1, 4
+    cu = [0, 7, 7, 19, 20]
+    d = _inputs(B=1, L=20, H=H, P=P, G=G, N=N, seed=72)
+    packed = {k: (v[0] if k in ("x", "dt", "Bm", "Cm") else v) for k, v in d.items()}
+    h0 = np.random.default_rng(73).standard_normal((4, H, P, N))
+    y, fs = oracle.ssd_scan_varlen(cu_seqlens=cu, init_state=h0, **packed)
+    np.testing.assert_array_equal(fs[1], h0[1])                   # empty sequence
+    # perturbing sequence 2's tokens leaves sequences 0 and 3 unchanged
+    x2 = packed["x"].copy()
+    x2[7:19] += 1.0
+    y2, fs2 = oracle.ssd_scan_varlen(cu_seqlens=cu, init_state=h0, **{**packed, "x": x2})
+    np.testing.assert_array_equal(y2[:7], y[:7])
+    np.testing.assert_array_equal(y2[19:], y[19:])
+    np.testing.assert_array_equal(fs2[[0, 1, 3]], fs[[0, 1, 3]])
+    assert not np.allclose(y2[7:19], y[7:19])
+    # a sequence starts from its own state, not from the previous sequence's
+    # end: its first output is dt x (C.B) + D x + C.(decay h0[b]) x-free term
+    t = 7
+    A = -np.exp(packed["A_log"])
+    for h in range(H):
+        st = np.exp(packed["dt"][t, h] * A[h]) * h0[2, h] + packed["dt"][t, h] * np.outer(packed["x"][t, h],
+                                                                                            packed["Bm"][t, 0])
+        np.testing.assert_allclose(y[t, h], st @ packed["Cm"][t, 0] + packed["D"][h] * packed["x"][t, h],
+                                   rtol=1e-13, atol=1e-13)
