@@ -335,6 +335,48 @@ def norm_record(args):
                      "decode_rows": {"workload": dw.name, "rows": dw.B, "graph_us": round(dms * 1e3, 2)}}}
 
 
+def bench_varlen(args):
+    """Prefill of 16 prompts of the workload's layer packed without padding,
+    lengths log-uniform in [64, 4096], against the same prompts padded to the
+    longest one in a uniform batch."""
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    lengths = synth.make_lengths(16, 64, 4096, seed=9)
+    d = {k: v.cuda() for k, v in synth.make_varlen(lengths, w.H, w.P, w.G, w.N, w.dtype, seed=10).items()}
+    T = sum(lengths)
+    y = torch.empty_like(d["x"])
+    fs = torch.empty((len(lengths), w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+    code = bd.SSD_BF16 if w.dtype == "bf16" else bd.SSD_F32
+    ws = torch.empty(max(1, bd.lib().ssd_prefill_varlen_workspace_bytes(len(lengths), T, w.H, w.P, w.G, w.N, w.Q,
+                                                                        code)), dtype=torch.uint8, device="cuda")
+
+    def step(_):
+        bd.ssd_prefill_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], d["cu_seqlens"], None, Q=w.Q,
+                              y=y, final_state=fs, workspace=ws)
+
+    ms = _timed(step, args.steps, args.warmup, "varlen")
+    del d, y, ws
+    Lmax = max(lengths)
+    p = {k: v.cuda() for k, v in synth.make_prefill(len(lengths), Lmax, w.H, w.P, w.G, w.N, w.dtype, seed=11).items()}
+
+    def padded(_):
+        bd.ssd_prefill(p["x"], p["dt"], p["A_log"], p["Bm"], p["Cm"], p["D"], None, Q=w.Q, final_state=fs)
+
+    pms = _timed(padded, max(5, args.steps // 5), 2, "varlen_padded")
+    return lengths, T, ms, Lmax, pms
+
+
+def varlen_record(args):
+    lengths, T, ms, Lmax, pms = bench_varlen(args)
+    return {"varlen": {"sequences": len(lengths), "tokens": T, "lengths": lengths, "us": round(ms * 1e3, 2),
+                       "tokens_per_s": round(T / (ms * 1e-3), 1),
+                       "padded": {"batch": len(lengths), "seq_len": Lmax, "us": round(pms * 1e3, 2)}}}
+
+
 def cpu_baseline(args):
     import oracle
     from mamba_ssd_scan_chunk_amd import synth
@@ -365,9 +407,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-only", action="store_true", help="skip the decode, conv and norm legs")
-    ap.add_argument("--legs", default="prefill,decode,conv,norm",
-                    help="comma-separated subset of prefill,decode,conv,norm,copy (for profiling runs)")
+    ap.add_argument("--prefill-only", action="store_true", help="skip every leg but the prefill")
+    ap.add_argument("--legs", default="prefill,decode,conv,norm,varlen",
+                    help="comma-separated subset of prefill,decode,conv,norm,varlen,copy (for profiling runs)")
     ap.add_argument("--no-decode-extras", action="store_true",
                     help="decode leg: only the stated workload's one-state and rotated-state runs (no other batch, "
                          "raw-step or recompute legs), so that every decode dispatch has the same size")
@@ -398,6 +440,8 @@ def main():
         out.update(conv_record(args))
     if "norm" in legs:
         out.update(norm_record(args))
+    if "varlen" in legs:
+        out.update(varlen_record(args))
     if "copy" in legs:
         out.update(copy_record(args))
     if HOST_BOUND:

@@ -91,8 +91,9 @@ enum {
  * Q is the chunk length (the last chunk may be shorter: L need not be a
  * multiple of Q).  L = 0 is allowed: y is untouched and final_state receives
  * init_state (or zeros).  Alignment: x, Bm, Cm, y, init_state, final_state
- * 16-byte aligned.  Limits: 1 <= P <= 256, 1 <= N <= 256, 16 <= Q <= 256
- * (Q a multiple of 16).  bf16 with (P, N, Q) = (64, 128, 256) runs on MFMA
+ * 16-byte aligned.  Limits: 1 <= P <= 256, 1 <= N <= 256, 1 <= Q <= 1024
+ * (Q = 512 is the chunk suggested for contexts beyond 8k tokens, bqwf.cn
+ * article §6.3).  bf16 with (P, N, Q) = (64, 128, 256) runs on MFMA
  * (bf16 operands, fp32 accumulation, decay factors in fp32); every other
  * shape runs on the fp32 vector path.  The MFMA path factors the decay
  * exp(cs_l - cs_s) per 32-token tile; a chunk whose factors would leave the
@@ -132,6 +133,42 @@ int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, int dtyp
  * Returns (size_t)-1 for arguments ssd_prefill would reject. */
 size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N,
                                    int Q, int dtype);
+
+/*
+ * ssd_prefill_varlen -- ssd_prefill over B sequences of different lengths
+ * packed one after another (no padding): sequence b is the token rows
+ * [cu_seqlens[b], cu_seqlens[b + 1]) of
+ *
+ *   x [T,H,P], dt [T,H], Bm [T,G,N], Cm [T,G,N], y [T,H,P]
+ *
+ * and its scan starts from init_state[b] (or zeros) and leaves
+ * final_state[b] ([B,H,P,N] as in ssd_prefill).  Each sequence is chunked
+ * from its own first token (its last chunk may be short), so the result for
+ * a sequence equals ssd_prefill on that sequence alone.  Source: the
+ * chunked scan of bqwf.cn article §1.1-§1.2, applied per sequence.
+ *
+ *   cu_seqlens [B+1] int32, DEVICE memory, 4-byte aligned: 0 = cu_seqlens[0]
+ *                <= cu_seqlens[1] <= ... <= cu_seqlens[B] = T.  The library
+ *                reads it on the device only (no host synchronisation), so it
+ *                cannot check it: offsets that break this contract give
+ *                unspecified outputs but never an access outside x, y, dt,
+ *                Bm, Cm or the workspace (offsets are clamped to [0, T]).
+ *   T            total tokens (0 allowed: final_state receives init_state)
+ * Empty sequences are allowed (their final state is their initial state).
+ * The workspace (ssd_prefill_varlen_workspace_bytes) also holds the chunk
+ * table the library builds on the device.  Every other argument, limit,
+ * alignment rule and error is as for ssd_prefill; T < 2^31.
+ */
+int ssd_prefill_varlen(int B, int T, int H, int P, int G, int N, int Q, int dtype,
+                       const int *cu_seqlens, const void *x, const float *dt, const float *A_log,
+                       const void *Bm, const void *Cm, const float *D,
+                       const float *init_state, void *y, float *final_state,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssd_prefill_varlen needs (0 if none); (size_t)-1 for
+ * arguments it would reject. */
+size_t ssd_prefill_varlen_workspace_bytes(int B, int T, int H, int P, int G, int N,
+                                          int Q, int dtype);
 
 /*
  * ssd_decode_step -- one token of the recurrence on the O(1) cache, fused

@@ -97,14 +97,13 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, unsigned
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-// Load the x chunk of head h ([Q tokens][P] bf16, row stride H*P): thread t
-// owns the 8x8 block of tokens 8*(t/8).. and features 8*(t%8)..; tokens at
-// or past Qc read as zero.
-__device__ __forceinline__ void load_x_raw(const PrefillArgs &a, int b, int t0, int Qc, int h, u32x4 (&raw)[8],
-                                           int t) {
+// Load the x chunk of head h ([Q tokens][P] bf16, row stride H*P) whose
+// first token is row tok0: thread t owns the 8x8 block of tokens 8*(t/8)..
+// and features 8*(t%8)..; tokens at or past Qc read as zero.
+__device__ __forceinline__ void load_x_raw(const PrefillArgs &a, long tok0, int Qc, int h, u32x4 (&raw)[8], int t) {
     const int sb = t >> 3, pb = t & 7;
     const unsigned rs = (unsigned)a.H * kP * 2;  // row stride in bytes
-    const bf16_t *x0 = (const bf16_t *)a.x + (((long)b * a.L + t0) * a.H + h) * kP;
+    const bf16_t *x0 = (const bf16_t *)a.x + (tok0 * a.H + h) * kP;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(x0, (unsigned)(Qc - 1) * rs + kP * 2);
 #pragma unroll
     for (int k = 0; k < 8; ++k) raw[k] = buf_load16(r, (unsigned)(sb * 8 + k) * rs + pb * 16);
@@ -112,8 +111,8 @@ __device__ __forceinline__ void load_x_raw(const PrefillArgs &a, int b, int t0, 
 
 // dt of token tid of the chunk (0 at or past Qc), after the optional
 // preprocessing of the raw value.
-__device__ __forceinline__ float load_dt(const PrefillArgs &a, int b, int t0, int Qc, int h, int t) {
-    const float *d0 = a.dt + ((long)b * a.L + t0) * a.H + h;
+__device__ __forceinline__ float load_dt(const PrefillArgs &a, long tok0, int Qc, int h, int t) {
+    const float *d0 = a.dt + tok0 * a.H + h;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(d0, (unsigned)((Qc - 1) * a.H + 1) * 4);
     const float v = buf_load_f32(r, (unsigned)t * a.H * 4);
     if (!a.dtp.dt_raw) return v;
@@ -177,16 +176,17 @@ constexpr int kK0Blocks = kK0Tiles + kN / 32;  // plus one per 32 columns of B
 
 __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char bl[kQ * 64];  // B[:, 32 columns] as [token][32] bf16
-    const int c = blockIdx.x, b = blockIdx.z;
+    const long f = (long)blockIdx.z * a.nchunks + blockIdx.x;
+    const ChunkEntry ch = chunk_at(a, f);
+    const int Qc = ch.Qc;
+    if (Qc <= 0) return;  // unused slot of a packed prefill
     const int part = blockIdx.y % kK0Blocks, g = blockIdx.y / kK0Blocks;
-    const int t0 = c * kQ;
-    const int Qc = min(kQ, a.L - t0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
-    const long cg = ((long)b * a.nchunks + c) * a.G + g;
+    const long cg = f * a.G + g;
     const unsigned rs = (unsigned)a.G * kN * 2;  // token stride of B and C in bytes
-    const long base = (((long)b * a.L + t0) * a.G + g) * kN;
+    const long base = ((long)ch.tok0 * a.G + g) * kN;
     const unsigned bytes = (unsigned)(Qc - 1) * rs + kN * 2;
     const __amdgpu_buffer_rsrc_t brs = make_rsrc((const bf16_t *)a.Bm + base, bytes);
 
@@ -279,17 +279,18 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     const int li = lane & 31, lh = lane >> 5;
     const int item = xcd_item(blockIdx.x, gridDim.x);  // grid = one workgroup per item
     const int h = item % a.H, bc = item / a.H;
-    const int c = bc % a.nchunks, b = bc / a.nchunks;
-    const int t0 = c * kQ;
-    const int Qc = min(kQ, a.L - t0);
+    const ChunkEntry ch = chunk_at(a, bc);
+    const int Qc = ch.Qc;
+    if (Qc <= 0) return;  // unused slot of a packed prefill
+    const long tok0 = ch.tok0;
     const int g = h / (a.H / a.G);
     const long cg = (long)bc * a.G + g;
 
     // every global load of this workgroup is issued before the cumsum, dt
     // first: loads retire in issue order, so the cumsum waits for dt only
-    const float dtv = load_dt(a, b, t0, Qc, h, tid);
+    const float dtv = load_dt(a, tok0, Qc, h, tid);
     u32x4 raw[8];
-    load_x_raw(a, b, t0, Qc, h, raw, tid);
+    load_x_raw(a, tok0, Qc, h, raw, tid);
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[kQ / 16];
 #pragma unroll
@@ -411,18 +412,19 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
     const int ltA = wave, ltB = kTiles - 1 - wave;
     const int item = xcd_item(blockIdx.x, gridDim.x);  // grid = one workgroup per item
     const int h = item % a.H, bc = item / a.H;
-    const int c = bc % a.nchunks, b = bc / a.nchunks;
-    const int t0 = c * kQ;
-    const int Qc = min(kQ, a.L - t0);
+    const ChunkEntry ch = chunk_at(a, bc);
+    const int Qc = ch.Qc;
+    if (Qc <= 0) return;  // unused slot of a packed prefill
+    const long tok0 = ch.tok0;
     const int g = h / (a.H / a.G);
     const long cg = (long)bc * a.G + g;
 
     // ---- global loads, all issued before the cumsum: dt, x, h_{c-1}, the C
     // operands of column tile ltA and the first G^T tiles
     // dt first: loads retire in issue order, so the cumsum waits for dt only
-    const float dtv = load_dt(a, b, t0, Qc, h, tid);
+    const float dtv = load_dt(a, tok0, Qc, h, tid);
     u32x4 raw[8], hv[4];
-    load_x_raw(a, b, t0, Qc, h, raw, tid);
+    load_x_raw(a, tok0, Qc, h, raw, tid);
     {
         const bf16_t *hg = a.ws_hb + (long)item * kP * kN;
 #pragma unroll
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
             const int r = 8 * i + (lane >> 3);
             const u32x4 v = *(const u32x4 *)(st + r * kYRow + 16 * (lane & 7));
             const int l = lt * 32 + r;
-            if (l < Qc) *(u32x4 *)((bf16_t *)a.y + (((long)b * a.L + t0 + l) * a.H + h) * kP + 8 * (lane & 7)) = v;
+            if (l < Qc) *(u32x4 *)((bf16_t *)a.y + ((tok0 + l) * a.H + h) * kP + 8 * (lane & 7)) = v;
         }
     };
 
@@ -646,14 +648,14 @@ __global__ __launch_bounds__(kThreads) void chunk_out_mfma(PrefillArgs a) {
 // + 8] (tokens past the end as zero).
 __device__ __forceinline__ void pack_c(const PrefillArgs &a, long blk) {
     const int q = (int)(blk % (kTiles / 2));
-    const long cg = blk / (kTiles / 2);  // (b * nchunks + c) * G + g
+    const long cg = blk / (kTiles / 2);  // slot * G + g
     const int g = (int)(cg % a.G);
-    const long bc = cg / a.G;
-    const int c = (int)(bc % a.nchunks), b = (int)(bc / a.nchunks);
-    const int t0 = c * kQ, Qc = min(kQ, a.L - t0);
+    const ChunkEntry ch = chunk_at(a, cg / a.G);
+    const int Qc = ch.Qc;
+    if (Qc <= 0) return;  // unused slot of a packed prefill
     const unsigned rs = (unsigned)a.G * kN * 2;
     const __amdgpu_buffer_rsrc_t crs =
-        make_rsrc((const bf16_t *)a.Cm + (((long)b * a.L + t0) * a.G + g) * kN, (unsigned)(Qc - 1) * rs + kN * 2);
+        make_rsrc((const bf16_t *)a.Cm + ((long)ch.tok0 * a.G + g) * kN, (unsigned)(Qc - 1) * rs + kN * 2);
     u32x4 *ct = (u32x4 *)(a.ws_ct + cg * kBTChunk);
     u32x4 v[4];
 #pragma unroll
@@ -677,9 +679,9 @@ __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long 
     const long bh = e / PN4;
     const long pn = e - bh * PN4;
     const int h = (int)(bh % a.H);
-    const long b = bh / a.H;
+    const SeqEntry sq = seq_chunks(a, bh / a.H);
     float4 hv = a.init_state ? ((const float4 *)a.init_state)[bh * PN4 + pn] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int nch = a.nchunks;
+    const int nch = sq.n;
     constexpr int kB = 8;
     for (int c0 = 0; c0 < nch; c0 += kB) {
         float4 sv[kB];
@@ -687,7 +689,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long 
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
             if (c0 + j < nch) {
-                const long hc = (b * nch + c0 + j) * a.H + h;
+                const long hc = ((long)sq.f0 + c0 + j) * a.H + h;
                 sv[j] = ((const float4 *)(a.ws_S + hc * kP * kN))[pn];
                 dv[j] = a.ws_dec[hc];
             }
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long 
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
             if (c0 + j < nch) {
-                const long hc = (b * nch + c0 + j) * a.H + h;
+                const long hc = ((long)sq.f0 + c0 + j) * a.H + h;
                 u32x2 o = {pack_bf16(hv.x, hv.y), pack_bf16(hv.z, hv.w)};
                 ((u32x2 *)(a.ws_hb + hc * kP * kN))[pn] = o;
                 const float d = dv[j];
@@ -717,17 +719,18 @@ long prefill_mfma_gt_elems_per_chunk() { return kGTChunk; }
 long prefill_mfma_bt_elems_per_chunk() { return kBTChunk; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
-    const long nitems = (long)a.B * a.nchunks * a.H;
+    const int gridB = a.chunks ? 1 : a.B;  // packed sequences: nchunks slots in all
+    const long nitems = (long)gridB * a.nchunks * a.H;
     if (nitems > 0x7fffffffL || (long)a.G * kK0Blocks > 65535 || a.nchunks > 0x7fffffff) return hipErrorInvalidConfiguration;
     stage_begin();
-    hipError_t e = launch_stage("chunk_pack_mfma", chunk_pack_mfma, dim3(a.nchunks, kK0Blocks * a.G, a.B),
+    hipError_t e = launch_stage("chunk_pack_mfma", chunk_pack_mfma, dim3(a.nchunks, kK0Blocks * a.G, gridB),
                                 dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
     e = launch_stage("chunk_state_mfma", chunk_state_mfma, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
     const long state_blocks = (total + kThreads - 1) / kThreads;
-    const long pack_blocks = (long)a.B * a.nchunks * a.G * (kTiles / 2);
+    const long pack_blocks = (long)gridB * a.nchunks * a.G * (kTiles / 2);
     if (state_blocks + pack_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)(state_blocks + pack_blocks)),
                      dim3(kThreads), 0, s, a, total, state_blocks);

@@ -45,18 +45,18 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(PrefillArgs a, lon
     const long bh = e / PNv;
     const long pn = e - bh * PNv;
     const int h = (int)(bh % a.H);
-    const long b = bh / a.H;
+    const SeqEntry sq = seq_chunks(a, bh / a.H);
     V hv;
     if (a.init_state) hv = ((const V *)a.init_state)[bh * PNv + pn];
     else vzero(hv);
-    const int nch = a.nchunks;
+    const int nch = sq.n;
     for (int c0 = 0; c0 < nch; c0 += kBatch) {
         V sv[kBatch];
         float dv[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             if (c0 + j < nch) {
-                const long hc = (b * nch + c0 + j) * a.H + h;
+                const long hc = ((long)sq.f0 + c0 + j) * a.H + h;
                 sv[j] = ((const V *)(a.ws_S + hc * a.P * a.N))[pn];
                 dv[j] = a.ws_dec[hc];
             }
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(PrefillArgs a, lon
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             if (c0 + j < nch) {
-                const long hc = (b * nch + c0 + j) * a.H + h;
+                const long hc = ((long)sq.f0 + c0 + j) * a.H + h;
                 ((V *)(a.ws_S + hc * a.P * a.N))[pn] = hv;
                 hv = step(dv[j], hv, sv[j]);
             }

@@ -19,6 +19,9 @@ namespace ssd {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTpt = 4;                    // chunk tokens per thread in the chunk-state kernel
+constexpr int kMaxQ = kThreads * kTpt;     // largest chunk this path takes
+static_assert(kMaxQ == kPrefillMaxQ, "chunk limit of the vector path");
 
 __device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
     const int lane = threadIdx.x & 63;
@@ -31,45 +34,69 @@ __device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
 }
 
 // Grid (nchunks, H, B).  Writes the in-chunk cumsum, the chunk decay and S_c.
+// A thread owns kTpt consecutive tokens of the chunk (Q <= kThreads * kTpt):
+// it sums them in order, a block scan of the thread totals gives each
+// thread's offset.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void chunk_state_vec(PrefillArgs a) {
     __shared__ double wsum[kThreads / 64];
-    __shared__ float wgt[256];
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int t0 = c * a.Q;
-    const int Qc = min(a.Q, a.L - t0);
+    __shared__ float wgt[kMaxQ];
+    __shared__ double cs_last_sh;
+    const int h = blockIdx.y;
+    const long f = (long)blockIdx.z * a.nchunks + blockIdx.x;
+    const ChunkEntry ch = chunk_at(a, f);
+    const int Qc = ch.Qc;
+    if (Qc <= 0) return;  // unused slot of a packed prefill
+    const long tok0 = ch.tok0;
     const int g = h / (a.H / a.G);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const double A = -exp((double)a.A_log[h]);
     const float Af = (float)A;
+    const int tpt = (Qc + kThreads - 1) / kThreads;  // tokens per thread, 1 .. kTpt
 
-    float dtv = 0.0f;
-    double v = 0.0;
-    if (tid < Qc) {
-        dtv = dt_value(a.dt[((long)b * a.L + t0 + tid) * a.H + h], a.dtp.dt_raw, a.dtp.dt_bias, h, a.dtp.dt_min,
-                       a.dtp.dt_max);
-        v = (double)(dtv * Af);
+    float dtv[kTpt];
+    double loc[kTpt];
+    double run = 0.0;
+#pragma unroll
+    for (int k = 0; k < kTpt; ++k) {
+        const int t = tid * tpt + k;
+        dtv[k] = 0.0f;
+        if (k < tpt && t < Qc) {
+            dtv[k] = dt_value(a.dt[(tok0 + t) * a.H + h], a.dtp.dt_raw, a.dtp.dt_bias, h,
+                              a.dtp.dt_min, a.dtp.dt_max);
+            run += (double)(dtv[k] * Af);
+        }
+        loc[k] = run;
     }
-    double inc = wave_inclusive_sum_f64(v);
+    double inc = wave_inclusive_sum_f64(run);
     if (lane == 63) wsum[wid] = inc;
     __syncthreads();
-    for (int w = 0; w < wid; ++w) inc += wsum[w];
-    __shared__ double cs_last_sh;
-    if (tid == Qc - 1) cs_last_sh = inc;
+    double base = inc - run;  // exclusive offset of this thread
+    for (int w = 0; w < wid; ++w) base += wsum[w];
+    const long hc = f * a.H + h;
+#pragma unroll
+    for (int k = 0; k < kTpt; ++k) {
+        const int t = tid * tpt + k;
+        if (k < tpt && t == Qc - 1) cs_last_sh = base + loc[k];
+    }
     __syncthreads();
     const double cs_last = cs_last_sh;
-    const long hc = ((long)b * a.nchunks + c) * a.H + h;
-    if (tid < Qc) {
-        wgt[tid] = expf((float)(cs_last - inc)) * dtv;
-        a.ws_cs[hc * a.Q + tid] = inc;
+#pragma unroll
+    for (int k = 0; k < kTpt; ++k) {
+        const int t = tid * tpt + k;
+        if (k < tpt && t < Qc) {
+            const double cs = base + loc[k];
+            wgt[t] = expf((float)(cs_last - cs)) * dtv[k];
+            a.ws_cs[hc * a.Q + t] = cs;
+        }
     }
     if (tid == 0) a.ws_dec[hc] = expm1f((float)cs_last);
     __syncthreads();
 
     const int P = a.P, N = a.N;
     const long HP = (long)a.H * P, GN = (long)a.G * N;
-    const T *xp = (const T *)a.x + (((long)b * a.L + t0) * a.H + h) * P;
-    const T *Bp = (const T *)a.Bm + (((long)b * a.L + t0) * a.G + g) * N;
+    const T *xp = (const T *)a.x + (tok0 * a.H + h) * P;
+    const T *Bp = (const T *)a.Bm + (tok0 * a.G + g) * N;
     float *Sp = a.ws_S + hc * P * N;
     for (int o = tid; o < P * N; o += kThreads) {
         const int p = o / N, n = o - (o / N) * N;
@@ -97,9 +124,11 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
 
     const int nlt = (a.Q + LT - 1) / LT;
     const int c = blockIdx.x / nlt, lt = blockIdx.x - (blockIdx.x / nlt) * nlt;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int t0 = c * a.Q;
-    const int Qc = min(a.Q, a.L - t0);
+    const int h = blockIdx.y;
+    const long f = (long)blockIdx.z * a.nchunks + c;
+    const ChunkEntry ch = chunk_at(a, f);
+    const int Qc = ch.Qc;
+    const long tok0 = ch.tok0;
     const int l0 = lt * LT;
     if (l0 >= Qc) return;
     const int lrows = min(LT, Qc - l0);
@@ -107,11 +136,11 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
     const int P = a.P, N = a.N;
     const long HP = (long)a.H * P, GN = (long)a.G * N;
     const int tid = threadIdx.x;
-    const long hc = ((long)b * a.nchunks + c) * a.H + h;
+    const long hc = f * a.H + h;
     const double *cs = a.ws_cs + hc * a.Q;
-    const T *xp = (const T *)a.x + (((long)b * a.L + t0) * a.H + h) * P;
-    const T *Bp = (const T *)a.Bm + (((long)b * a.L + t0) * a.G + g) * N;
-    const T *Cp = (const T *)a.Cm + (((long)b * a.L + t0) * a.G + g) * N;
+    const T *xp = (const T *)a.x + (tok0 * a.H + h) * P;
+    const T *Bp = (const T *)a.Bm + (tok0 * a.G + g) * N;
+    const T *Cp = (const T *)a.Cm + (tok0 * a.G + g) * N;
 
     for (int i = tid; i < LT * N; i += kThreads) {
         const int r = i / N, n = i - (i / N) * N;
@@ -137,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
         }
         if (tid < ST) {
             css[tid] = tid < srows ? cs[s0 + tid] : 0.0;
-            dts[tid] = tid < srows ? dt_value(a.dt[((long)b * a.L + t0 + s0 + tid) * a.H + h], a.dtp.dt_raw,
+            dts[tid] = tid < srows ? dt_value(a.dt[(tok0 + s0 + tid) * a.H + h], a.dtp.dt_raw,
                                               a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max)
                                    : 0.0f;
         }
@@ -167,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
 
     const float *hin = a.ws_S + hc * P * N;
     const float Dh = a.D ? a.D[h] : 0.0f;
-    T *yp = (T *)a.y + (((long)b * a.L + t0) * a.H + h) * P;
+    T *yp = (T *)a.y + (tok0 * a.H + h) * P;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int o = tid + k * kThreads;
@@ -188,9 +217,10 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s) {
-    if (a.B > 65535 || a.H > 65535) return hipErrorInvalidConfiguration;
+    const int gridB = a.chunks ? 1 : a.B;  // packed sequences: nchunks slots in all
+    if (gridB > 65535 || a.H > 65535) return hipErrorInvalidConfiguration;
     stage_begin();
-    dim3 g1(a.nchunks, a.H, a.B);
+    dim3 g1(a.nchunks, a.H, gridB);
     hipError_t e = dtype == DT_BF16
                        ? launch_stage("chunk_state_vec", chunk_state_vec<bf16_t>, g1, dim3(kThreads), 0, s, a)
                        : launch_stage("chunk_state_vec", chunk_state_vec<float>, g1, dim3(kThreads), 0, s, a);
@@ -198,7 +228,7 @@ hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s)
     e = launch_state_pass(a, s);
     if (e != hipSuccess) return e;
     const long nlt = (a.Q + LT - 1) / LT;
-    dim3 g3((unsigned)(a.nchunks * nlt), a.H, a.B);
+    dim3 g3((unsigned)(a.nchunks * nlt), a.H, gridB);
     return dtype == DT_BF16 ? launch_stage("chunk_out_vec", chunk_out_vec<bf16_t>, g3, dim3(kThreads), 0, s, a)
                             : launch_stage("chunk_out_vec", chunk_out_vec<float>, g3, dim3(kThreads), 0, s, a);
 }

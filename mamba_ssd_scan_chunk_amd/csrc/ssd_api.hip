@@ -39,20 +39,25 @@ size_t mul(size_t a, size_t b) {
     return a * b;
 }
 
+// L: tokens per sequence (uniform batch) or the packed total T (varlen).
 struct PrefillShape {
     int B, L, H, P, G, N, Q, dtype;
+    bool varlen;
 };
 
 int check_prefill_shape(const PrefillShape &s) {
     if (!valid_dtype(s.dtype)) return SSD_ERR_INVALID_ARG;
     if (s.B < 1 || s.L < 0 || s.H < 1 || s.P < 1 || s.G < 1 || s.N < 1 || s.Q < 1) return SSD_ERR_INVALID_ARG;
     if (s.H % s.G != 0) return SSD_ERR_INVALID_ARG;
-    if (s.P > 256 || s.N > 256 || s.Q > 256) return SSD_ERR_UNSUPPORTED;
+    if (s.P > 256 || s.N > 256 || s.Q > ssd::kPrefillMaxQ) return SSD_ERR_UNSUPPORTED;
     if (s.B > 65535 || s.H > 65535) return SSD_ERR_UNSUPPORTED;
     // in-chunk row offsets are 32-bit: Q * H * P and Q * G * N below 2^31
     if ((long)s.Q * s.H * s.P >= (1L << 31) || (long)s.Q * s.G * s.N >= (1L << 31)) return SSD_ERR_UNSUPPORTED;
-    // every element index must fit comfortably in 63 bits
-    if (mul(mul(mul((size_t)s.B, (size_t)s.L + (size_t)s.Q), (size_t)s.H), (size_t)s.P * s.N) >= ((size_t)1 << 60))
+    // token rows index with 32 bits; every element index must fit
+    // comfortably in 63 bits
+    const size_t rows = s.varlen ? (size_t)s.L : (size_t)s.B * s.L;
+    if (rows >= ((size_t)1 << 31)) return SSD_ERR_UNSUPPORTED;
+    if (mul(mul(rows + (size_t)s.B * s.Q, (size_t)s.H), (size_t)s.P * s.N) >= ((size_t)1 << 60))
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
@@ -65,12 +70,11 @@ bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
     return dtype == SSD_BF16 && P == 64 && N == 128 && Q == 256;
 }
 
-WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, int G, bool mfma) {
-    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0};
-    if (L <= 0) return w;
-    const size_t nch = ((size_t)L + Q - 1) / Q;
-    const size_t heads = (size_t)B * nch * H;
-    const size_t groups = (size_t)B * nch * G;
+WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq) {
+    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0};
+    if (slots <= 0) return w;
+    const size_t heads = (size_t)slots * H;
+    const size_t groups = (size_t)slots * G;
     w.off_S = 0;
     w.off_dec = align_up(w.off_S + heads * P * N * sizeof(float), 256);
     w.off_cs = align_up(w.off_dec + heads * sizeof(float), 256);
@@ -82,16 +86,38 @@ WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int 
     w.off_bt = align_up(w.off_gt + gt_bytes, 256);
     const size_t bt_bytes = mfma ? groups * prefill_mfma_bt_elems_per_chunk() * sizeof(uint16_t) : 0;
     w.off_ct = align_up(w.off_bt + bt_bytes, 256);
-    w.total = align_up(w.off_ct + bt_bytes, 256);  // C packed like B
+    w.off_tab = align_up(w.off_ct + bt_bytes, 256);  // C packed like B
+    const size_t tab_bytes = nseq > 0 ? (size_t)slots * sizeof(ChunkEntry) + (size_t)nseq * sizeof(SeqEntry) : 0;
+    w.total = align_up(w.off_tab + tab_bytes, 256);
     return w;
 }
 
 }  // namespace ssd
 
+namespace {
+// Chunk slots of a prefill: B * ceil(L / Q) for a uniform batch, the bound
+// varlen_slots(T, B, Q) for packed sequences (0 when there are no tokens).
+long prefill_slots(const PrefillShape &s) {
+    if (s.L <= 0) return 0;
+    return s.varlen ? ssd::varlen_slots(s.L, s.B, s.Q) : (long)s.B * ((s.L + s.Q - 1) / s.Q);
+}
+size_t workspace_bytes_for(const PrefillShape &s) {
+    return ssd::prefill_workspace_layout(prefill_slots(s), s.H, s.P, s.N, s.Q, s.G,
+                                         ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype), s.varlen ? s.B : 0)
+        .total;
+}
+}  // namespace
+
 SSD_API size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N, int Q, int dtype) {
-    const PrefillShape s{B, L, H, P, G, N, Q, dtype};
+    const PrefillShape s{B, L, H, P, G, N, Q, dtype, false};
     if (check_prefill_shape(s) != SSD_OK) return (size_t)-1;
-    return ssd::prefill_workspace_layout(B, L, H, P, N, Q, G, ssd::prefill_uses_mfma(P, N, Q, dtype)).total;
+    return workspace_bytes_for(s);
+}
+
+SSD_API size_t ssd_prefill_varlen_workspace_bytes(int B, int T, int H, int P, int G, int N, int Q, int dtype) {
+    const PrefillShape s{B, T, H, P, G, N, Q, dtype, true};
+    if (check_prefill_shape(s) != SSD_OK) return (size_t)-1;
+    return workspace_bytes_for(s);
 }
 
 namespace {
@@ -103,20 +129,25 @@ bool valid_dt_prep(float dt_min, float dt_max, const float *dt_bias) {
     return aligned(dt_bias, 4);
 }
 
-int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+// L is the per-sequence length, or with cu_seqlens (packed sequences, a
+// device array of B + 1 token offsets) the packed total T.
+int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, const int *cu_seqlens,
                  const void *x, const float *dt, const float *A_log,
                  const void *Bm, const void *Cm, const float *D,
                  const float *init_state, void *y, float *final_state,
-                 void *workspace, size_t workspace_bytes, hipStream_t stream, const ssd::DtPrep &dtp) {
-    const PrefillShape s{B, L, H, P, G, N, Q, dtype};
+                 void *workspace, size_t workspace_bytes, hipStream_t stream, const ssd::DtPrep &dtp,
+                 bool varlen = false) {
+    const PrefillShape s{B, L, H, P, G, N, Q, dtype, varlen};
     int rc = check_prefill_shape(s);
     if (rc != SSD_OK) return rc;
-    if (!A_log) return SSD_ERR_INVALID_ARG;
+    if (!A_log || (varlen && !cu_seqlens)) return SSD_ERR_INVALID_ARG;
     if (L > 0 && (!x || !dt || !Bm || !Cm || !y)) return SSD_ERR_INVALID_ARG;
+    if (!aligned(cu_seqlens, 4)) return SSD_ERR_ALIGNMENT;
 
     const size_t es = esize(dtype);
-    const size_t n_x = (size_t)B * L * H * P, n_bc = (size_t)B * L * G * N;
-    const size_t n_dt = (size_t)B * L * H, n_state = (size_t)B * H * P * N;
+    const size_t rows = varlen ? (size_t)L : (size_t)B * L;  // token rows of x, y, dt, Bm, Cm
+    const size_t n_x = rows * H * P, n_bc = rows * G * N;
+    const size_t n_dt = rows * H, n_state = (size_t)B * H * P * N;
     const size_t b_x = n_x * es, b_bc = n_bc * es, b_dt = n_dt * 4, b_state = n_state * 4;
 
     if (!aligned(x, 16) || !aligned(Bm, 16) || !aligned(Cm, 16) || !aligned(y, 16) ||
@@ -125,14 +156,16 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype,
         return SSD_ERR_ALIGNMENT;
 
     const bool mfma = ssd::prefill_uses_mfma(P, N, Q, dtype);
-    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(B, L, H, P, N, Q, G, mfma);
+    const long slots = prefill_slots(s);
+    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(slots, H, P, N, Q, G, mfma, varlen ? B : 0);
     const size_t b_ws = wl.total;
 
     // outputs may not overlap inputs, workspace or each other
     // (final_state == init_state exactly is allowed)
     struct R { const void *p; size_t n; };
     const R ins[] = {{x, b_x}, {dt, b_dt}, {A_log, (size_t)H * 4}, {Bm, b_bc}, {Cm, b_bc}, {D, D ? (size_t)H * 4 : 0},
-                     {dtp.dt_bias, dtp.dt_bias ? (size_t)H * 4 : 0}};
+                     {dtp.dt_bias, dtp.dt_bias ? (size_t)H * 4 : 0},
+                     {cu_seqlens, cu_seqlens ? (size_t)(B + 1) * 4 : 0}};
     if (L > 0) {
         for (const R &r : ins) if (overlap(y, b_x, r.p, r.n)) return SSD_ERR_INVALID_ARG;
         if (overlap(y, b_x, init_state, b_state) || overlap(y, b_x, final_state, b_state) ||
@@ -156,8 +189,10 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype,
     }
 
     ssd::PrefillArgs a;
-    a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.Q = Q;
-    a.nchunks = (L + Q - 1) / Q;
+    a.B = B; a.L = varlen ? 0 : L; a.H = H; a.P = P; a.G = G; a.N = N; a.Q = Q;
+    a.nchunks = varlen ? (int)slots : (L + Q - 1) / Q;
+    a.T = (int)rows;
+    a.cu_seqlens = varlen ? cu_seqlens : nullptr;
     a.x = x; a.dt = dt; a.A_log = A_log; a.Bm = Bm; a.Cm = Cm; a.D = D;
     a.dtp = dtp;
     a.init_state = init_state; a.y = y; a.final_state = final_state;
@@ -169,6 +204,16 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype,
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
+    a.chunks = nullptr;
+    a.seqs = nullptr;
+    if (varlen) {
+        ssd::ChunkEntry *chunks = (ssd::ChunkEntry *)(ws + wl.off_tab);
+        ssd::SeqEntry *seqs = (ssd::SeqEntry *)(ws + wl.off_tab + (size_t)slots * sizeof(ssd::ChunkEntry));
+        hipError_t e = ssd::launch_chunk_table(a, chunks, seqs, stream);
+        if (e != hipSuccess) return hip_status(e);
+        a.chunks = chunks;
+        a.seqs = seqs;
+    }
     hipError_t e = mfma ? ssd::launch_prefill_mfma(a, stream) : ssd::launch_prefill_vector(a, dtype, stream);
     return hip_status(e);
 }
@@ -236,8 +281,17 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
                         const void *Bm, const void *Cm, const float *D,
                         const float *init_state, void *y, float *final_state,
                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return prefill_impl(B, L, H, P, G, N, Q, dtype, x, dt, A_log, Bm, Cm, D, init_state, y, final_state,
+    return prefill_impl(B, L, H, P, G, N, Q, dtype, nullptr, x, dt, A_log, Bm, Cm, D, init_state, y, final_state,
                         workspace, workspace_bytes, stream, ssd::DtPrep{0, nullptr, 0.0f, 0.0f});
+}
+
+SSD_API int ssd_prefill_varlen(int B, int T, int H, int P, int G, int N, int Q, int dtype, const int *cu_seqlens,
+                               const void *x, const float *dt, const float *A_log,
+                               const void *Bm, const void *Cm, const float *D,
+                               const float *init_state, void *y, float *final_state,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return prefill_impl(B, T, H, P, G, N, Q, dtype, cu_seqlens, x, dt, A_log, Bm, Cm, D, init_state, y,
+                        final_state, workspace, workspace_bytes, stream, ssd::DtPrep{0, nullptr, 0.0f, 0.0f}, true);
 }
 
 SSD_API int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, int dtype,
@@ -246,8 +300,8 @@ SSD_API int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, 
                                const float *D, const float *init_state, void *y, float *final_state,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dt_prep(dt_min, dt_max, dt_bias)) return aligned(dt_bias, 4) ? SSD_ERR_INVALID_ARG : SSD_ERR_ALIGNMENT;
-    return prefill_impl(B, L, H, P, G, N, Q, dtype, x, dt_raw, A_log, Bm, Cm, D, init_state, y, final_state,
-                        workspace, workspace_bytes, stream, ssd::DtPrep{1, dt_bias, dt_min, dt_max});
+    return prefill_impl(B, L, H, P, G, N, Q, dtype, nullptr, x, dt_raw, A_log, Bm, Cm, D, init_state, y,
+                        final_state, workspace, workspace_bytes, stream, ssd::DtPrep{1, dt_bias, dt_min, dt_max});
 }
 
 SSD_API int ssd_decode_step(int B, int H, int P, int G, int N, int dtype,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssd_internal.hpp"
+
 namespace ssd {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
@@ -44,6 +46,27 @@ __device__ __forceinline__ float dt_softplus_clamp(float u, float lo, float hi) 
 __device__ __forceinline__ float dt_value(float v, int raw, const float *bias, int h, float lo, float hi) {
     if (!raw) return v;
     return dt_softplus_clamp(v + (bias ? bias[h] : 0.0f), lo, hi);
+}
+
+// ---------------------------------------------------------------- chunk slots
+// The chunk in slot f (see PrefillArgs): from the slot table for packed
+// sequences, by arithmetic for a uniform batch.
+__device__ __forceinline__ ChunkEntry chunk_at(const PrefillArgs &a, long f) {
+    if (a.chunks) return a.chunks[f];
+    ChunkEntry e;
+    e.seq = (int)(f / a.nchunks);
+    e.c = (int)(f - (long)e.seq * a.nchunks);
+    e.tok0 = e.seq * a.L + e.c * a.Q;
+    e.Qc = min(a.Q, a.L - e.c * a.Q);
+    return e;
+}
+// Slots of sequence b's chunks: [f0, f0 + n).
+__device__ __forceinline__ SeqEntry seq_chunks(const PrefillArgs &a, long b) {
+    if (a.seqs) return a.seqs[b];
+    SeqEntry e;
+    e.f0 = (int)(b * a.nchunks);
+    e.n = a.nchunks;
+    return e;
 }
 
 // ---------------------------------------------------------------- wave ops

@@ -19,8 +19,27 @@ struct DtPrep {
     float dt_min, dt_max;
 };
 
+// Chunks are addressed by a flat slot f.  Uniform batch [B, L]: f = b *
+// nchunks + c.  Packed sequences (cu_seqlens): nchunks slots in all (B = 1 in
+// the grids), described by the table that build_chunk_table writes into the
+// workspace; a slot past the last chunk has Qc = 0.
+struct ChunkEntry {
+    int seq;   // sequence (batch element)
+    int c;     // chunk within the sequence
+    int tok0;  // token row of the chunk's first token in x / y / dt / Bm / Cm
+    int Qc;    // tokens in the chunk (0: unused slot)
+};
+struct SeqEntry {
+    int f0;  // slot of the sequence's first chunk
+    int n;   // chunks of the sequence
+};
+
 struct PrefillArgs {
     int B, L, H, P, G, N, Q, nchunks;
+    int T;                    // token rows of x (B * L, or the packed total)
+    const int *cu_seqlens;    // packed sequences: [B + 1] token offsets; null: uniform
+    const ChunkEntry *chunks; // packed sequences: [nchunks] slot table
+    const SeqEntry *seqs;     // packed sequences: [B]
     const void *x;
     const float *dt, *A_log;
     DtPrep dtp;
@@ -39,11 +58,18 @@ struct PrefillArgs {
 };
 
 struct WorkspaceLayout {
-    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, total;
+    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, off_tab, total;
 };
+constexpr int kPrefillMaxQ = 1024;  // largest chunk (vector path; the MFMA path is Q = 256)
 long prefill_mfma_gt_elems_per_chunk();
 long prefill_mfma_bt_elems_per_chunk();
-WorkspaceLayout prefill_workspace_layout(int B, int L, int H, int P, int N, int Q, int G, bool mfma);
+// Workspace for `slots` chunk slots of H heads (and G groups), plus the slot
+// and sequence tables of packed sequences when nseq > 0.
+WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq);
+// Chunk slots of a packed prefill of T tokens in B sequences: an upper bound
+// of sum over sequences of ceil(L_b / Q).
+inline long varlen_slots(long T, int B, int Q) { return T / Q + B; }
+hipError_t launch_chunk_table(const PrefillArgs &a, ChunkEntry *chunks, SeqEntry *seqs, hipStream_t s);
 bool prefill_uses_mfma(int P, int N, int Q, int dtype);
 
 // Stage timing (profiling aid, per host thread).  stage_begin starts a new

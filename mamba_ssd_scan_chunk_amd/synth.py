@@ -15,6 +15,7 @@ Distributions (``N(mu, v)`` has variance ``v``):
     conv_w ~ N(0, 0.02),  raw conv inputs ~ N(0, 1)
     dt_raw ~ N(0, 1), dt_bias ~ U(ln 1e-3, ln 0.1)   (raw step-size projection)
     z ~ N(0, 1), norm_w ~ U(0.5, 1.5)   (gate branch and normalisation weight)
+    packed sequence lengths: log-uniform in [lo, hi]
 Variants: "spec" (as above), "d0" (D = 0, so the output is the SSM term
 alone), "slow" (A_log ~ U(-7, -4) and dt = 1e-3, so state survives across
 thousands of tokens and every chunk hand-off matters), "steep" (A_log ~
@@ -143,6 +144,24 @@ def make_gate(shape, D, dtype="f32", seed=0):
     z = _normal(rng, tuple(shape) + (D,))
     w = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
     return _store(z, dtype), torch.from_numpy(w)
+
+
+def make_lengths(nseq, lo, hi, seed=0):
+    """Sequence lengths for a packed (varlen) batch: log-uniform in [lo, hi]
+    (integers), the mix of prompt lengths a serving batch sees."""
+    rng = np.random.default_rng(seed)
+    return [int(v) for v in np.exp(rng.uniform(math.log(lo), math.log(hi), size=nseq)).round()]
+
+
+def make_varlen(lengths, H, P, G, N, dtype="f32", seed=0, variant="spec"):
+    """Inputs of a packed prefill: make_prefill of one sequence of sum(lengths)
+    tokens, with the batch axis dropped (x [T,H,P], dt [T,H], Bm/Cm [T,G,N]),
+    plus cu_seqlens [len(lengths) + 1] int32 (token offsets)."""
+    T = int(sum(lengths))
+    d = make_prefill(1, T, H, P, G, N, dtype, seed, variant)
+    out = {k: (v[0] if k in ("x", "dt", "Bm", "Cm") else v) for k, v in d.items()}
+    out["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    return out
 
 
 def make_state(B, H, P, N, seed=0, scale=1.0):

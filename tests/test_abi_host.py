@@ -82,7 +82,7 @@ def _prefill(lib, B=1, L=64, H=2, P=16, G=1, N=16, Q=32, dtype=0, **over):
     (dict(y=None), bd.SSD_ERR_INVALID_ARG),
     (dict(P=257), bd.SSD_ERR_UNSUPPORTED),
     (dict(N=512), bd.SSD_ERR_UNSUPPORTED),
-    (dict(Q=512), bd.SSD_ERR_UNSUPPORTED),
+    (dict(Q=1025), bd.SSD_ERR_UNSUPPORTED),
     (dict(x=_addr(0, 2)), bd.SSD_ERR_ALIGNMENT),
     (dict(y=_addr(7, 8)), bd.SSD_ERR_ALIGNMENT),
     (dict(final=_addr(8, 4)), bd.SSD_ERR_ALIGNMENT),
@@ -171,6 +171,40 @@ def _decode(lib, B=2, H=2, P=16, G=1, N=16, dtype=0, K=4, act=1, stride=0, **ove
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def _varlen(lib, B=3, T=500, H=2, P=64, G=1, N=128, Q=256, dtype=1, ws_bytes=1 << 40, **over):
+    p = dict(cu=_addr(13), x=_addr(0), dt=_addr(1), A_log=_addr(2), Bm=_addr(3), Cm=_addr(4), D=_addr(5),
+             init=_addr(6), y=_addr(7), final=_addr(8), ws=_addr(9))
+    p.update(over)
+    return lib.ssd_prefill_varlen(B, T, H, P, G, N, Q, dtype, p["cu"], p["x"], p["dt"], p["A_log"], p["Bm"],
+                                  p["Cm"], p["D"], p["init"], p["y"], p["final"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(cu=_addr(13, 2)), bd.SSD_ERR_ALIGNMENT),
+    (dict(y=_addr(13, 0)), bd.SSD_ERR_INVALID_ARG),      # y overlaps cu_seqlens
+    (dict(final=_addr(13, 0)), bd.SSD_ERR_INVALID_ARG),  # final_state overlaps cu_seqlens
+    (dict(ws=_addr(13, 0)), bd.SSD_ERR_INVALID_ARG),     # workspace overlaps cu_seqlens
+    (dict(T=-1), bd.SSD_ERR_INVALID_ARG),
+    (dict(B=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(G=3, H=4), bd.SSD_ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), bd.SSD_ERR_WORKSPACE),
+    (dict(ws=None), bd.SSD_ERR_WORKSPACE),
+    (dict(Q=2048), bd.SSD_ERR_UNSUPPORTED),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert _varlen(lib, **kw) == code
+
+
+def test_varlen_workspace_bytes(lib):
+    n = lib.ssd_prefill_varlen_workspace_bytes(3, 500, 2, 64, 1, 128, 256, 1)
+    # chunk slots: 500 / 256 + 3 = 4; the slot and sequence tables come last
+    per_slot = lib.ssd_prefill_workspace_bytes(1, 256, 2, 64, 1, 128, 256, 1)
+    assert abs(n - (4 * per_slot + 4 * 16 + 3 * 8)) <= 8 * 256  # up to 256-byte padding per region
+    assert lib.ssd_prefill_varlen_workspace_bytes(3, 0, 2, 64, 1, 128, 256, 1) == 0
+    assert lib.ssd_prefill_varlen_workspace_bytes(0, 10, 2, 64, 1, 128, 256, 1) == ctypes.c_size_t(-1).value
 
 
 def _decode_raw(lib, B=2, H=2, P=16, G=1, N=16, dtype=0, K=4, act=1, dt_min=0.0, dt_max=1.0, **over):

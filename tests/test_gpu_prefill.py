@@ -43,6 +43,12 @@ CASES = [
     ("f32-max-dims", 1, 300, 1, 256, 1, 256, 256, "f32"),
     ("bf16-max-dims", 1, 270, 1, 256, 1, 256, 256, "bf16"),
     ("f32-min-q", 1, 50, 2, 1, 1, 1, 16, "f32"),
+    # chunks longer than 256 tokens (vector path): Q = 512 as suggested for
+    # long contexts, up to the largest chunk, with ragged thread shares
+    ("bf16-q512", 1, 1300, 2, 64, 1, 128, 512, "bf16"),
+    ("f32-q1024", 1, 2200, 2, 16, 1, 16, 1024, "f32"),
+    ("f32-q384-groups", 2, 900, 4, 8, 2, 32, 384, "f32"),
+    ("f32-q1000-eq-l", 1, 1000, 1, 4, 1, 8, 1000, "f32"),
 ]
 
 
