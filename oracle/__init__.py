@@ -208,6 +208,24 @@ def conv_update(conv_state, xBC, w, bias=None, activation=False):
     return st, out
 
 
+def conv_update_varlen(conv_state, xBC, cu_seqlens, w, bias=None, activation=False):
+    """``conv_update`` per packed sequence: sequence b is rows cu_seqlens[b]
+    .. cu_seqlens[b+1] of xBC [T,C] and starts from conv_state[b] [C,K-1].
+    Returns (new_state [B,C,K-1], out [T,C]) as float64."""
+    st = _f64(conv_state)
+    xBC = _f64(xBC)
+    cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+    assert cu[0] == 0 and cu[-1] == xBC.shape[0] and all(a <= b for a, b in zip(cu, cu[1:]))
+    new = np.empty_like(st)
+    out = np.empty_like(xBC)
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        nb, ob = conv_update(st[b:b + 1], xBC[None, lo:hi], w, bias, activation)
+        new[b] = nb[0]
+        out[lo:hi] = ob[0]
+    return new, out
+
+
 def decode_step(x_t, dt_t, A_log, B_t, C_t, D, ssm_state, *, conv_state=None,
                 conv_w=None, conv_b=None, activation=False, nthreads=None):
     """One cached decode step: conv window step (optional), then one token of

@@ -519,3 +519,36 @@ def test_varlen_sequences_are_independent_and_empty_ones_keep_state(oracle):
                                                                                             packed["Bm"][t, 0])
         np.testing.assert_allclose(y[t, h], st @ packed["Cm"][t, 0] + packed["D"][h] * packed["x"][t, h],
                                    rtol=1e-13, atol=1e-13)
+
+
+def test_conv_varlen_equal_lengths_is_the_batched_conv(oracle):
+    B, L, C, K = 3, 9, 5, 4
+    rng = np.random.default_rng(80)
+    st = rng.standard_normal((B, C, K - 1))
+    x = rng.standard_normal((B, L, C))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    nb, ob = oracle.conv_update(st, x, w, bias, True)
+    nv, ov = oracle.conv_update_varlen(st, x.reshape(B * L, C), [0, L, 2 * L, 3 * L], w, bias, True)
+    np.testing.assert_array_equal(nv, nb)
+    np.testing.assert_array_equal(ov, ob.reshape(B * L, C))
+
+
+def test_conv_varlen_sequences_independent_and_empty_keeps_cache(oracle):
+    C, K = 4, 4
+    rng = np.random.default_rng(81)
+    cu = [0, 2, 2, 11]
+    st = rng.standard_normal((3, C, K - 1))
+    x = rng.standard_normal((11, C))
+    w = rng.standard_normal((C, K))
+    nv, ov = oracle.conv_update_varlen(st, x, cu, w)
+    np.testing.assert_array_equal(nv[1], st[1])                      # empty sequence
+    # sequence 0 has 2 < K-1 tokens: the new cache keeps its oldest cached tap
+    np.testing.assert_array_equal(nv[0][:, 0], st[0][:, 2])
+    np.testing.assert_array_equal(nv[0][:, 1:], x[0:2].T)
+    # sequence 2's first output sees its own cache, not sequence 0's tokens
+    np.testing.assert_allclose(ov[2], (w[:, :K - 1] * st[2]).sum(1) + w[:, K - 1] * x[2], rtol=1e-15)
+    x2 = x.copy()
+    x2[0:2] += 1.0
+    _, ov2 = oracle.conv_update_varlen(st, x2, cu, w)
+    np.testing.assert_array_equal(ov2[2:], ov[2:])
