@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -360,6 +361,23 @@ def bench_varlen(args):
 
     ms = _timed(step, args.steps, args.warmup, "varlen")
     del d, y, ws
+    # the depthwise conv over the same packed prompts (x | B | C channels)
+    C = w.conv_channels
+    xbc = synth.make_tokens(1, T, C, w.dtype, seed=12)[0].cuda()
+    cw, _ = synth.make_conv(C, w.K, w.dtype, seed=13)
+    cw = cw.cuda()
+    cst = torch.zeros((len(lengths), C, w.K - 1), dtype=xbc.dtype, device="cuda")
+    cu = torch.tensor([0] + list(itertools.accumulate(lengths)), dtype=torch.int32, device="cuda")
+    cout = torch.empty_like(xbc)
+    cws = torch.empty(max(1, bd.lib().conv_state_update_varlen_workspace_bytes(len(lengths), T)), dtype=torch.uint8,
+                      device="cuda")
+
+    def conv_step(_):
+        bd.conv_state_update_varlen(cst, xbc, cu, cw, activation=1, out=cout, workspace=cws)
+
+    cms = _timed(conv_step, args.steps, args.warmup, "varlen_conv")
+    cbytes = 2 * T * C * xbc.element_size()
+    del xbc, cout
     Lmax = max(lengths)
     p = {k: v.cuda() for k, v in synth.make_prefill(len(lengths), Lmax, w.H, w.P, w.G, w.N, w.dtype, seed=11).items()}
 
@@ -367,14 +385,15 @@ def bench_varlen(args):
         bd.ssd_prefill(p["x"], p["dt"], p["A_log"], p["Bm"], p["Cm"], p["D"], None, Q=w.Q, final_state=fs)
 
     pms = _timed(padded, max(5, args.steps // 5), 2, "varlen_padded")
-    return lengths, T, ms, Lmax, pms
+    return lengths, T, ms, Lmax, pms, cms, cbytes
 
 
 def varlen_record(args):
-    lengths, T, ms, Lmax, pms = bench_varlen(args)
+    lengths, T, ms, Lmax, pms, cms, cbytes = bench_varlen(args)
     return {"varlen": {"sequences": len(lengths), "tokens": T, "lengths": lengths, "us": round(ms * 1e3, 2),
                        "tokens_per_s": round(T / (ms * 1e-3), 1),
-                       "padded": {"batch": len(lengths), "seq_len": Lmax, "us": round(pms * 1e3, 2)}}}
+                       "padded": {"batch": len(lengths), "seq_len": Lmax, "us": round(pms * 1e3, 2)},
+                       "conv": {"us": round(cms * 1e3, 2), "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1)}}}
 
 
 def cpu_baseline(args):

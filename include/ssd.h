@@ -248,6 +248,30 @@ int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_state,
                       int activation, void *out, hipStream_t stream);
 
 /*
+ * conv_state_update_varlen -- conv_state_update over B sequences packed
+ * without padding, as ssd_prefill_varlen packs them: sequence b is the token
+ * rows [cu_seqlens[b], cu_seqlens[b + 1]) of xBC [T,C] and out [T,C], and its
+ * window starts from conv_state[b] ([B,C,K-1], updated in place to the
+ * sequence's last K-1 inputs; an empty sequence keeps its cache).
+ * Source: bqwf.cn article §2.1-§2.2, per sequence.
+ *
+ *   cu_seqlens [B+1] int32, DEVICE memory, contract as in ssd_prefill_varlen
+ *   workspace  conv_state_update_varlen_workspace_bytes(B, T) bytes, 256-byte
+ *              aligned (the block table the library builds on the device)
+ * Requirements beyond conv_state_update's: C a multiple of 16 bytes of
+ * elements (8 bf16, 4 fp32) else SSD_ERR_UNSUPPORTED; conv_state, xBC,
+ * conv_w, conv_b and out 16-byte aligned else SSD_ERR_ALIGNMENT.  T = 0 is a
+ * no-op.  out may be NULL (caches only).
+ */
+int conv_state_update_varlen(int B, int T, int C, int K, int dtype, const int *cu_seqlens, void *conv_state,
+                             const void *xBC, const void *conv_w, const void *conv_b, int activation, void *out,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace conv_state_update_varlen needs; (size_t)-1 if B < 1 or
+ * T < 0. */
+size_t conv_state_update_varlen_workspace_bytes(int B, int T);
+
+/*
  * ssd_gated_rmsnorm -- the normalisation that closes the layer, in the gated
  * RMS form of the Mamba-2 mixer (bqwf.cn article §3.2: normalisation fused
  * with its neighbours; §4.1: its variance in fp32 even for bf16 inputs).

@@ -36,6 +36,8 @@ SIGNATURES = {
     "ssd_decode_step": (_i, [_i] * 6 + [_p] * 8 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "ssd_decode_step_dt_raw": (_i, [_i] * 6 + [_p] * 3 + [_f, _f] + [_p] * 6 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "conv_state_update": (_i, [_i] * 5 + [_p] * 4 + [_i, _p, _p]),
+    "conv_state_update_varlen": (_i, [_i] * 5 + [_p] * 5 + [_i, _p, _p, _sz, _p]),
+    "conv_state_update_varlen_workspace_bytes": (_sz, [_i, _i]),
     "ssd_gated_rmsnorm": (_i, [_l, _i, _i, _i, _p, _p, _l, _p, _f, _p, _p]),
     "ssd_stage_timing": (_i, [_i]),
     "ssd_stage_times": (_i, [ctypes.POINTER(ctypes.c_float), _i, ctypes.POINTER(_i)]),
@@ -273,6 +275,31 @@ def ssd_gated_rmsnorm(y, z=None, norm_w=None, *, group, eps=1e-5, out=None, stre
     rc = lib().ssd_gated_rmsnorm(rows, D, int(group), _dtype_code(y), _ptr(y), _ptr(z), z_stride, _ptr(norm_w),
                                  float(eps), _ptr(out), _stream(stream))
     _check("ssd_gated_rmsnorm", rc)
+    return out
+
+
+def conv_state_update_varlen(conv_state, xBC, cu_seqlens, conv_w, conv_b=None, *, activation=0, out=None,
+                             want_out=True, workspace=None, stream=None):
+    """conv_state_update over packed sequences: xBC [T,C], cu_seqlens [B+1]
+    int32 on the GPU, conv_state [B,C,K-1] updated in place.  Returns out
+    [T,C] (or None)."""
+    for t, n in ((conv_state, "conv_state"), (xBC, "xBC"), (conv_w, "conv_w"), (conv_b, "conv_b"), (out, "out"),
+                 (cu_seqlens, "cu_seqlens")):
+        _dense(t, n)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    B, C, Km1 = conv_state.shape
+    T = xBC.shape[0]
+    code = _dtype_code(conv_state)
+    if out is None and want_out:
+        out = torch.empty_like(xBC)
+    nws = lib().conv_state_update_varlen_workspace_bytes(B, T)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=xBC.device)
+    rc = lib().conv_state_update_varlen(B, T, C, Km1 + 1, code, _ptr(cu_seqlens), _ptr(conv_state), _ptr(xBC),
+                                        _ptr(conv_w), _ptr(conv_b), int(activation), _ptr(out), _ptr(workspace),
+                                        0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("conv_state_update_varlen", rc)
     return out
 
 

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(PrefillArgs a,
         if (b < a.B) {
             const long long f0 = min(first, slots);
             const int cnt = (int)min(n, slots - f0);
-            seqs[b] = SeqEntry{(int)f0, cnt};
+            seqs[b] = SeqEntry{(int)f0, cnt, start, len};
             for (int c = 0; c < cnt; ++c)
                 chunks[f0 + c] = ChunkEntry{b, c, start + c * a.Q, min(a.Q, len - c * a.Q)};
         }

@@ -27,6 +27,7 @@ constexpr int kTBV = 8;  // tokens per thread, channel-group form
 // a token block other than the first reads its window from the tokens before
 // it, never from the cache that the first block rewrites
 static_assert(kTB >= kMaxK - 1 && kTBV >= kMaxK - 1, "token blocks must cover a window");
+static_assert(kTBV == kConvSlotTokens, "slot table of packed sequences");
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void conv_update_kernel(ConvArgs a) {
@@ -100,12 +101,29 @@ __global__ __launch_bounds__(kVThreads) void conv_update_vec(ConvArgs a) {
     using VT = Vec16<T>;
     constexpr int V = VT::V;
     const long ngrp = a.C / V;
-    const long grp = (long)blockIdx.x * kVThreads + threadIdx.x;
+    // grid (channel blocks, token blocks, B), or (slots, channel blocks) for
+    // packed sequences
+    const long grp = (long)(a.blocks ? blockIdx.y : blockIdx.x) * kVThreads + threadIdx.x;
     if (grp >= ngrp) return;
-    const int tb = blockIdx.y, b = blockIdx.z;
-    const int T_ = a.T;
+    // sequence b, its token block tb (tokens t0 .. t1 - 1 of the sequence),
+    // and the token row of the sequence's first token
+    int b, tb, t1;
+    long row0;
+    if (a.blocks) {
+        const ChunkEntry e = a.blocks[blockIdx.x];
+        if (e.Qc <= 0) return;  // unused slot
+        b = e.seq;
+        tb = e.c;
+        row0 = (long)e.tok0 - (long)e.c * kTBV;
+        t1 = e.c * kTBV + e.Qc;
+    } else {
+        b = blockIdx.z;
+        tb = blockIdx.y;
+        row0 = (long)b * a.T;
+        t1 = min(a.T, tb * kTBV + kTBV);
+    }
     const long C = a.C, c0 = grp * V;
-    const int t0 = tb * kTBV, t1 = min(T_, t0 + kTBV);
+    const int t0 = tb * kTBV;
     // tap k of channel c0 + i is element i * K + k of the V*K taps of the group
     float w[V][K];
     {
@@ -125,7 +143,7 @@ __global__ __launch_bounds__(kVThreads) void conv_update_vec(ConvArgs a) {
         for (int i = 0; i < V; ++i) bias[i] = 0.0f;
     }
     T *stp = (T *)a.state + ((long)b * C + c0) * (K - 1);  // V channels x (K-1), contiguous
-    const uint4 *xp = (const uint4 *)((const T *)a.xBC + (long)b * T_ * C + c0);  // token t at xp[t * C / V]
+    const uint4 *xp = (const uint4 *)((const T *)a.xBC + row0 * C + c0);  // token t at xp[t * C / V]
     const long xs = C / V;
     // win[j][i]: input j of the K-1 before token t0, channel c0 + i; old:
     // the old cache (token block 0 only)
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(kVThreads) void conv_update_vec(ConvArgs a) {
     uint4 raw[kTBV];
 #pragma unroll
     for (int t = 0; t < kTBV; ++t) raw[t] = t0 + t < t1 ? xp[(long)(t0 + t) * xs] : make_uint4(0, 0, 0, 0);
-    uint4 *op = a.out ? (uint4 *)((T *)a.out + (long)b * T_ * C + c0) : nullptr;
+    uint4 *op = a.out ? (uint4 *)((T *)a.out + row0 * C + c0) : nullptr;
 #pragma unroll
     for (int t = 0; t < kTBV; ++t) {
         if (t0 + t >= t1) break;
@@ -175,6 +193,7 @@ __global__ __launch_bounds__(kVThreads) void conv_update_vec(ConvArgs a) {
         // new cache = hist[T .. T+K-2] with hist = (old cache, tokens): the
         // last K-1 tokens, preceded by the end of the old cache (read by this
         // thread into `old` before it is overwritten) when T < K-1
+        const int T_ = a.blocks ? a.seqs[b].len : a.T;
         float nc[K - 1][V];
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) {
@@ -221,6 +240,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t launch_conv_update(const ConvArgs &a, int dtype, hipStream_t s) {
     if (a.T == 0 || a.B == 0) return hipSuccess;
+    if (a.blocks) {
+        // packed sequences: channel-group form only (checked by the caller)
+        const long gblocks = (a.C / (dtype == DT_BF16 ? 8 : 4) + kVThreads - 1) / kVThreads;
+        if (gblocks > 65535) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)a.nslots, (unsigned)gblocks, 1);
+        return dtype == DT_BF16 ? launch_vec<bf16_t>(a, grid, s) : launch_vec<float>(a, grid, s);
+    }
     if (a.B > 65535) return hipErrorInvalidConfiguration;
     const int V = dtype == DT_BF16 ? 8 : 4;
     const long vblocks = (a.T + kTBV - 1) / kTBV;

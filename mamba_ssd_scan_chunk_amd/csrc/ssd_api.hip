@@ -352,6 +352,60 @@ SSD_API int conv_state_update(int B, int T, int C, int K, int dtype, void *conv_
     ssd::ConvArgs a;
     a.B = B; a.T = T; a.C = C; a.K = K; a.activation = activation;
     a.state = conv_state; a.xBC = xBC; a.w = conv_w; a.bias = conv_b; a.out = out;
+    a.blocks = nullptr; a.seqs = nullptr; a.nslots = 0;
+    return hip_status(ssd::launch_conv_update(a, dtype, stream));
+}
+
+namespace {
+size_t conv_varlen_ws(int B, int T) {
+    const long slots = ssd::varlen_slots(T, B, ssd::kConvSlotTokens);
+    return T > 0 ? align_up((size_t)slots * sizeof(ssd::ChunkEntry) + (size_t)B * sizeof(ssd::SeqEntry), 256) : 0;
+}
+}  // namespace
+
+SSD_API size_t conv_state_update_varlen_workspace_bytes(int B, int T) {
+    if (B < 1 || T < 0) return (size_t)-1;
+    return conv_varlen_ws(B, T);
+}
+
+SSD_API int conv_state_update_varlen(int B, int T, int C, int K, int dtype, const int *cu_seqlens, void *conv_state,
+                                     const void *xBC, const void *conv_w, const void *conv_b, int activation,
+                                     void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSD_ERR_INVALID_ARG;
+    if (B < 1 || T < 0 || C < 1 || K < 2 || K > 8 || (activation != 0 && activation != 1)) return SSD_ERR_INVALID_ARG;
+    if (!cu_seqlens || !conv_state || !conv_w || (T > 0 && !xBC)) return SSD_ERR_INVALID_ARG;
+    const size_t es = esize(dtype);
+    const int V = (int)(16 / es);
+    if (C % V != 0 || (long)C / V > 65535L * 64) return SSD_ERR_UNSUPPORTED;
+    if (!aligned(cu_seqlens, 4) || !aligned(conv_state, 16) || !aligned(xBC, 16) || !aligned(conv_w, 16) ||
+        !aligned(conv_b, 16) || !aligned(out, 16) || !aligned(workspace, 256))
+        return SSD_ERR_ALIGNMENT;
+    const size_t b_state = (size_t)B * C * (K - 1) * es, b_x = (size_t)T * C * es;
+    const size_t b_w = (size_t)C * K * es, b_b = conv_b ? (size_t)C * es : 0, b_cu = (size_t)(B + 1) * 4;
+    const size_t b_ws = conv_varlen_ws(B, T);
+    struct R { const void *p; size_t n; };
+    const R ins[] = {{xBC, b_x}, {conv_w, b_w}, {conv_b, b_b}, {cu_seqlens, b_cu}};
+    for (const R &r : ins) {
+        if (overlap(conv_state, b_state, r.p, r.n) || overlap(out, b_x, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+        if (overlap(workspace, b_ws, r.p, r.n)) return SSD_ERR_INVALID_ARG;
+    }
+    if (overlap(out, b_x, conv_state, b_state) || overlap(workspace, b_ws, conv_state, b_state) ||
+        overlap(workspace, b_ws, out, b_x))
+        return SSD_ERR_INVALID_ARG;
+    if (T == 0) return SSD_OK;
+    if (!workspace || workspace_bytes < b_ws) return SSD_ERR_WORKSPACE;
+    // the slot table of kConvSlotTokens-token blocks, built on the device
+    ssd::PrefillArgs t{};
+    t.B = B; t.T = T; t.Q = ssd::kConvSlotTokens; t.cu_seqlens = cu_seqlens;
+    t.nchunks = (int)ssd::varlen_slots(T, B, ssd::kConvSlotTokens);
+    ssd::ChunkEntry *blocks = (ssd::ChunkEntry *)workspace;
+    ssd::SeqEntry *seqs = (ssd::SeqEntry *)((char *)workspace + (size_t)t.nchunks * sizeof(ssd::ChunkEntry));
+    hipError_t e = ssd::launch_chunk_table(t, blocks, seqs, stream);
+    if (e != hipSuccess) return hip_status(e);
+    ssd::ConvArgs a;
+    a.B = B; a.T = T; a.C = C; a.K = K; a.activation = activation;
+    a.state = conv_state; a.xBC = xBC; a.w = conv_w; a.bias = conv_b; a.out = out;
+    a.blocks = blocks; a.seqs = seqs; a.nslots = t.nchunks;
     return hip_status(ssd::launch_conv_update(a, dtype, stream));
 }
 

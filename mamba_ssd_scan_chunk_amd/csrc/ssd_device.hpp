@@ -66,6 +66,8 @@ __device__ __forceinline__ SeqEntry seq_chunks(const PrefillArgs &a, long b) {
     SeqEntry e;
     e.f0 = (int)(b * a.nchunks);
     e.n = a.nchunks;
+    e.tok0 = (int)(b * a.L);
+    e.len = a.L;
     return e;
 }
 

@@ -30,8 +30,10 @@ struct ChunkEntry {
     int Qc;    // tokens in the chunk (0: unused slot)
 };
 struct SeqEntry {
-    int f0;  // slot of the sequence's first chunk
-    int n;   // chunks of the sequence
+    int f0;    // slot of the sequence's first chunk
+    int n;     // chunks of the sequence
+    int tok0;  // token row of the sequence's first token
+    int len;   // tokens of the sequence
 };
 
 struct PrefillArgs {
@@ -117,7 +119,13 @@ struct ConvArgs {
     void *state;
     const void *xBC, *w, *bias;
     void *out;
+    // packed sequences (xBC and out [T, C], T the packed total): a slot table
+    // of kConvSlotTokens-token blocks; null for a uniform batch [B, T, C]
+    const ChunkEntry *blocks;
+    const SeqEntry *seqs;
+    int nslots;
 };
+constexpr int kConvSlotTokens = 8;  // tokens per thread of the channel-group conv kernel
 hipError_t launch_conv_update(const ConvArgs &a, int dtype, hipStream_t s);
 
 struct NormArgs {

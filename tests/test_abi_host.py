@@ -252,6 +252,38 @@ def test_conv_rejects(lib, kw, code):
     assert _conv(lib, **kw) == code
 
 
+def _conv_vl(lib, B=2, T=40, C=64, K=4, dtype=1, act=1, ws_bytes=1 << 30, **over):
+    p = dict(cu=_addr(5), state=_addr(0), x=_addr(1), w=_addr(2), b=_addr(3), out=_addr(4), ws=_addr(6))
+    p.update(over)
+    return lib.conv_state_update_varlen(B, T, C, K, dtype, p["cu"], p["state"], p["x"], p["w"], p["b"], act,
+                                        p["out"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(B=0), bd.SSD_ERR_INVALID_ARG),
+    (dict(K=9), bd.SSD_ERR_INVALID_ARG),
+    (dict(state=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(out=_addr(5, 0)), bd.SSD_ERR_INVALID_ARG),    # out overlaps cu_seqlens
+    (dict(ws=_addr(1, 256)), bd.SSD_ERR_INVALID_ARG),   # workspace overlaps xBC
+    (dict(C=60), bd.SSD_ERR_UNSUPPORTED),               # not a multiple of 8 bf16
+    (dict(x=_addr(1, 8)), bd.SSD_ERR_ALIGNMENT),
+    (dict(cu=_addr(5, 2)), bd.SSD_ERR_ALIGNMENT),
+    (dict(ws=_addr(6, 64)), bd.SSD_ERR_ALIGNMENT),
+    (dict(ws_bytes=16), bd.SSD_ERR_WORKSPACE),
+    (dict(ws=None), bd.SSD_ERR_WORKSPACE),
+])
+def test_conv_varlen_rejects(lib, kw, code):
+    assert _conv_vl(lib, **kw) == code
+
+
+def test_conv_varlen_workspace(lib):
+    assert _conv_vl(lib, T=0, x=None, ws=None) == bd.SSD_OK
+    assert lib.conv_state_update_varlen_workspace_bytes(2, 0) == 0
+    assert lib.conv_state_update_varlen_workspace_bytes(2, 40) >= (40 // 8 + 2) * 16 + 2 * 16
+    assert lib.conv_state_update_varlen_workspace_bytes(0, 40) == ctypes.c_size_t(-1).value
+
+
 def test_conv_zero_tokens_is_a_no_op(lib):
     assert _conv(lib, T=0, x=None) == bd.SSD_OK
 

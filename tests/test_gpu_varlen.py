@@ -123,3 +123,82 @@ def test_varlen_serving_mix_sampled(oracle):
         y_ref, fs_ref = oracle.ssd_scan(**sub)
         assert rel_err(y[lo:hi, h:h + 1], y_ref[0]) <= TOL_BF16, (b, h)
         assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [2, 4, 8])
+@pytest.mark.parametrize("mix", list(MIXES))
+def test_conv_varlen_matches_oracle(oracle, dtype, K, mix):
+    """Depthwise conv over packed sequences: outputs and per-sequence caches
+    (sequences shorter than K-1 keep part of their old cache; empty ones keep
+    all of it)."""
+    lengths = MIXES[mix] + [2]
+    C = 96
+    x = synth.make_tokens(1, sum(lengths), C, dtype, seed=720 + K)[0]
+    w, bias = synth.make_conv(C, K, dtype, seed=721, with_bias=True)
+    st = synth.make_tokens(len(lengths), K - 1, C, dtype, seed=722).transpose(1, 2).contiguous()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    stg = st.cuda()
+    announce("conv varlen", dtype, K, mix)
+    out = bd.conv_state_update_varlen(stg, x.cuda(), cu.cuda(), w.cuda(), bias.cuda(), activation=1)
+    torch.cuda.synchronize()
+    new_ref, out_ref = oracle.conv_update_varlen(st, x, cu, w, bias, True)
+    np.testing.assert_array_equal(stg.cpu().double().numpy(), new_ref)   # raw values, shifted exactly
+    assert rel_err(out, out_ref) <= (1e-6 if dtype == "f32" else 8e-3)
+
+
+def test_conv_varlen_equal_lengths_bitwise_equals_batched():
+    B, L, C, K = 3, 70, 5376, 4
+    x = synth.make_tokens(B, L, C, "bf16", seed=723)
+    w, _ = synth.make_conv(C, K, "bf16", seed=724)
+    st = synth.make_tokens(B, K - 1, C, "bf16", seed=725).transpose(1, 2).contiguous()
+    s1, s2 = st.cuda(), st.cuda()
+    announce("conv varlen equal lengths")
+    o1 = bd.conv_state_update(s1, x.cuda(), w.cuda(), activation=1)
+    cu = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device="cuda")
+    o2 = bd.conv_state_update_varlen(s2, x.reshape(B * L, C).cuda(), cu, w.cuda(), activation=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1.reshape(B * L, C))
+    assert torch.equal(s2, s1)
+
+
+def test_packed_prompts_then_decode(oracle):
+    """Serving path on packed prompts: conv and SSD prefill over the packed
+    batch, then one cached decode step per sequence from the caches they
+    left, against the oracle's per-sequence run over prompt + 1 tokens."""
+    H, P, G, N, K = 4, 64, 1, 128, 4
+    lengths = [300, 1, 0, 513]
+    C = H * P + 2 * G * N
+    T = sum(lengths)
+    xbc = synth.make_tokens(1, T + len(lengths), C, "bf16", seed=730)[0]
+    prompt, step_tok = xbc[:T], xbc[T:]
+    dts = synth.make_decode_stream(1, len(lengths), H, P, G, N, "bf16", seed=731)[1][0]
+    d = synth.make_varlen(lengths, H, P, G, N, "bf16", seed=732)
+    w, bias = synth.make_conv(C, K, "bf16", seed=733, with_bias=True)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    conv0 = torch.zeros((len(lengths), C, K - 1), dtype=torch.bfloat16)
+    announce("packed prompts then decode")
+    cst = conv0.cuda()
+    xc = bd.conv_state_update_varlen(cst, prompt.cuda(), cu.cuda(), w.cuda(), bias.cuda(), activation=1)
+    x_p = xc[:, :H * P].reshape(T, H, P).contiguous()
+    B_p = xc[:, H * P:H * P + G * N].reshape(T, G, N).contiguous()
+    C_p = xc[:, H * P + G * N:].reshape(T, G, N).contiguous()
+    dd = dev(d)
+    _, state = bd.ssd_prefill_varlen(x_p, dd["dt"], dd["A_log"], B_p, C_p, dd["D"], cu.cuda(), Q=256)
+    row = step_tok.cuda()
+    cout = torch.empty_like(cst)
+    y = bd.ssd_decode_step(row[:, :H * P], dts.cuda(), dd["A_log"], row[:, H * P:H * P + G * N],
+                           row[:, H * P + G * N:], dd["D"], state, in_stride=C, G=G, conv_state_in=cst,
+                           conv_state_out=cout, conv_w=w.cuda(), conv_b=bias.cuda(), K=K, activation=1)
+    torch.cuda.synchronize()
+    # oracle: per sequence, conv over the prompt then the scan, then one step
+    new_c, xc_ref = oracle.conv_update_varlen(conv0, prompt, cu, w, bias, True)
+    _, st_ref = oracle.ssd_scan_varlen(xc_ref[:, :H * P].reshape(T, H, P), d["dt"], d["A_log"],
+                                       xc_ref[:, H * P:H * P + G * N].reshape(T, G, N),
+                                       xc_ref[:, H * P + G * N:].reshape(T, G, N), cu, d["D"])
+    r = step_tok
+    y_ref, st2, _ = oracle.decode_step(r[:, :H * P], dts, d["A_log"], r[:, H * P:H * P + G * N],
+                                       r[:, H * P + G * N:], d["D"], st_ref, conv_state=new_c, conv_w=w,
+                                       conv_b=bias, activation=True)
+    assert rel_err(y, y_ref) <= TOL_BF16
+    assert rel_err(state, st2) <= TOL_BF16
