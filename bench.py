@@ -396,6 +396,62 @@ def varlen_record(args):
                        "conv": {"us": round(cms * 1e3, 2), "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1)}}}
 
 
+def bench_other_prefills(args):
+    """The other prefill workloads: the 130M-shaped layer (B=1, L=4096, H=24)
+    and the batched long-context prefill (B=8, L=16384, H=80) followed by its
+    cached decode steps (B=8, in a HIP graph of 256 steps)."""
+    import torch
+
+    from mamba_ssd_scan_chunk_amd import binding as bd
+    from mamba_ssd_scan_chunk_amd import synth
+
+    out = {}
+    for name in ("mamba2-130m-prefill", "mamba2-2.7b-longctx"):
+        if name == args.workload:
+            continue
+        w = synth.WORKLOADS[name]
+        d = {k: v.cuda() for k, v in synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, w.dtype, seed=14).items()}
+        y = torch.empty_like(d["x"])
+        fs = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, bd.ssd_prefill_workspace_bytes(w.B, w.L, w.H, w.P, w.G, w.N, w.Q, bd.SSD_BF16)),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(_):
+            bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], None, Q=w.Q, y=y,
+                           final_state=fs, workspace=ws)
+
+        steps = max(3, args.steps // (8 if w.B * w.L > 65536 else 1))
+        ms = _timed(step, steps, min(args.warmup, 3), name)
+        flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
+        rec = {"batch": w.B, "seq_len": w.L, "heads": w.H, "us": round(ms * 1e3, 2),
+               "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+               "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if w.decode_steps:
+            del d, y, ws
+            xbc, dts = synth.make_decode_stream(256, w.B, w.H, w.P, w.G, w.N, w.dtype, seed=15)
+            xbc, dts = xbc.cuda(), dts.cuda()
+            C, K = w.conv_channels, w.K
+            cw, _ = synth.make_conv(C, K, w.dtype, seed=16)
+            cw = cw.cuda()
+            conv = [torch.zeros((w.B, C, K - 1), dtype=xbc.dtype, device="cuda") for _ in range(2)]
+            yd = torch.empty((w.B, w.H, w.P), dtype=xbc.dtype, device="cuda")
+            A_log, Dv = synth.make_prefill(1, 1, w.H, w.P, w.G, w.N, w.dtype, seed=14)["A_log"].cuda(), None
+            HP, GN = w.H * w.P, w.G * w.N
+
+            def dstep(i):
+                row = xbc[i]
+                bd.ssd_decode_step(row[:, :HP], dts[i], A_log, row[:, HP:HP + GN], row[:, HP + GN:], Dv, fs,
+                                   y_t=yd, in_stride=C, G=w.G, conv_state_in=conv[i & 1],
+                                   conv_state_out=conv[(i + 1) & 1], conv_w=cw, K=K, activation=1)
+
+            gms = _graph_timed(dstep, 256)
+            dbytes = decode_bytes(w.B, w.H, w.P, w.G, w.N, K, 2)
+            rec["decode"] = {"steps": 256, "graph_us_per_step": round(gms * 1e3, 3),
+                             "gbs": round(dbytes / (gms * 1e-3) / 1e9, 1)}
+        out[name] = rec
+    return {"other_workloads": out}
+
+
 def cpu_baseline(args):
     import oracle
     from mamba_ssd_scan_chunk_amd import synth
@@ -427,8 +483,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip every leg but the prefill")
-    ap.add_argument("--legs", default="prefill,decode,conv,norm,varlen",
-                    help="comma-separated subset of prefill,decode,conv,norm,varlen,copy (for profiling runs)")
+    ap.add_argument("--legs", default="prefill,decode,conv,norm,varlen,other",
+                    help="comma-separated subset of prefill,decode,conv,norm,varlen,other,copy (for profiling runs)")
     ap.add_argument("--no-decode-extras", action="store_true",
                     help="decode leg: only the stated workload's one-state and rotated-state runs (no other batch, "
                          "raw-step or recompute legs), so that every decode dispatch has the same size")
@@ -461,6 +517,8 @@ def main():
         out.update(norm_record(args))
     if "varlen" in legs:
         out.update(varlen_record(args))
+    if "other" in legs:
+        out.update(bench_other_prefills(args))
     if "copy" in legs:
         out.update(copy_record(args))
     if HOST_BOUND:
