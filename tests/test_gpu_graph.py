@@ -105,3 +105,64 @@ def test_prefill_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), rep
         assert torch.equal(fs, fs_ref), rep
+
+
+def _capture(call):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    return g
+
+
+def test_packed_serving_graph_replays_match_eager():
+    """conv over packed prompts, the packed prefill (its chunk tables built on
+    the device inside the graph) and the gated normalisation of its output,
+    captured as one graph: every replay equals the eager result."""
+    H, P, G, N, K = 4, 64, 1, 128, 4
+    lengths = [300, 0, 1, 513, 40]
+    T, C = sum(lengths), H * P + 2 * G * N
+    d = {k: v.cuda() for k, v in synth.make_varlen(lengths, H, P, G, N, "bf16", seed=76).items()}
+    xbc = synth.make_tokens(1, T, C, "bf16", seed=77)[0].cuda()
+    cw, cb = (t.cuda() for t in synth.make_conv(C, K, "bf16", seed=78, with_bias=True))
+    z, nw = (t.cuda() for t in synth.make_gate((T,), H * P, "bf16", seed=79))
+    cst0 = synth.make_tokens(len(lengths), K - 1, C, "bf16", seed=80).transpose(1, 2).contiguous().cuda()
+    cu = d["cu_seqlens"]
+    B = len(lengths)
+    cws = torch.empty(bd.lib().conv_state_update_varlen_workspace_bytes(B, T), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(bd.lib().ssd_prefill_varlen_workspace_bytes(B, T, H, P, G, N, 256, bd.SSD_BF16),
+                      dtype=torch.uint8, device="cuda")
+    cst, xc = cst0.clone(), torch.empty_like(xbc)
+    y = torch.empty((T, H, P), dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty((B, H, P, N), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H * P), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        bd.conv_state_update_varlen(cst, xbc, cu, cw, cb, activation=1, out=xc, workspace=cws)
+        bd.ssd_prefill_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], cu, Q=256, y=y,
+                              final_state=fs, workspace=pws)
+        bd.ssd_gated_rmsnorm(y.reshape(T, H * P), z, nw, group=H * P, out=out)
+
+    announce("graph packed serving")
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (cst, xc, y, fs, out)]
+    g = _capture(call)
+    for rep in range(3):
+        cst.copy_(cst0)
+        for t in (xc, y, fs, out):
+            t.zero_()
+        cws.fill_(0xCD)
+        pws.fill_(0xAB)
+        # unrelated eager work on the same library between replays
+        bd.ssd_gated_rmsnorm(torch.ones((3, 512), dtype=torch.bfloat16, device="cuda"), group=512)
+        torch.cuda.synchronize()
+        cst.copy_(cst0)
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((cst, xc, y, fs, out), ref):
+            assert torch.equal(got, want), rep
