@@ -491,7 +491,7 @@ def main():
     ap.add_argument("--stage-runs", type=int, default=20, help="timed calls for the per-kernel durations")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; the scan "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark measures one GPU; the scan "
               "shards over (batch, head) with no communication, so N GPUs run N independent copies",
               file=sys.stderr)
         return 2

@@ -61,7 +61,7 @@ enum {
 enum {
     SSD_OK = 0,
     SSD_ERR_INVALID_ARG = -1, /* null required pointer, bad dimension, G not dividing H, K < 2, aliasing */
-    SSD_ERR_UNSUPPORTED = -2, /* shape / dtype combination this build has no kernel for */
+    SSD_ERR_UNSUPPORTED = -2, /* shape / dtype combination the library has no kernel for */
     SSD_ERR_ALIGNMENT = -3,   /* a pointer or row stride breaks the documented alignment */
     SSD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query returned */
     SSD_ERR_HIP = -5,         /* a HIP call failed; see ssd_last_hip_error() */

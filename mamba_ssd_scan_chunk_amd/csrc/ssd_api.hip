@@ -496,7 +496,7 @@ SSD_API const char *ssd_status_string(int status) {
     switch (status) {
         case SSD_OK: return "success";
         case SSD_ERR_INVALID_ARG: return "invalid argument (null pointer, bad dimension, G not dividing H, bad K or overlapping buffers)";
-        case SSD_ERR_UNSUPPORTED: return "unsupported shape or dtype for this build";
+        case SSD_ERR_UNSUPPORTED: return "unsupported shape or dtype (no kernel in this library)";
         case SSD_ERR_ALIGNMENT: return "pointer or stride breaks the required alignment";
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_HIP: return "HIP call failed (see ssd_last_hip_error)";
