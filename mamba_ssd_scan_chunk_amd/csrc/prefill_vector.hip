@@ -20,8 +20,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTpt = 4;                    // chunk tokens per thread in the chunk-state kernel
+constexpr int kSP = 64, kSN = 128, kST = 16;  // chunk-state output pass (16 x 16 threads of 4 x 8) and token step
 constexpr int kMaxQ = kThreads * kTpt;     // largest chunk this path takes
+constexpr int LT = 16;    // rows per workgroup of the C B^T kernel
+constexpr int LTO = 64;   // output rows per workgroup of the output kernel
+constexpr int ST = 16;    // source tokens per step of the output kernel
+constexpr int MAXD = 256;  // largest P and N
 static_assert(kMaxQ == kPrefillMaxQ, "chunk limit of the vector path");
+static_assert(LTO * 4 == kThreads && (LTO * ST) % kThreads == 0 && 4 * 64 == MAXD,
+              "output kernel: 16 threads per four output rows, 64 features per pass");
 
 __device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
     const int lane = threadIdx.x & 63;
@@ -42,6 +49,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_vec(PrefillArgs a) {
     __shared__ double wsum[kThreads / 64];
     __shared__ float wgt[kMaxQ];
     __shared__ double cs_last_sh;
+    __shared__ __attribute__((aligned(16))) float xs[kST][kSP];
+    __shared__ __attribute__((aligned(16))) float bs[kST][kSN];
     const int h = blockIdx.y;
     const long f = (long)blockIdx.z * a.nchunks + blockIdx.x;
     const ChunkEntry ch = chunk_at(a, f);
@@ -93,125 +102,279 @@ __global__ __launch_bounds__(kThreads) void chunk_state_vec(PrefillArgs a) {
     if (tid == 0) a.ws_dec[hc] = expm1f((float)cs_last);
     __syncthreads();
 
+    // S[p][n] = sum_s wgt_s x_s[p] B_s[n], in passes of kSP x kSN outputs:
+    // thread (tp, tn) accumulates a 4 x 8 tile; kST tokens of x' = wgt x and
+    // of B are staged in LDS per step.
     const int P = a.P, N = a.N;
     const long HP = (long)a.H * P, GN = (long)a.G * N;
     const T *xp = (const T *)a.x + (tok0 * a.H + h) * P;
     const T *Bp = (const T *)a.Bm + (tok0 * a.G + g) * N;
     float *Sp = a.ws_S + hc * P * N;
-    for (int o = tid; o < P * N; o += kThreads) {
-        const int p = o / N, n = o - (o / N) * N;
-        float acc = 0.0f;
-        for (int s = 0; s < Qc; ++s)
-            acc = fmaf(wgt[s] * ld(xp + s * HP + p), ld(Bp + s * GN + n), acc);
-        Sp[o] = acc;
+    const int tp = tid >> 4, tn = tid & 15;
+    for (int p0 = 0; p0 < P; p0 += kSP) {
+        for (int n0 = 0; n0 < N; n0 += kSN) {
+            float acc[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+            for (int s0 = 0; s0 < Qc; s0 += kST) {
+                __syncthreads();  // the previous step's tiles are consumed
+                for (int i = tid; i < kST * kSP; i += kThreads) {
+                    const int r = i / kSP, c = i - r * kSP, sx = s0 + r, px = p0 + c;
+                    xs[r][c] = (sx < Qc && px < P) ? wgt[sx] * ld(xp + sx * HP + px) : 0.0f;
+                }
+                for (int i = tid; i < kST * kSN; i += kThreads) {
+                    const int r = i / kSN, c = i - r * kSN, sx = s0 + r, nx = n0 + c;
+                    bs[r][c] = (sx < Qc && nx < N) ? ld(Bp + sx * GN + nx) : 0.0f;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < kST; ++r) {
+                    const float4 av = *(const float4 *)&xs[r][4 * tp];
+                    const float4 b0 = *(const float4 *)&bs[r][8 * tn];
+                    const float4 b1 = *(const float4 *)&bs[r][8 * tn + 4];
+                    const float xa[4] = {av.x, av.y, av.z, av.w};
+                    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xa[i], bb[j], acc[i][j]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pp = p0 + 4 * tp + i;
+                if (pp >= P) continue;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int nn = n0 + 8 * tn + j;
+                    if (nn < N) Sp[(long)pp * N + nn] = acc[i][j];
+                }
+            }
+        }
     }
 }
 
-constexpr int LT = 16;   // output rows per workgroup
-constexpr int ST = 16;   // source tokens per step
-constexpr int MAXD = 256;
-
-// Grid (nchunks * ceil(Q/LT), H, B).  Reads the carried-in state h_{c-1}
-// that the state pass left in ws_S.
+// Grid (nchunks * ceil(Q/LT), G, B).  The causal masked product of the
+// chunk, G[l][s] = C_l . B_s for s <= l (0 above the diagonal), once per
+// (chunk, group) for every head of the group: rows l0 .. l0+LT-1, all
+// columns s <= l0+LT-1, in LT x LT tiles (one element per thread).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void chunk_cb_vec(PrefillArgs a) {
     __shared__ float Cl[LT][MAXD + 1];
-    __shared__ float Bs[ST][MAXD + 1];
-    __shared__ float Xs[ST][MAXD + 1];
-    __shared__ float Gt[LT][ST + 1];
-    __shared__ double csl[LT], css[ST];
-    __shared__ float dts[ST];
-
+    __shared__ float Bt[LT][MAXD + 1];
     const int nlt = (a.Q + LT - 1) / LT;
+    const int c = blockIdx.x / nlt, lt = blockIdx.x - (blockIdx.x / nlt) * nlt;
+    const int g = blockIdx.y;
+    const long f = (long)blockIdx.z * a.nchunks + c;
+    const ChunkEntry ch = chunk_at(a, f);
+    const int Qc = ch.Qc;
+    const int l0 = lt * LT;
+    if (l0 >= Qc) return;
+    const int N = a.N;
+    const long GN = (long)a.G * N;
+    const long tok0 = ch.tok0;
+    const T *Bp = (const T *)a.Bm + (tok0 * a.G + g) * N;
+    const T *Cp = (const T *)a.Cm + (tok0 * a.G + g) * N;
+    float *Gp = a.ws_cb + (f * a.G + g) * a.Q * a.Q;
+    const int tid = threadIdx.x, i = tid / LT, j = tid - (tid / LT) * LT;
+    for (int e = tid; e < LT * N; e += kThreads) {
+        const int r = e / N, n = e - r * N;
+        Cl[r][n] = l0 + r < Qc ? ld(Cp + (l0 + r) * GN + n) : 0.0f;
+    }
+    for (int s0 = 0; s0 <= l0; s0 += LT) {
+        __syncthreads();
+        for (int e = tid; e < LT * N; e += kThreads) {
+            const int r = e / N, n = e - r * N;
+            Bt[r][n] = s0 + r < Qc ? ld(Bp + (s0 + r) * GN + n) : 0.0f;
+        }
+        __syncthreads();
+        float d = 0.0f;
+        if (l0 + i >= s0 + j) {
+            for (int n = 0; n < N; ++n) d = fmaf(Cl[i][n], Bt[j][n], d);
+        }
+        if (l0 + i < Qc && s0 + j < Qc) Gp[(long)(l0 + i) * a.Q + s0 + j] = d;
+    }
+}
+
+
+// Grid (nchunks * ceil(Q/LTO), H, B).  Reads the masked C B^T of the chunk
+// and group (chunk_cb_vec) and the carried-in state h_{c-1} that the state
+// pass left in ws_S.  A workgroup forms LTO output rows; thread (i, q) owns
+// rows l0 + 4i .. 4i+3 and the features 4q + 64m .. +3 (m < MQ): per source
+// token four LDS reads of G' and one 16-byte read of x per m feed 16 FMAs per m.
+template <typename T, int MQ>
+__global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) float Xs[ST][MAXD];
+    __shared__ __attribute__((aligned(16))) float Hs[ST][MAXD];
+    __shared__ float Gt[LTO][ST + 1];
+    __shared__ float Cl[LTO][ST + 1];
+    __shared__ double css[kMaxQ];  // cumsum of the chunk's sources s < l0 + LTO
+    __shared__ float dts[kMaxQ];   // their steps
+
+    const int nlt = (a.Q + LTO - 1) / LTO;
     const int c = blockIdx.x / nlt, lt = blockIdx.x - (blockIdx.x / nlt) * nlt;
     const int h = blockIdx.y;
     const long f = (long)blockIdx.z * a.nchunks + c;
     const ChunkEntry ch = chunk_at(a, f);
     const int Qc = ch.Qc;
     const long tok0 = ch.tok0;
-    const int l0 = lt * LT;
+    const int l0 = lt * LTO;
     if (l0 >= Qc) return;
-    const int lrows = min(LT, Qc - l0);
+    const int lrows = min(LTO, Qc - l0);
     const int g = h / (a.H / a.G);
     const int P = a.P, N = a.N;
     const long HP = (long)a.H * P, GN = (long)a.G * N;
     const int tid = threadIdx.x;
+    const int oi = tid >> 4, oq = tid & 15;  // output row quad, feature quad within 64
     const long hc = f * a.H + h;
     const double *cs = a.ws_cs + hc * a.Q;
     const T *xp = (const T *)a.x + (tok0 * a.H + h) * P;
-    const T *Bp = (const T *)a.Bm + (tok0 * a.G + g) * N;
     const T *Cp = (const T *)a.Cm + (tok0 * a.G + g) * N;
+    const float *Gp = a.ws_cb + (f * a.G + g) * a.Q * a.Q;
 
-    for (int i = tid; i < LT * N; i += kThreads) {
-        const int r = i / N, n = i - (i / N) * N;
-        Cl[r][n] = r < lrows ? ld(Cp + (l0 + r) * GN + n) : 0.0f;
-    }
-    if (tid < LT) csl[tid] = tid < lrows ? cs[l0 + tid] : 0.0;
-
-    float acc[16];
+    float acc[4][MQ][4];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m = 0; m < MQ; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[r][m][e] = 0.0f;
 
     const int send = l0 + lrows;  // sources s < send
-    for (int s0 = 0; s0 < send; s0 += ST) {
-        const int srows = min(ST, send - s0);
-        __syncthreads();
-        for (int i = tid; i < ST * N; i += kThreads) {
-            const int r = i / N, n = i - (i / N) * N;
-            Bs[r][n] = r < srows ? ld(Bp + (s0 + r) * GN + n) : 0.0f;
-        }
-        for (int i = tid; i < ST * P; i += kThreads) {
-            const int r = i / P, p = i - (i / P) * P;
-            Xs[r][p] = r < srows ? ld(xp + (s0 + r) * HP + p) : 0.0f;
-        }
-        if (tid < ST) {
-            css[tid] = tid < srows ? cs[s0 + tid] : 0.0;
-            dts[tid] = tid < srows ? dt_value(a.dt[(tok0 + s0 + tid) * a.H + h], a.dtp.dt_raw,
-                                              a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max)
-                                   : 0.0f;
-        }
-        __syncthreads();
-        {
-            const int i = tid / ST, j = tid - (tid / ST) * ST;
-            float gv = 0.0f;
-            if (i < lrows && j < srows && l0 + i >= s0 + j) {
-                float d = 0.0f;
-                for (int n = 0; n < N; ++n) d = fmaf(Cl[i][n], Bs[j][n], d);
-                gv = d * expf((float)(csl[i] - css[j])) * dts[j];
-            }
-            Gt[i][j] = gv;
-        }
-        __syncthreads();
+    for (int sx = tid; sx < send; sx += kThreads) {
+        css[sx] = cs[sx];
+        dts[sx] = dt_value(a.dt[(tok0 + sx) * a.H + h], a.dtp.dt_raw, a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max);
+    }
+    // G' = G * exp(cs_l - cs_s) * dt_s of a LTO x ST tile (four elements per
+    // thread) and its x rows (up to XPT elements per thread), into registers;
+    // the next tile's are loaded while the current one is consumed
+    constexpr int GPT = LTO * ST / kThreads, XPT = ST * MAXD / kThreads;
+    float gnext[GPT], xnext[XPT];
+    auto load_tile = [&](int s0) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int o = tid + k * kThreads;
-            if (o < LT * P) {
-                const int i = o / P, p = o - (o / P) * P;
-                float sacc = acc[k];
-                for (int j = 0; j < srows; ++j) sacc = fmaf(Gt[i][j], Xs[j][p], sacc);
-                acc[k] = sacc;
+        for (int k = 0; k < GPT; ++k) {
+            const int e = tid + k * kThreads;
+            const int gi = e / ST, gj = e - (e / ST) * ST, sx = s0 + gj;
+            gnext[k] = (gi < lrows && sx < send && l0 + gi >= sx)
+                           ? Gp[(long)(l0 + gi) * a.Q + sx] * expf((float)(css[l0 + gi] - css[sx])) * dts[sx]
+                           : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int e = tid + k * kThreads;
+            const int r = e / P, p = e - (e / P) * P;
+            xnext[k] = (e < ST * P && s0 + r < send) ? ld(xp + (s0 + r) * HP + p) : 0.0f;
+        }
+    };
+    __syncthreads();  // css, dts
+    load_tile(0);
+    for (int s0 = 0; s0 < send; s0 += ST) {
+        __syncthreads();  // the previous tile is consumed
+#pragma unroll
+        for (int k = 0; k < GPT; ++k) {
+            const int e = tid + k * kThreads;
+            Gt[e / ST][e - (e / ST) * ST] = gnext[k];
+        }
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int e = tid + k * kThreads;
+            if (e < ST * P) Xs[e / P][e - (e / P) * P] = xnext[k];
+        }
+        __syncthreads();
+        if (s0 + ST < send) load_tile(s0 + ST);
+        const int srows = min(ST, send - s0);
+        for (int j = 0; j < srows; ++j) {
+            float gg[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gg[r] = Gt[4 * oi + r][j];
+#pragma unroll
+            for (int m = 0; m < MQ; ++m) {
+                const float4 x4 = *(const float4 *)&Xs[j][64 * m + 4 * oq];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[r][m][0] = fmaf(gg[r], x4.x, acc[r][m][0]);
+                    acc[r][m][1] = fmaf(gg[r], x4.y, acc[r][m][1]);
+                    acc[r][m][2] = fmaf(gg[r], x4.z, acc[r][m][2]);
+                    acc[r][m][3] = fmaf(gg[r], x4.w, acc[r][m][3]);
+                }
             }
         }
     }
 
+    // carried-in state: off = C_l . h[p], ST columns of n at a time
     const float *hin = a.ws_S + hc * P * N;
-    const float Dh = a.D ? a.D[h] : 0.0f;
-    T *yp = (T *)a.y + (tok0 * a.H + h) * P;
+    float off[4][MQ][4];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int o = tid + k * kThreads;
-        if (o < LT * P) {
-            const int i = o / P, p = o - (o / P) * P;
-            if (i < lrows) {
-                float off = 0.0f;
-                const float *hr = hin + (long)p * N;
-                for (int n = 0; n < N; ++n) off = fmaf(Cl[i][n], hr[n], off);
-                const float xv = ld(xp + (l0 + i) * HP + p);
-                const float yv = acc[k] + expf((float)csl[i]) * off + Dh * xv;
-                st(yp + (l0 + i) * HP + p, yv);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m = 0; m < MQ; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) off[r][m][e] = 0.0f;
+    for (int n0 = 0; n0 < N; n0 += ST) {
+        const int ncols = min(ST, N - n0);
+        __syncthreads();
+        for (int e = tid; e < ST * P; e += kThreads) {  // Hs[nn][p] = h[p][n0 + nn]
+            const int p = e / ST, nn = e - (e / ST) * ST;
+            Hs[nn][p] = nn < ncols ? hin[(long)p * N + n0 + nn] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < LTO * ST / kThreads; ++k) {
+            const int e = tid + k * kThreads;
+            const int r = e / ST, nn = e - (e / ST) * ST;
+            Cl[r][nn] = (r < lrows && nn < ncols) ? ld(Cp + (l0 + r) * GN + n0 + nn) : 0.0f;
+        }
+        __syncthreads();
+        for (int nn = 0; nn < ncols; ++nn) {
+            float cv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cv[r] = Cl[4 * oi + r][nn];
+#pragma unroll
+            for (int m = 0; m < MQ; ++m) {
+                const float4 h4 = *(const float4 *)&Hs[nn][64 * m + 4 * oq];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    off[r][m][0] = fmaf(cv[r], h4.x, off[r][m][0]);
+                    off[r][m][1] = fmaf(cv[r], h4.y, off[r][m][1]);
+                    off[r][m][2] = fmaf(cv[r], h4.z, off[r][m][2]);
+                    off[r][m][3] = fmaf(cv[r], h4.w, off[r][m][3]);
+                }
             }
         }
     }
+
+    const float Dh = a.D ? a.D[h] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 4 * oi + r;
+        if (i >= lrows) break;
+        const float el = expf((float)css[l0 + i]);
+        const T *xl = xp + (l0 + i) * HP;
+        T *yl = (T *)a.y + (tok0 + l0 + i) * HP + (long)h * P;
+#pragma unroll
+        for (int m = 0; m < MQ; ++m) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = 64 * m + 4 * oq + e;
+                if (p < P) st(yl + p, acc[r][m][e] + el * off[r][m][e] + Dh * ld(xl + p));
+            }
+        }
+    }
+}
+
+template <typename T, int MQ>
+hipError_t launch_out(const PrefillArgs &a, dim3 grid, hipStream_t s) {
+    return launch_stage("chunk_out_vec", chunk_out_vec<T, MQ>, grid, dim3(kThreads), 0, s, a);
+}
+
+// MQ = ceil(P / 64): 1, 2 or 4 (P <= 256)
+template <typename T>
+hipError_t launch_out_p(const PrefillArgs &a, dim3 grid, hipStream_t s) {
+    const int mq = (a.P + 63) / 64;
+    if (mq <= 1) return launch_out<T, 1>(a, grid, s);
+    if (mq <= 2) return launch_out<T, 2>(a, grid, s);
+    return launch_out<T, 4>(a, grid, s);
 }
 
 }  // namespace
@@ -225,12 +388,17 @@ hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s)
                        ? launch_stage("chunk_state_vec", chunk_state_vec<bf16_t>, g1, dim3(kThreads), 0, s, a)
                        : launch_stage("chunk_state_vec", chunk_state_vec<float>, g1, dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
+    const long nlt = (a.Q + LT - 1) / LT;
+    if (a.G > 65535) return hipErrorInvalidConfiguration;
+    dim3 g2((unsigned)(a.nchunks * nlt), a.G, gridB);
+    e = dtype == DT_BF16 ? launch_stage("chunk_cb_vec", chunk_cb_vec<bf16_t>, g2, dim3(kThreads), 0, s, a)
+                         : launch_stage("chunk_cb_vec", chunk_cb_vec<float>, g2, dim3(kThreads), 0, s, a);
+    if (e != hipSuccess) return e;
     e = launch_state_pass(a, s);
     if (e != hipSuccess) return e;
-    const long nlt = (a.Q + LT - 1) / LT;
-    dim3 g3((unsigned)(a.nchunks * nlt), a.H, gridB);
-    return dtype == DT_BF16 ? launch_stage("chunk_out_vec", chunk_out_vec<bf16_t>, g3, dim3(kThreads), 0, s, a)
-                            : launch_stage("chunk_out_vec", chunk_out_vec<float>, g3, dim3(kThreads), 0, s, a);
+    const long nlto = (a.Q + LTO - 1) / LTO;
+    dim3 g3((unsigned)(a.nchunks * nlto), a.H, gridB);
+    return dtype == DT_BF16 ? launch_out_p<bf16_t>(a, g3, s) : launch_out_p<float>(a, g3, s);
 }
 
 }  // namespace ssd

@@ -82,7 +82,9 @@ WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q,
     w.off_hb = align_up(w.off_cs + cs_bytes, 256);
     const size_t hb_bytes = mfma ? heads * P * N * sizeof(uint16_t) : 0;
     w.off_gt = align_up(w.off_hb + hb_bytes, 256);
-    const size_t gt_bytes = mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t) : 0;
+    // MFMA path: G^T tiles in bf16; vector path: the Q x Q masked C B^T in fp32
+    const size_t gt_bytes = mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t)
+                                 : groups * (size_t)Q * Q * sizeof(float);
     w.off_bt = align_up(w.off_gt + gt_bytes, 256);
     const size_t bt_bytes = mfma ? groups * prefill_mfma_bt_elems_per_chunk() * sizeof(uint16_t) : 0;
     w.off_ct = align_up(w.off_bt + bt_bytes, 256);
@@ -204,6 +206,7 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
+    a.ws_cb = mfma ? nullptr : (float *)(ws + wl.off_gt);
     a.chunks = nullptr;
     a.seqs = nullptr;
     if (varlen) {

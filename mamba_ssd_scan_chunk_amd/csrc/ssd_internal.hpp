@@ -57,6 +57,7 @@ struct PrefillArgs {
     uint16_t *ws_gt;  // [B, nchunks, G, tiles, 2, lanes, 8] bf16: masked C B^T (MFMA path)
     uint16_t *ws_bt;  // [B, nchunks, G, Q*N] bf16: B in MFMA operand order (MFMA path)
     uint16_t *ws_ct;  // [B, nchunks, G, Q*N] bf16: C in MFMA operand order (MFMA path)
+    float *ws_cb;     // [B, nchunks, G, Q, Q] fp32: C B^T masked to s <= l (vector path)
 };
 
 struct WorkspaceLayout {

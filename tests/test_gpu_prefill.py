@@ -249,7 +249,7 @@ def test_long_context_prefill_then_decode_sampled_heads(oracle):
 
 @pytest.mark.parametrize("dtype,P,N,Q,kernels", [
     ("bf16", 64, 128, 256, ["chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]),
-    ("f32", 16, 16, 64, ["chunk_state_vec", "state_pass", "chunk_out_vec"]),
+    ("f32", 16, 16, 64, ["chunk_state_vec", "chunk_cb_vec", "state_pass", "chunk_out_vec"]),
 ])
 def test_stage_timing_reports_each_kernel(dtype, P, N, Q, kernels):
     d = synth.make_prefill(1, 700, 4, P, 1, N, dtype, seed=12)
