@@ -397,9 +397,10 @@ def varlen_record(args):
 
 
 def bench_other_prefills(args):
-    """The other prefill workloads: the 130M-shaped layer (B=1, L=4096, H=24)
-    and the batched long-context prefill (B=8, L=16384, H=80) followed by its
-    cached decode steps (B=8, in a HIP graph of 256 steps)."""
+    """The other prefill workloads: the 130M-shaped layer (B=1, L=4096, H=24),
+    the batched long-context prefill (B=8, L=16384, H=80) followed by its
+    cached decode steps (B=8, in a HIP graph of 256 steps), and the 2.7B-shaped
+    layer with 512-token chunks and with fp32 activations."""
     import torch
 
     from mamba_ssd_scan_chunk_amd import binding as bd
@@ -449,6 +450,27 @@ def bench_other_prefills(args):
             rec["decode"] = {"steps": 256, "graph_us_per_step": round(gms * 1e3, 3),
                              "gbs": round(dbytes / (gms * 1e-3) / 1e9, 1)}
         out[name] = rec
+    # the 2.7B-shaped prefill with 512-token chunks (vector path) and with fp32
+    # activations (vector path)
+    w = synth.WORKLOADS["mamba2-2.7b-prefill"]
+    for key, dtype, Q in (("mamba2-2.7b-prefill-q512", "bf16", 512), ("mamba2-2.7b-prefill-f32", "f32", 256)):
+        d = {k: v.cuda() for k, v in synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, dtype, seed=17).items()}
+        y = torch.empty_like(d["x"])
+        fs = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+        code = bd.SSD_BF16 if dtype == "bf16" else bd.SSD_F32
+        ws = torch.empty(max(1, bd.ssd_prefill_workspace_bytes(w.B, w.L, w.H, w.P, w.G, w.N, Q, code)),
+                         dtype=torch.uint8, device="cuda")
+
+        def vstep(_):
+            bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], None, Q=Q, y=y, final_state=fs,
+                           workspace=ws)
+
+        ms = _timed(vstep, 5, 1, key)
+        flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, Q)
+        out[key] = {"dtype": dtype, "chunk": Q, "path": "vector", "us": round(ms * 1e3, 1),
+                    "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        del d, y, ws
     return {"other_workloads": out}
 
 
