@@ -17,7 +17,13 @@
  * ssd_decode_step advances it by one token from a cached state, optionally
  * after one step of the depthwise causal convolution whose (K-1)-token input
  * window is the other half of the cache; conv_state_update runs that
- * convolution over T tokens.
+ * convolution over T tokens.  Around them:
+ *   - ssd_prefill_dt_raw / ssd_decode_step_dt_raw form the step from its raw
+ *     projection inside the kernels (softplus, bias, clip; §1.2);
+ *   - ssd_prefill_varlen / conv_state_update_varlen take sequences of
+ *     different lengths packed without padding;
+ *   - ssd_gated_rmsnorm is the normalisation that closes the layer (the
+ *     output gated by the z branch, then RMS-normalised per group, §3.2).
  *
  * Conventions shared by every entry point
  *   - Layouts: dense, row-major (C-contiguous) in the shapes given, unless a
@@ -41,7 +47,8 @@
  *     buffers do not overlap.
  *   - dtype: SSD_F32 or SSD_BF16, the storage type of the activations named
  *     "void*" below (x, Bm, Cm, y and the conv data).  dt, A_log, D and the
- *     SSM state are always fp32; all arithmetic accumulates in fp32.
+ *     SSM state are always fp32; all arithmetic accumulates in fp32 (the
+ *     in-chunk cumsum of the fp32 vector path in fp64).
  */
 #ifndef MAMBA_SSD_H
 #define MAMBA_SSD_H
