@@ -13,6 +13,9 @@
 // which makes the in-place update race free.  Two forms: one channel per
 // thread (any C and alignment), and V channels per thread with 16-byte
 // accesses (C % V == 0, 16-byte aligned tensors), the one the 2.7B shape uses.
+// For sequences packed without padding the channel-group form takes its
+// token blocks (sequence, block, first row, tokens) from a slot table built
+// on the device (chunk_table.hip), each sequence starting from its own cache.
 #include "ssd_device.hpp"
 #include "ssd_internal.hpp"
 

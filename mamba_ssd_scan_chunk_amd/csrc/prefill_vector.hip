@@ -7,11 +7,14 @@
 //   h_c      = exp(cs_last) h_{c-1} + S_c                          (state pass)
 //   y_l      = sum_{s<=l} (C_l . B_s) exp(cs_l - cs_s) dt_s x_s
 //              + exp(cs_l) C_l . h_{c-1} + D x_l                    (output)
-// Three kernels: chunk states, the state pass (prefill_state_pass.hip) and
-// the output.  Used for fp32 activations and for any bf16 shape the MFMA
-// path does not cover.  All arithmetic is fp32 except the in-chunk cumsum,
-// which is kept in fp64 so that differences cs_l - cs_s stay exact to fp32
-// rounding even when |cs| reaches a few hundred.
+// Four kernels: chunk states, the masked C . B products (once per chunk and
+// group, shared by the group's heads), the state pass
+// (prefill_state_pass.hip) and the output.  Used for fp32 activations and
+// for any bf16 shape the MFMA path does not cover (P, N <= 256, Q <= 1024).
+// All arithmetic is fp32 except the in-chunk cumsum, which is kept in fp64
+// so that differences cs_l - cs_s stay exact to fp32 rounding even when |cs|
+// reaches a few hundred.  Chunks come from chunk_at, so packed sequences use
+// the same kernels.
 #include "ssd_device.hpp"
 #include "ssd_internal.hpp"
 
