@@ -25,11 +25,12 @@ constexpr int kThreads = 256;
 constexpr int kTpt = 4;                    // chunk tokens per thread in the chunk-state kernel
 constexpr int kSP = 64, kSN = 128, kST = 16;  // chunk-state output pass (16 x 16 threads of 4 x 8) and token step
 constexpr int kMaxQ = kThreads * kTpt;     // largest chunk this path takes
-constexpr int LT = 16;    // rows per workgroup of the C B^T kernel
+constexpr int CBT = 64, CBN = 32;  // C B^T kernel: 64 x 64 tiles, 32 columns of n per step
 constexpr int LTO = 64;   // output rows per workgroup of the output kernel
 constexpr int ST = 16;    // source tokens per step of the output kernel
 constexpr int MAXD = 256;  // largest P and N
 static_assert(kMaxQ == kPrefillMaxQ, "chunk limit of the vector path");
+static_assert(CBT * CBT == 16 * kThreads, "C B^T kernel: 4 x 4 outputs per thread");
 static_assert(LTO * 4 == kThreads && (LTO * ST) % kThreads == 0 && 4 * 64 == MAXD,
               "output kernel: 16 threads per four output rows, 64 features per pass");
 
@@ -159,21 +160,29 @@ __global__ __launch_bounds__(kThreads) void chunk_state_vec(PrefillArgs a) {
     }
 }
 
-// Grid (nchunks * ceil(Q/LT), G, B).  The causal masked product of the
-// chunk, G[l][s] = C_l . B_s for s <= l (0 above the diagonal), once per
-// (chunk, group) for every head of the group: rows l0 .. l0+LT-1, all
-// columns s <= l0+LT-1, in LT x LT tiles (one element per thread).
+// Grid (nchunks * T(T+1)/2, G, B) with T = ceil(Q/CBT).  The causal masked
+// product of the chunk, G[l][s] = C_l . B_s for s <= l (0 above the
+// diagonal), once per (chunk, group) for every head of the group: one
+// workgroup per CBT x CBT tile on or below the diagonal, each thread a
+// 4 x 4 register tile.  C and B
+// are staged transposed ([n][row]) CBN columns of n at a time, so a step of n
+// is two 16-byte LDS reads for 16 FMAs.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void chunk_cb_vec(PrefillArgs a) {
-    __shared__ float Cl[LT][MAXD + 1];
-    __shared__ float Bt[LT][MAXD + 1];
-    const int nlt = (a.Q + LT - 1) / LT;
-    const int c = blockIdx.x / nlt, lt = blockIdx.x - (blockIdx.x / nlt) * nlt;
+    // rows padded by 4 floats: the transposing stores spread over 8 banks,
+    // the 16-byte reads stay aligned
+    __shared__ __attribute__((aligned(16))) float Ct[CBN][CBT + 4];
+    __shared__ __attribute__((aligned(16))) float Bt[CBN][CBT + 4];
+    const int nlt = (a.Q + CBT - 1) / CBT, ntile = nlt * (nlt + 1) / 2;
+    const int c = blockIdx.x / ntile, tix = blockIdx.x - (blockIdx.x / ntile) * ntile;
+    int lt = 0;
+    while ((lt + 1) * (lt + 2) / 2 <= tix) ++lt;
+    const int st = tix - lt * (lt + 1) / 2;  // source tile, st <= lt
     const int g = blockIdx.y;
     const long f = (long)blockIdx.z * a.nchunks + c;
     const ChunkEntry ch = chunk_at(a, f);
     const int Qc = ch.Qc;
-    const int l0 = lt * LT;
+    const int l0 = lt * CBT;
     if (l0 >= Qc) return;
     const int N = a.N;
     const long GN = (long)a.G * N;
@@ -181,26 +190,44 @@ __global__ __launch_bounds__(kThreads) void chunk_cb_vec(PrefillArgs a) {
     const T *Bp = (const T *)a.Bm + (tok0 * a.G + g) * N;
     const T *Cp = (const T *)a.Cm + (tok0 * a.G + g) * N;
     float *Gp = a.ws_cb + (f * a.G + g) * a.Q * a.Q;
-    const int tid = threadIdx.x, i = tid / LT, j = tid - (tid / LT) * LT;
-    for (int e = tid; e < LT * N; e += kThreads) {
-        const int r = e / N, n = e - r * N;
-        Cl[r][n] = l0 + r < Qc ? ld(Cp + (l0 + r) * GN + n) : 0.0f;
-    }
-    for (int s0 = 0; s0 <= l0; s0 += LT) {
-        __syncthreads();
-        for (int e = tid; e < LT * N; e += kThreads) {
-            const int r = e / N, n = e - r * N;
-            Bt[r][n] = s0 + r < Qc ? ld(Bp + (s0 + r) * GN + n) : 0.0f;
+    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;  // rows 4ti.., columns 4tj..
+    {
+        const int s0 = st * CBT;
+        float acc[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[r][q] = 0.0f;
+        for (int n0 = 0; n0 < N; n0 += CBN) {
+            __syncthreads();  // the previous step is consumed
+            for (int e = tid; e < CBN * CBT; e += kThreads) {  // element (row, nn), nn fastest for coalescing
+                const int row = e / CBN, nn = e - (e / CBN) * CBN, n = n0 + nn;
+                Ct[nn][row] = (l0 + row < Qc && n < N) ? ld(Cp + (l0 + row) * GN + n) : 0.0f;
+                Bt[nn][row] = (s0 + row < Qc && n < N) ? ld(Bp + (s0 + row) * GN + n) : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll 8
+            for (int nn = 0; nn < CBN; ++nn) {
+                const float4 cv = *(const float4 *)&Ct[nn][4 * ti];
+                const float4 bv = *(const float4 *)&Bt[nn][4 * tj];
+                const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, bq[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[r][q] = fmaf(cr[r], bq[q], acc[r][q]);
+            }
         }
-        __syncthreads();
-        float d = 0.0f;
-        if (l0 + i >= s0 + j) {
-            for (int n = 0; n < N; ++n) d = fmaf(Cl[i][n], Bt[j][n], d);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int l = l0 + 4 * ti + r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int sx = s0 + 4 * tj + q;
+                if (l < Qc && sx < Qc && sx <= l0 + CBT - 1) Gp[(long)l * a.Q + sx] = sx <= l ? acc[r][q] : 0.0f;
+            }
         }
-        if (l0 + i < Qc && s0 + j < Qc) Gp[(long)(l0 + i) * a.Q + s0 + j] = d;
     }
 }
-
 
 // Grid (nchunks * ceil(Q/LTO), H, B).  Reads the masked C B^T of the chunk
 // and group (chunk_cb_vec) and the carried-in state h_{c-1} that the state
@@ -209,8 +236,11 @@ __global__ __launch_bounds__(kThreads) void chunk_cb_vec(PrefillArgs a) {
 // token four LDS reads of G' and one 16-byte read of x per m feed 16 FMAs per m.
 template <typename T, int MQ>
 __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) float Xs[ST][MAXD];
-    __shared__ __attribute__((aligned(16))) float Hs[ST][MAXD];
+    // x rows of a source step in the main loop, then h columns in the state
+    // term: one LDS array for both
+    __shared__ __attribute__((aligned(16))) float XHs[ST][MAXD];
+    float (*Xs)[MAXD] = XHs;
+    float (*Hs)[MAXD] = XHs;
     __shared__ float Gt[LTO][ST + 1];
     __shared__ float Cl[LTO][ST + 1];
     __shared__ double css[kMaxQ];  // cumsum of the chunk's sources s < l0 + LTO
@@ -250,43 +280,37 @@ __global__ __launch_bounds__(kThreads) void chunk_out_vec(PrefillArgs a) {
         css[sx] = cs[sx];
         dts[sx] = dt_value(a.dt[(tok0 + sx) * a.H + h], a.dtp.dt_raw, a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max);
     }
-    // G' = G * exp(cs_l - cs_s) * dt_s of a LTO x ST tile (four elements per
-    // thread) and its x rows (up to XPT elements per thread), into registers;
-    // the next tile's are loaded while the current one is consumed
-    constexpr int GPT = LTO * ST / kThreads, XPT = ST * MAXD / kThreads;
-    float gnext[GPT], xnext[XPT];
-    auto load_tile = [&](int s0) {
+    // the product G of a LTO x ST tile, four elements per thread, read one
+    // step ahead (its scattered 64-byte rows are the longest wait of a step)
+    constexpr int GPT = LTO * ST / kThreads;
+    float gnext[GPT];
+    auto load_g = [&](int s0) {
 #pragma unroll
         for (int k = 0; k < GPT; ++k) {
             const int e = tid + k * kThreads;
             const int gi = e / ST, gj = e - (e / ST) * ST, sx = s0 + gj;
-            gnext[k] = (gi < lrows && sx < send && l0 + gi >= sx)
-                           ? Gp[(long)(l0 + gi) * a.Q + sx] * expf((float)(css[l0 + gi] - css[sx])) * dts[sx]
-                           : 0.0f;
-        }
-#pragma unroll
-        for (int k = 0; k < XPT; ++k) {
-            const int e = tid + k * kThreads;
-            const int r = e / P, p = e - (e / P) * P;
-            xnext[k] = (e < ST * P && s0 + r < send) ? ld(xp + (s0 + r) * HP + p) : 0.0f;
+            gnext[k] = (gi < lrows && sx < send && l0 + gi >= sx) ? Gp[(long)(l0 + gi) * a.Q + sx] : 0.0f;
         }
     };
+    load_g(0);
     __syncthreads();  // css, dts
-    load_tile(0);
     for (int s0 = 0; s0 < send; s0 += ST) {
-        __syncthreads();  // the previous tile is consumed
+        __syncthreads();  // the previous step is consumed
+        // G' = G * exp(cs_l - cs_s) * dt_s, and the step's x rows
 #pragma unroll
         for (int k = 0; k < GPT; ++k) {
             const int e = tid + k * kThreads;
-            Gt[e / ST][e - (e / ST) * ST] = gnext[k];
+            const int gi = e / ST, gj = e - (e / ST) * ST, sx = s0 + gj;
+            Gt[gi][gj] = (gi < lrows && sx < send && l0 + gi >= sx)
+                             ? gnext[k] * expf((float)(css[l0 + gi] - css[sx])) * dts[sx]
+                             : 0.0f;
         }
-#pragma unroll
-        for (int k = 0; k < XPT; ++k) {
-            const int e = tid + k * kThreads;
-            if (e < ST * P) Xs[e / P][e - (e / P) * P] = xnext[k];
+        if (s0 + ST < send) load_g(s0 + ST);
+        for (int e = tid; e < ST * P; e += kThreads) {
+            const int r = e / P, p = e - (e / P) * P;
+            Xs[r][p] = s0 + r < send ? ld(xp + (s0 + r) * HP + p) : 0.0f;
         }
         __syncthreads();
-        if (s0 + ST < send) load_tile(s0 + ST);
         const int srows = min(ST, send - s0);
         for (int j = 0; j < srows; ++j) {
             float gg[4];
@@ -391,9 +415,10 @@ hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s)
                        ? launch_stage("chunk_state_vec", chunk_state_vec<bf16_t>, g1, dim3(kThreads), 0, s, a)
                        : launch_stage("chunk_state_vec", chunk_state_vec<float>, g1, dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
-    const long nlt = (a.Q + LT - 1) / LT;
     if (a.G > 65535) return hipErrorInvalidConfiguration;
-    dim3 g2((unsigned)(a.nchunks * nlt), a.G, gridB);
+    const long ncb = (a.Q + CBT - 1) / CBT;
+    if ((long)a.nchunks * (ncb * (ncb + 1) / 2) > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    dim3 g2((unsigned)(a.nchunks * (ncb * (ncb + 1) / 2)), a.G, gridB);
     e = dtype == DT_BF16 ? launch_stage("chunk_cb_vec", chunk_cb_vec<bf16_t>, g2, dim3(kThreads), 0, s, a)
                          : launch_stage("chunk_cb_vec", chunk_cb_vec<float>, g2, dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
