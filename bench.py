@@ -450,8 +450,8 @@ def bench_other_prefills(args):
             rec["decode"] = {"steps": 256, "graph_us_per_step": round(gms * 1e3, 3),
                              "gbs": round(dbytes / (gms * 1e-3) / 1e9, 1)}
         out[name] = rec
-    # the 2.7B-shaped prefill with 512-token chunks (vector path) and with fp32
-    # activations (vector path)
+    # the 2.7B-shaped prefill with 512-token chunks (MFMA kernels, 256-token
+    # sub-chunks) and with fp32 activations (vector path)
     w = synth.WORKLOADS["mamba2-2.7b-prefill"]
     for key, dtype, Q in (("mamba2-2.7b-prefill-q512", "bf16", 512), ("mamba2-2.7b-prefill-f32", "f32", 256)):
         d = {k: v.cuda() for k, v in synth.make_prefill(w.B, w.L, w.H, w.P, w.G, w.N, dtype, seed=17).items()}
@@ -467,7 +467,8 @@ def bench_other_prefills(args):
 
         ms = _timed(vstep, 5, 1, key)
         flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, Q)
-        out[key] = {"dtype": dtype, "chunk": Q, "path": "vector", "us": round(ms * 1e3, 1),
+        path = "mfma, 256-token sub-chunks" if dtype == "bf16" and Q % 256 == 0 else "vector"
+        out[key] = {"dtype": dtype, "chunk": Q, "path": path, "us": round(ms * 1e3, 1),
                     "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
                     "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
         del d, y, ws

@@ -100,9 +100,12 @@ enum {
  * init_state (or zeros).  Alignment: x, Bm, Cm, y, init_state, final_state
  * 16-byte aligned.  Limits: 1 <= P <= 256, 1 <= N <= 256, 1 <= Q <= 1024
  * (Q = 512 is the chunk suggested for contexts beyond 8k tokens, bqwf.cn
- * article §6.3).  bf16 with (P, N, Q) = (64, 128, 256) runs on MFMA
- * (bf16 operands, fp32 accumulation, decay factors in fp32); every other
- * shape runs on the fp32 vector path.  The MFMA path factors the decay
+ * article §6.3).  bf16 with (P, N) = (64, 128) and Q a multiple of 256 runs
+ * on MFMA (bf16 operands, fp32 accumulation, decay factors in fp32) in
+ * 256-token sub-chunks linked by the state pass: the chunked scan is the same
+ * for any chunk length up to rounding, and 256 is the chunk these kernels are
+ * built for.  Every other shape runs on the fp32 vector path with chunks of
+ * exactly Q tokens.  The MFMA path factors the decay
  * exp(cs_l - cs_s) per 32-token tile; a chunk whose factors would leave the
  * normal fp32 range (a token more than 60 from its tile reference in cumsum
  * of dt*A, tile references more than 80 apart, dt <= 0, or |D/dt| > 1e30)

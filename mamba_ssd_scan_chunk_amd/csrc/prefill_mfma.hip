@@ -1,5 +1,6 @@
 // prefill_mfma.hip -- chunked SSD prefill on bf16 MFMA (gfx950),
-// P = 64, N = 128, chunk Q = 256.
+// P = 64, N = 128, chunks of 256 tokens (a longer chunk, a multiple of 256,
+// runs as 256-token sub-chunks linked by the state pass).
 //
 // The chunked form of the scan of arXiv 2603.09555 as laid out in the bqwf.cn
 // article on its compiler-first Mamba-2 implementation: §1.1 (fixed chunks,
@@ -49,7 +50,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQ = 256, kP = 64, kN = 128, kThreads = 256;
+constexpr int kQ = kMfmaQ, kP = 64, kN = 128, kThreads = 256;
 constexpr int kTiles = kQ / 32;                      // token tiles per chunk
 constexpr int kGTiles = kTiles * (kTiles + 1) / 2;   // causal 32x32 tiles of G^T
 constexpr long kGTChunk = (long)kGTiles * 64 * 16;   // bf16 per chunk (64 lanes x 16)

@@ -66,8 +66,12 @@ int check_prefill_shape(const PrefillShape &s) {
 
 namespace ssd {
 
+// The MFMA kernels run 256-token chunks.  A chunk of any multiple of 256
+// tokens runs as 256-token sub-chunks whose hand-off goes through the state
+// pass: the chunked form gives the same scan for any chunk length (up to
+// rounding), so the sub-chunks are an evaluation order, not an approximation.
 bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
-    return dtype == SSD_BF16 && P == 64 && N == 128 && Q == 256;
+    return dtype == SSD_BF16 && P == 64 && N == 128 && Q % kMfmaQ == 0;
 }
 
 WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq) {
@@ -97,14 +101,19 @@ WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q,
 }  // namespace ssd
 
 namespace {
-// Chunk slots of a prefill: B * ceil(L / Q) for a uniform batch, the bound
-// varlen_slots(T, B, Q) for packed sequences (0 when there are no tokens).
+// Chunk length the kernels run: 256 on the MFMA path (see prefill_uses_mfma),
+// Q on the vector path.
+int run_q(const PrefillShape &s) { return ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype) ? ssd::kMfmaQ : s.Q; }
+// Chunk slots of a prefill: B * ceil(L / q) for a uniform batch, the bound
+// varlen_slots(T, B, q) for packed sequences (0 when there are no tokens),
+// q = run_q.
 long prefill_slots(const PrefillShape &s) {
     if (s.L <= 0) return 0;
-    return s.varlen ? ssd::varlen_slots(s.L, s.B, s.Q) : (long)s.B * ((s.L + s.Q - 1) / s.Q);
+    const int q = run_q(s);
+    return s.varlen ? ssd::varlen_slots(s.L, s.B, q) : (long)s.B * ((s.L + q - 1) / q);
 }
 size_t workspace_bytes_for(const PrefillShape &s) {
-    return ssd::prefill_workspace_layout(prefill_slots(s), s.H, s.P, s.N, s.Q, s.G,
+    return ssd::prefill_workspace_layout(prefill_slots(s), s.H, s.P, s.N, run_q(s), s.G,
                                          ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype), s.varlen ? s.B : 0)
         .total;
 }
@@ -158,8 +167,9 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
         return SSD_ERR_ALIGNMENT;
 
     const bool mfma = ssd::prefill_uses_mfma(P, N, Q, dtype);
+    const int q = run_q(s);
     const long slots = prefill_slots(s);
-    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(slots, H, P, N, Q, G, mfma, varlen ? B : 0);
+    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(slots, H, P, N, q, G, mfma, varlen ? B : 0);
     const size_t b_ws = wl.total;
 
     // outputs may not overlap inputs, workspace or each other
@@ -191,8 +201,8 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     }
 
     ssd::PrefillArgs a;
-    a.B = B; a.L = varlen ? 0 : L; a.H = H; a.P = P; a.G = G; a.N = N; a.Q = Q;
-    a.nchunks = varlen ? (int)slots : (L + Q - 1) / Q;
+    a.B = B; a.L = varlen ? 0 : L; a.H = H; a.P = P; a.G = G; a.N = N; a.Q = q;
+    a.nchunks = varlen ? (int)slots : (L + q - 1) / q;
     a.T = (int)rows;
     a.cu_seqlens = varlen ? cu_seqlens : nullptr;
     a.x = x; a.dt = dt; a.A_log = A_log; a.Bm = Bm; a.Cm = Cm; a.D = D;

@@ -63,7 +63,8 @@ struct PrefillArgs {
 struct WorkspaceLayout {
     size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, off_tab, total;
 };
-constexpr int kPrefillMaxQ = 1024;  // largest chunk (vector path; the MFMA path is Q = 256)
+constexpr int kPrefillMaxQ = 1024;  // largest chunk
+constexpr int kMfmaQ = 256;         // chunk of the MFMA kernels
 long prefill_mfma_gt_elems_per_chunk();
 long prefill_mfma_bt_elems_per_chunk();
 // Workspace for `slots` chunk slots of H heads (and G groups), plus the slot

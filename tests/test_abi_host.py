@@ -198,6 +198,16 @@ def test_varlen_rejects(lib, kw, code):
     assert _varlen(lib, **kw) == code
 
 
+def test_mfma_longer_chunks_use_the_256_token_workspace(lib):
+    w256 = lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 128, 256, 1)
+    assert lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 128, 512, 1) == w256
+    assert lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 128, 1024, 1) == w256
+    # not a multiple of 256, or not the MFMA shape: the vector path's workspace
+    assert lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 128, 384, 1) != w256
+    assert lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 64, 512, 1) != \
+        lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 64, 256, 1)
+
+
 def test_varlen_workspace_bytes(lib):
     n = lib.ssd_prefill_varlen_workspace_bytes(3, 500, 2, 64, 1, 128, 256, 1)
     # chunk slots: 500 / 256 + 3 = 4; the slot and sequence tables come last

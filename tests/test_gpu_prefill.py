@@ -43,9 +43,12 @@ CASES = [
     ("f32-max-dims", 1, 300, 1, 256, 1, 256, 256, "f32"),
     ("bf16-max-dims", 1, 270, 1, 256, 1, 256, 256, "bf16"),
     ("f32-min-q", 1, 50, 2, 1, 1, 1, 16, "f32"),
-    # chunks longer than 256 tokens (vector path): Q = 512 as suggested for
-    # long contexts, up to the largest chunk, with ragged thread shares
+    # chunks longer than 256 tokens: Q = 512 as suggested for long contexts
+    # (MFMA shape: 256-token sub-chunks; other shapes: the vector path with
+    # 512-token chunks), up to the largest chunk, with ragged thread shares
     ("bf16-q512", 1, 1300, 2, 64, 1, 128, 512, "bf16"),
+    ("bf16-q768-mfma", 2, 1700, 3, 64, 1, 128, 768, "bf16"),
+    ("bf16-q512-vector", 1, 1300, 2, 64, 1, 64, 512, "bf16"),
     ("f32-q1024", 1, 2200, 2, 16, 1, 16, 1024, "f32"),
     ("f32-q384-groups", 2, 900, 4, 8, 2, 32, 384, "f32"),
     ("f32-q1000-eq-l", 1, 1000, 1, 4, 1, 8, 1000, "f32"),
@@ -90,6 +93,19 @@ def test_prefill_dt_raw_matches_oracle(oracle, name, raw_dt):
     y_ref, fs_ref = oracle.ssd_scan(d["x"], dt_ref, d["A_log"], d["Bm"], d["Cm"], d["D"], init)
     assert rel_err(y, y_ref) <= _tol(dtype)
     assert rel_err(fs, fs_ref) <= _tol(dtype)
+
+
+def test_mfma_longer_chunks_are_256_token_sub_chunks():
+    """On the MFMA shape a chunk of 512 or 1024 tokens runs as 256-token
+    sub-chunks linked by the state pass: the same arithmetic as Q = 256, so
+    the same bits."""
+    d = dev(synth.make_prefill(2, 1500, 3, 64, 1, 128, "bf16", seed=460))
+    announce("mfma Q=512/1024 vs 256")
+    y0, f0 = bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=256)
+    for Q in (512, 1024):
+        y1, f1 = bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=Q)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y0) and torch.equal(f1, f0), Q
 
 
 @pytest.mark.parametrize("with_init", [False, True])

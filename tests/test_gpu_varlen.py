@@ -14,7 +14,8 @@ PATHS = [
     # name, H, P, G, N, Q, dtype
     ("mfma", 4, 64, 2, 128, 256, "bf16"),
     ("vector-f32", 3, 16, 1, 16, 64, "f32"),
-    ("vector-bf16-q512", 2, 64, 1, 128, 512, "bf16"),
+    ("mfma-q512", 2, 64, 1, 128, 512, "bf16"),
+    ("vector-bf16-q512", 2, 64, 1, 64, 512, "bf16"),
 ]
 MIXES = {
     # empty sequences, one token, chunk-size boundaries, ragged tails
