@@ -20,8 +20,8 @@
  * convolution over T tokens.  Around them:
  *   - ssd_prefill_dt_raw / ssd_decode_step_dt_raw form the step from its raw
  *     projection inside the kernels (softplus, bias, clip; §1.2);
- *   - ssd_prefill_varlen / conv_state_update_varlen take sequences of
- *     different lengths packed without padding;
+ *   - ssd_prefill_varlen (and its _dt_raw form) / conv_state_update_varlen
+ *     take sequences of different lengths packed without padding;
  *   - ssd_gated_rmsnorm is the normalisation that closes the layer (the
  *     output gated by the z branch, then RMS-normalised per group, §3.2).
  *
@@ -174,6 +174,19 @@ int ssd_prefill_varlen(int B, int T, int H, int P, int G, int N, int Q, int dtyp
                        const void *Bm, const void *Cm, const float *D,
                        const float *init_state, void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssd_prefill_varlen_dt_raw -- ssd_prefill_varlen with the step computed from
+ * its raw value inside the kernels, as in ssd_prefill_dt_raw (dt_raw [T,H],
+ * dt_bias [H] or NULL, 0 <= dt_min <= dt_max).  Same workspace size as
+ * ssd_prefill_varlen.
+ */
+int ssd_prefill_varlen_dt_raw(int B, int T, int H, int P, int G, int N, int Q, int dtype,
+                              const int *cu_seqlens, const void *x, const float *dt_raw,
+                              const float *dt_bias, float dt_min, float dt_max, const float *A_log,
+                              const void *Bm, const void *Cm, const float *D,
+                              const float *init_state, void *y, float *final_state,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace ssd_prefill_varlen needs (0 if none); (size_t)-1 for
  * arguments it would reject. */

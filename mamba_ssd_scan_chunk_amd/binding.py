@@ -33,6 +33,7 @@ SIGNATURES = {
     "ssd_prefill_workspace_bytes": (_sz, [_i] * 8),
     "ssd_prefill_varlen": (_i, [_i] * 8 + [_p] * 11 + [_sz, _p]),
     "ssd_prefill_varlen_workspace_bytes": (_sz, [_i] * 8),
+    "ssd_prefill_varlen_dt_raw": (_i, [_i] * 8 + [_p] * 4 + [_f, _f] + [_p] * 8 + [_sz, _p]),
     "ssd_decode_step": (_i, [_i] * 6 + [_p] * 8 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "ssd_decode_step_dt_raw": (_i, [_i] * 6 + [_p] * 3 + [_f, _f] + [_p] * 6 + [_l] + [_p] * 4 + [_i, _i, _p]),
     "conv_state_update": (_i, [_i] * 5 + [_p] * 4 + [_i, _p, _p]),
@@ -153,14 +154,18 @@ def ssd_prefill(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y=None,
 
 
 def ssd_prefill_varlen(x, dt, A_log, Bm, Cm, D, cu_seqlens, init_state=None, *, Q, y=None, final_state=None,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, dt_raw=False, dt_bias=None, dt_min=0.0, dt_max=float("inf")):
     """Prefill of B sequences packed without padding: x [T,H,P], dt [T,H],
     Bm/Cm [T,G,N], cu_seqlens [B+1] int32 on the GPU (sequence b is rows
     cu_seqlens[b] .. cu_seqlens[b+1]).  init_state / final_state [B,H,P,N].
-    Returns (y [T,H,P], final_state)."""
+    With ``dt_raw`` the step is clamp(softplus(dt + dt_bias), dt_min, dt_max)
+    (ssd_prefill_varlen_dt_raw).  Returns (y [T,H,P], final_state)."""
     for t, n in ((x, "x"), (dt, "dt"), (A_log, "A_log"), (Bm, "Bm"), (Cm, "Cm"), (D, "D"),
-                 (init_state, "init_state"), (y, "y"), (final_state, "final_state"), (cu_seqlens, "cu_seqlens")):
+                 (init_state, "init_state"), (y, "y"), (final_state, "final_state"), (cu_seqlens, "cu_seqlens"),
+                 (dt_bias, "dt_bias")):
         _dense(t, n)
+    if dt_bias is not None and not dt_raw:
+        raise ValueError("dt_bias is used only with dt_raw=True")
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     T, H, P = x.shape
@@ -176,10 +181,18 @@ def ssd_prefill_varlen(x, dt, A_log, Bm, Cm, D, cu_seqlens, init_state=None, *, 
         raise ValueError("ssd_prefill_varlen would reject these arguments")
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
-    rc = lib().ssd_prefill_varlen(B, T, H, P, G, N, Q, code, _ptr(cu_seqlens), _ptr(x), _ptr(dt), _ptr(A_log),
-                                  _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
-                                  _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
-    _check("ssd_prefill_varlen", rc)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if dt_raw:
+        rc = lib().ssd_prefill_varlen_dt_raw(B, T, H, P, G, N, Q, code, _ptr(cu_seqlens), _ptr(x), _ptr(dt),
+                                             _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(A_log), _ptr(Bm),
+                                             _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                                             _ptr(workspace), ws_bytes, _stream(stream))
+        _check("ssd_prefill_varlen_dt_raw", rc)
+    else:
+        rc = lib().ssd_prefill_varlen(B, T, H, P, G, N, Q, code, _ptr(cu_seqlens), _ptr(x), _ptr(dt), _ptr(A_log),
+                                      _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                                      _ptr(workspace), ws_bytes, _stream(stream))
+        _check("ssd_prefill_varlen", rc)
     return y, final_state
 
 

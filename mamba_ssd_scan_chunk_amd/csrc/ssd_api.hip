@@ -307,6 +307,18 @@ SSD_API int ssd_prefill_varlen(int B, int T, int H, int P, int G, int N, int Q, 
                         final_state, workspace, workspace_bytes, stream, ssd::DtPrep{0, nullptr, 0.0f, 0.0f}, true);
 }
 
+SSD_API int ssd_prefill_varlen_dt_raw(int B, int T, int H, int P, int G, int N, int Q, int dtype,
+                                      const int *cu_seqlens, const void *x, const float *dt_raw,
+                                      const float *dt_bias, float dt_min, float dt_max, const float *A_log,
+                                      const void *Bm, const void *Cm, const float *D,
+                                      const float *init_state, void *y, float *final_state,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dt_prep(dt_min, dt_max, dt_bias)) return aligned(dt_bias, 4) ? SSD_ERR_INVALID_ARG : SSD_ERR_ALIGNMENT;
+    return prefill_impl(B, T, H, P, G, N, Q, dtype, cu_seqlens, x, dt_raw, A_log, Bm, Cm, D, init_state, y,
+                        final_state, workspace, workspace_bytes, stream, ssd::DtPrep{1, dt_bias, dt_min, dt_max},
+                        true);
+}
+
 SSD_API int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, int dtype,
                                const void *x, const float *dt_raw, const float *dt_bias, float dt_min,
                                float dt_max, const float *A_log, const void *Bm, const void *Cm,

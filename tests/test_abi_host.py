@@ -208,6 +208,25 @@ def test_mfma_longer_chunks_use_the_256_token_workspace(lib):
         lib.ssd_prefill_workspace_bytes(1, 4096, 80, 64, 1, 64, 256, 1)
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt_min=-1.0), bd.SSD_ERR_INVALID_ARG),
+    (dict(dt_max=float("nan")), bd.SSD_ERR_INVALID_ARG),
+    (dict(bias=_addr(12, 2)), bd.SSD_ERR_ALIGNMENT),
+    (dict(cu=None), bd.SSD_ERR_INVALID_ARG),
+    (dict(y=_addr(12, 0)), bd.SSD_ERR_INVALID_ARG),  # y overlaps dt_bias
+])
+def test_varlen_dt_raw_rejects(lib, kw, code):
+    p = dict(cu=_addr(13), x=_addr(0), dt=_addr(1), bias=_addr(12), A_log=_addr(2), Bm=_addr(3), Cm=_addr(4),
+             D=_addr(5), init=_addr(6), y=_addr(7), final=_addr(8), ws=_addr(9))
+    kw = dict(kw)
+    lo, hi = kw.pop("dt_min", 0.0), kw.pop("dt_max", 1.0)
+    p.update(kw)
+    rc = lib.ssd_prefill_varlen_dt_raw(3, 500, 2, 64, 1, 128, 256, 1, p["cu"], p["x"], p["dt"], p["bias"], lo, hi,
+                                       p["A_log"], p["Bm"], p["Cm"], p["D"], p["init"], p["y"], p["final"], p["ws"],
+                                       1 << 40, None)
+    assert rc == code
+
+
 def test_varlen_workspace_bytes(lib):
     n = lib.ssd_prefill_varlen_workspace_bytes(3, 500, 2, 64, 1, 128, 256, 1)
     # chunk slots: 500 / 256 + 3 = 4; the slot and sequence tables come last

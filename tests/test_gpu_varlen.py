@@ -203,3 +203,22 @@ def test_packed_prompts_then_decode(oracle):
                                        conv_b=bias, activation=True)
     assert rel_err(y, y_ref) <= TOL_BF16
     assert rel_err(state, st2) <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", PATHS[:2], ids=[p[0] for p in PATHS[:2]])
+def test_varlen_dt_raw_matches_oracle(oracle, path):
+    """Packed sequences with the step preprocessed in the kernels."""
+    name, H, P, G, N, Q, dtype = path
+    lengths = MIXES["edges"]
+    d = synth.make_varlen(lengths, H, P, G, N, dtype, seed=740)
+    raw, dt_bias = synth.make_dt_raw((sum(lengths),), H, seed=741)
+    init = synth.make_state(len(lengths), H, P, N, seed=742, scale=0.5)
+    dd = dev(d)
+    announce("varlen dt_raw", name)
+    y, fs = bd.ssd_prefill_varlen(dd["x"], raw.cuda(), dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], dd["cu_seqlens"],
+                                  init.cuda(), Q=Q, dt_raw=True, dt_bias=dt_bias.cuda(), dt_min=1e-3, dt_max=0.1)
+    torch.cuda.synchronize()
+    dt_ref = oracle.dt_from_raw(raw, dt_bias, 1e-3, 0.1)
+    y_ref, fs_ref = oracle.ssd_scan_varlen(d["x"], dt_ref, d["A_log"], d["Bm"], d["Cm"], d["cu_seqlens"], d["D"], init)
+    assert rel_err(y, y_ref) <= _tol(dtype)
+    assert rel_err(fs, fs_ref) <= _tol(dtype)
