@@ -6,7 +6,9 @@
 // sequence's initial state, as the chunked form of the bqwf.cn article on
 // the compiler-first Mamba-2 implementation, §1.1, does per sequence).  One
 // workgroup lays the chunks of all sequences out in consecutive slots: an
-// exclusive scan of the chunk counts gives each sequence its first slot.
+// exclusive scan of the chunk counts gives each sequence its first slot, and
+// each wave then writes the entries of a share of the sequences, one entry
+// per lane.
 // Offsets are clamped to [0, T] and a negative length counts as empty, and
 // slots never exceed the bound the workspace was sized for, so offsets that
 // break the documented contract give unspecified results but every access
@@ -34,6 +36,7 @@ __device__ __forceinline__ long long wave_inclusive_sum_ll(long long v) {
 __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(PrefillArgs a, ChunkEntry *chunks, SeqEntry *seqs) {
     __shared__ long long wsum[kTabThreads / 64];
     __shared__ long long carry;
+    __shared__ SeqEntry pass_seq[kTabThreads];  // this pass's sequences, for the entry writers
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const long long slots = a.nchunks;
     if (tid == 0) carry = 0;
@@ -56,13 +59,21 @@ __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(PrefillArgs a,
         if (b < a.B) {
             const long long f0 = min(first, slots);
             const int cnt = (int)min(n, slots - f0);
-            seqs[b] = SeqEntry{(int)f0, cnt, start, len};
-            for (int c = 0; c < cnt; ++c)
-                chunks[f0 + c] = ChunkEntry{b, c, start + c * a.Q, min(a.Q, len - c * a.Q)};
+            const SeqEntry e{(int)f0, cnt, start, len};
+            seqs[b] = e;
+            pass_seq[tid] = e;
         }
-        __syncthreads();  // every thread has read carry
+        __syncthreads();  // every thread has read carry; pass_seq is complete
+        // the chunk entries: wave w writes those of the pass's sequences w,
+        // w + 16, ..., one entry per lane at a time
+        const int nb = min(kTabThreads, a.B - b0);
+        for (int j = wave; j < nb; j += kTabThreads / 64) {
+            const SeqEntry e = pass_seq[j];
+            for (int c = lane; c < e.n; c += 64)
+                chunks[(long long)e.f0 + c] = ChunkEntry{b0 + j, c, e.tok0 + c * a.Q, min(a.Q, e.len - c * a.Q)};
+        }
         if (tid == kTabThreads - 1) carry = first + n;
-        __syncthreads();
+        __syncthreads();  // carry is updated; pass_seq may be rewritten
     }
     const long long used = min(carry, slots);
     for (long long f = used + tid; f < slots; f += kTabThreads) chunks[f] = ChunkEntry{0, 0, 0, 0};
