@@ -107,6 +107,23 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+def measured_mfma(workload):
+    """Executed MFMA flops per launch of each prefill kernel, from a committed
+    rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 run on `workload`
+    (profiles/mfma_prefill_<workload>.json, written by
+    mamba_ssd_scan_chunk_amd.profiling), or {} if absent, taken on another
+    workload or on kernel sources that have changed since."""
+    from mamba_ssd_scan_chunk_amd.profiling import source_hash
+
+    path = os.path.join(PROFILES, f"mfma_prefill_{workload.replace('-prefill', '')}.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    if rec.get("workload") != workload or not rec.get("sources") or rec.get("source_hash") != source_hash(rec["sources"]):
+        return {}
+    return {k: v["flops"] for k, v in rec["kernels"].items()}
+
+
 HOST_BOUND = []
 
 
@@ -507,7 +524,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip every leg but the prefill")
     ap.add_argument("--legs", default="prefill,decode,conv,norm,varlen,other",
-                    help="comma-separated subset of prefill,decode,conv,norm,varlen,other,copy (for profiling runs)")
+                    help="comma-separated subset of prefill,decode,conv,norm,varlen,other, and the calibration "
+                         "legs copy and gemm (for profiling runs)")
     ap.add_argument("--no-decode-extras", action="store_true",
                     help="decode leg: only the stated workload's one-state and rotated-state runs (no other batch, "
                          "raw-step or recompute legs), so that every decode dispatch has the same size")
@@ -544,6 +562,8 @@ def main():
         out.update(bench_other_prefills(args))
     if "copy" in legs:
         out.update(copy_record(args))
+    if "gemm" in legs:
+        out.update(gemm_record(args))
     if HOST_BOUND:
         out["host_bound_legs"] = HOST_BOUND
     if not args.no_cpu_baseline:
@@ -557,10 +577,16 @@ def prefill_record(args):
     tflops = flops / (ms * 1e-3) / 1e12
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/B
     stage_rec = {}
+    counted = measured_mfma(w.name)
     for name, sms in stages.items():
         sb, sf = stage_work(name, w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
         stage_rec[name] = {"us": round(sms * 1e3, 2), "algorithmic_mb": round(sb / 1e6, 2),
                            "gbs": round(sb / (sms * 1e-3) / 1e9, 1), "tflops": round(sf / (sms * 1e-3) / 1e12, 2)}
+        if name in counted:
+            # flops the MFMA units executed (rocprofv3 counter, padding included) over this run's duration
+            stage_rec[name]["mfma_counted_gflop"] = round(counted[name] / 1e9, 3)
+            stage_rec[name]["mfma_counted_peak_frac"] = round(
+                counted[name] / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
     dom = max(stages, key=stages.get)
     db, dfl = stage_work(dom, w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
     dt_s = stages[dom] * 1e-3
@@ -612,6 +638,23 @@ def copy_record(args):
     ms = _timed(lambda _: torch.neg(src, out=dst), max(3, min(args.steps, 20)), 2, "copy")
     return {"copy": {"bytes_read": 4 * n, "bytes_written": 4 * n, "us": round(ms * 1e3, 2),
                      "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}}
+
+
+def gemm_record(args):
+    """A plain library GEMM of known flops, the reference for rocprofv3's MFMA
+    counters: torch.matmul of two contiguous 8192 x 8192 bf16 matrices
+    (2 * 8192^3 flops, no padding), timed like the other legs."""
+    import torch
+
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda", generator=g).contiguous()
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda", generator=g).contiguous()
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    ms = _timed(lambda _: torch.matmul(a, b, out=c), max(3, min(args.steps, 10)), 2, "gemm")
+    flops = 2 * n ** 3
+    return {"gemm": {"m": n, "n": n, "k": n, "flops": flops, "us": round(ms * 1e3, 2),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}}
 
 
 def cached_vs_recompute(args, cached_step_ms):

@@ -10,8 +10,16 @@
         counters of that plain 256 MiB read + 256 MiB write (torch.neg)
         calibrate both counters to bytes.
 
-bench.py reads the traffic files and reports their bytes only while the
-kernel sources still hash to the recorded value.
+    python -m mamba_ssd_scan_chunk_amd.profiling mfma --pmc DIR --stats DIR --kernels K1 K2 ... \
+            --command-pmc "..." --command-stats "..." --out profiles/mfma_NAME.json > profiles/mfma_NAME.md
+        MFMA work and utilisation per kernel from a `rocprofv3 --pmc
+        SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES ...` run and a
+        kernel-trace run of the same command, which also runs bench.py's gemm
+        leg: that bf16 GEMM of known flops checks the counter's unit (512 flops
+        per MOP) and shows what a library GEMM reaches by the same measure.
+
+bench.py reads the traffic and MFMA files and reports their figures only
+while the kernel sources still hash to the recorded value.
 """
 from __future__ import annotations
 
@@ -147,6 +155,70 @@ def cmd_traffic(a) -> int:
     return 0
 
 
+CLOCK_HZ = 2.4e9        # MI355X peak engine clock
+SIMDS = 256 * 4         # compute units x SIMDs per CU
+MOP_FLOPS = 512         # flops per unit of SQ_INSTS_VALU_MFMA_MOPS_*
+
+
+def kernel_durations_ns(d: str) -> dict:
+    """Average duration (ns) and call count per bare kernel name from a
+    `--kernel-trace --stats` run."""
+    out = {}
+    for r in csv.DictReader(open(_find(d, "kernel_stats.csv"))):
+        out[r["Name"]] = (float(r["AverageNs"]), int(r["Calls"]))
+    return out
+
+
+def cmd_mfma(a) -> int:
+    mops = counter_means(a.pmc, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy = counter_means(a.pmc, "SQ_VALU_MFMA_BUSY_CYCLES")
+    durs = kernel_durations_ns(a.stats)
+    peak = CLOCK_HZ * SIMDS * 1024  # flops/s: a 32x32x16 bf16 MFMA is 32768 flops in 32 cycles of one SIMD
+
+    def entry(pattern, exact):
+        km, kb, kd = _pick(mops, pattern, exact), _pick(busy, pattern, exact), _pick(durs, pattern, exact)
+        if not (km and kb and kd):
+            raise KeyError(f"{pattern}: seen {sorted(_short(k) for k in mops)}")
+        flops = mops[km][0] * MOP_FLOPS
+        dur = durs[kd][0] * 1e-9
+        return {"mops_bf16": mops[km][0], "flops": flops, "mfma_busy_cycles": busy[kb][0],
+                "avg_us": round(dur * 1e6, 3), "calls_traced": durs[kd][1], "dispatches_counted": mops[km][1],
+                "tflops": round(flops / dur / 1e12, 2),
+                "busy_frac": round(busy[kb][0] / (dur * CLOCK_HZ * SIMDS), 4),
+                "peak_frac": round(flops / dur / peak, 4)}
+
+    kernels = {k: entry(k, True) for k in a.kernels}
+    gemm = entry(a.gemm_kernel, False)
+    gemm["flops_expected"] = a.gemm_flops
+    sources = a.sources or []
+    rec = {"workload": a.workload, "kernels": kernels, "gemm_reference": gemm, "peak_tflops": peak / 1e12,
+           "clock_hz": CLOCK_HZ, "simds": SIMDS,
+           "commands": {"pmc": a.command_pmc, "stats": a.command_stats},
+           "sources": sources, "source_hash": source_hash(sources)}
+    with open(a.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(f"# rocprofv3 MFMA counters: {a.title}\n")
+    print("Commands (from the repository root on an MI355X):\n")
+    print(f"```\n{a.command_pmc}\n{a.command_stats}\n```\n")
+    print("Executed MFMA flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 per dispatch; the MFMA busy fraction is "
+          f"SQ_VALU_MFMA_BUSY_CYCLES / (average kernel-trace duration x {CLOCK_HZ / 1e9:g} GHz x {SIMDS} SIMDs); "
+          f"the peak is {peak / 1e12:.0f} TFLOP/s (listed by AMD as 2.5 PFLOP/s).\n")
+    print("| Kernel | MOPS_BF16 per dispatch | Executed GFLOP | MFMA busy cycles (sum over SIMDs) | "
+          "Average duration (us) | TFLOP/s | MFMA busy | Share of the bf16 peak |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name, e in list(kernels.items()) + [(f"{a.gemm_kernel}... (torch.matmul, reference)", gemm)]:
+        print(f"| {name} | {e['mops_bf16']:.0f} | {e['flops'] / 1e9:.3f} | {e['mfma_busy_cycles']:.0f} | "
+              f"{e['avg_us']:.2f} | {e['tflops']:.1f} | {100 * e['busy_frac']:.1f}% | {100 * e['peak_frac']:.1f}% |")
+    tot_f = sum(e["flops"] for e in kernels.values())
+    tot_t = sum(e["avg_us"] for e in kernels.values()) * 1e-6
+    print(f"\nAll listed kernels together: {tot_f / 1e9:.3f} GFLOP executed in {tot_t * 1e6:.1f} us of kernel time, "
+          f"{tot_f / tot_t / 1e12:.1f} TFLOP/s = {100 * tot_f / tot_t / peak:.1f}% of the peak.")
+    print(f"\nGEMM reference: counted {gemm['flops']:.6g} flops against 2 x {a.gemm_n}^3 = {a.gemm_flops:.6g} "
+          f"(ratio {gemm['flops'] / a.gemm_flops:.6f}).")
+    return 0
+
+
 def cmd_stats(a) -> int:
     rows = list(csv.DictReader(open(_find(a.dir, "kernel_stats.csv"))))
     print(f"# rocprofv3 kernel statistics: {a.title}\n")
@@ -177,7 +249,22 @@ def main(argv=None) -> int:
     st.add_argument("dir")
     st.add_argument("--title", default="")
     st.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True)
+    m.add_argument("--stats", required=True)
+    m.add_argument("--kernels", nargs="+", required=True)
+    m.add_argument("--gemm-kernel", default="Cijk_", help="substring naming the gemm leg's library kernel")
+    m.add_argument("--gemm-n", type=int, default=8192)
+    m.add_argument("--workload", required=True, help="bench.py workload name the counters were taken on")
+    m.add_argument("--title", default="")
+    m.add_argument("--command-pmc", default="")
+    m.add_argument("--command-stats", default="")
+    m.add_argument("--sources", nargs="*")
+    m.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "mfma":
+        a.gemm_flops = 2 * a.gemm_n ** 3
+        return cmd_mfma(a)
     return cmd_traffic(a) if a.cmd == "traffic" else cmd_stats(a)
 
 
