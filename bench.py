@@ -127,39 +127,68 @@ def measured_mfma(workload):
 HOST_BOUND = []
 
 
+HOT_MS = 50.0  # GPU work run right before a timed region, so that it starts at sustained clocks
+
+
 def _timed(fn, steps, warmup, name):
-    """GPU ms per call over ``steps`` back-to-back calls.  A GPU sleep sized
-    to the measured host enqueue time keeps the device busy until the whole
-    sequence is queued, so host launch overhead stays out of the figure."""
+    """GPU ms per call over ``steps`` back-to-back calls, none of which may
+    wait for the host.
+
+    A leg whose host enqueue per call is well below its GPU time gets a head
+    start: about HOT_MS of untimed calls enqueued right before the timed ones,
+    so the GPU is busy, and at the clocks it holds under sustained load, when
+    timing starts (after an idle gap the first tens of milliseconds run a few
+    percent slower).  A leg that is not (many tiny launches) instead waits
+    behind a GPU sleep sized to the measured host enqueue time, so that the
+    whole sequence is queued before the first timed call starts."""
     import torch
 
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
+    n0 = min(steps, 64)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
     t0 = time.perf_counter()
-    for i in range(min(steps, 64)):
+    for i in range(n0):
         fn(i)
-    per_call = (time.perf_counter() - t0) / min(steps, 64)
+    per_call = (time.perf_counter() - t0) / n0
+    p1.record()
     torch.cuda.synchronize()
-    # calibrate the sleep kernel's clock
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    torch.cuda._sleep(1_000_000)
-    s1.record()
-    torch.cuda.synchronize()
-    cyc_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
-    sleep_ms = 1.5 * per_call * steps * 1e3 + 5.0
+    gpu_call_ms = p0.elapsed_time(p1) / n0
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(sleep_ms * cyc_per_ms))
-    start.record()
-    h0 = time.perf_counter()
-    for i in range(steps):
-        fn(i)
-    host_ms = (time.perf_counter() - h0) * 1e3
-    end.record()
-    torch.cuda.synchronize()
-    gpu_ms = start.elapsed_time(end)
-    if host_ms > sleep_ms:
+    if per_call * 1e3 < 0.7 * gpu_call_ms:
+        n_pre = int(min(max(HOT_MS / gpu_call_ms, 16), 20000))
+        for i in range(n_pre):
+            fn(i)
+        start.record()
+        h0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        host_ms = (time.perf_counter() - h0) * 1e3
+        end.record()
+        torch.cuda.synchronize()
+        gpu_ms = start.elapsed_time(end)
+        covered_ms = n_pre * gpu_call_ms + gpu_ms  # the queue ran dry only if the host took longer
+    else:
+        # calibrate the sleep kernel's clock
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        torch.cuda._sleep(1_000_000)
+        s1.record()
+        torch.cuda.synchronize()
+        cyc_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
+        covered_ms = 1.5 * per_call * steps * 1e3 + 5.0
+        torch.cuda._sleep(int(covered_ms * cyc_per_ms))
+        start.record()
+        h0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        host_ms = (time.perf_counter() - h0) * 1e3
+        end.record()
+        torch.cuda.synchronize()
+        gpu_ms = start.elapsed_time(end)
+    if host_ms > covered_ms:
         if name not in HOST_BOUND:
             HOST_BOUND.append(name)
     return gpu_ms / steps
@@ -199,13 +228,14 @@ def bench_prefill(args):
     flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, w.Q)
     nbytes = prefill_bytes(w.B, w.L, w.H, w.P, w.G, w.N, 2 if w.dtype == "bf16" else 4)
     # per-kernel durations: HIP events the library records between its
-    # kernels on the call's stream; each sample is the last of four
-    # back-to-back calls, so the queue is busy as in the timed loop
+    # kernels on the call's stream; each sample is the last of about HOT_MS
+    # of back-to-back calls, so the GPU is busy as in the timed loop
     bd.stage_timing(True)
     stages = {}
+    n_hot = int(min(max(HOT_MS / (ms if ms > 0 else 1.0), 4), 5000))
     try:
         for _ in range(args.stage_runs):
-            for _ in range(4):
+            for _ in range(n_hot):
                 step(0)
             for name, kms in bd.stage_times():
                 stages.setdefault(name, []).append(kms)
@@ -274,10 +304,16 @@ def _graph_timed(fn, steps, reps=3):
     with torch.cuda.graph(g):
         for i in range(steps):
             fn(i)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
     g.replay()
+    p1.record()
     torch.cuda.synchronize()
+    n_pre = int(min(max(HOT_MS / max(p0.elapsed_time(p1), 1e-3), 1), 1000))
     best = float("inf")
     for _ in range(reps):
+        for _ in range(n_pre):  # untimed replays: the timed one starts on a busy GPU
+            g.replay()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         g.replay()
