@@ -17,8 +17,10 @@ C*B^T (.) decay * X, chunk states, the chunk-to-chunk state pass, C*h + D*x).
   * cpu_baseline: the CPU oracle on the same prefill workload.
 Inputs are seeded synthetic tensors (mamba_ssd_scan_chunk_amd.synth), resident
 in device memory before timing starts.  GPU times come from HIP events on the
-stream the kernels run on, with the queue pre-filled behind a short GPU sleep
-so that host launch overhead is not timed.
+stream the kernels run on.  Host launch overhead is kept out of the timed
+region: device-bound legs are timed right after about 50 ms of untimed calls
+(so the GPU is busy and at its sustained clocks when timing starts), legs of
+many tiny launches behind a GPU sleep sized to their host enqueue time.
 """
 from __future__ import annotations
 
