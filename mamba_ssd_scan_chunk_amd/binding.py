@@ -99,6 +99,55 @@ def _dense(t, name):
     return t
 
 
+def _want(t, name, shape, dtype, device):
+    """Raise unless t is None or a dense tensor of this shape and dtype on
+    this device.  The C ABI receives bare pointers and cannot see buffer
+    sizes, so a tensor of the wrong size or type would be read or written
+    out of bounds by the kernels: every tensor is checked here first."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _want_workspace(ws, need, device):
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.dim() != 1 or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+
+
+def _want_rows(t, name, rows, cols, dtype, device, stride):
+    """x_t / B_t / C_t of a decode step: [rows, cols] with row stride
+    ``stride`` elements (0: dense) and contiguous columns."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if stride == 0:
+        if not t.is_contiguous() or t.numel() != rows * cols:
+            raise ValueError(f"{name} must be dense with {rows}x{cols} elements when in_stride is 0")
+        return
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} must be a [{rows}, {cols}] view when in_stride is set, got {tuple(t.shape)}")
+    if t.stride(1) != 1 or (rows > 1 and t.stride(0) != stride):
+        raise ValueError(f"{name} must have row stride {stride} and contiguous columns, got strides {t.stride()}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -124,17 +173,28 @@ def ssd_prefill(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y=None,
     Bm/Cm [B,L,G,N], D [H] f32 or None, init_state [B,H,P,N] f32 or None.
     With ``dt_raw`` the kernels use clamp(softplus(dt + dt_bias), dt_min,
     dt_max) as the step (ssd_prefill_dt_raw).  Returns (y, final_state)."""
-    for t, n in ((x, "x"), (dt, "dt"), (A_log, "A_log"), (Bm, "Bm"), (Cm, "Cm"), (D, "D"),
-                 (init_state, "init_state"), (y, "y"), (final_state, "final_state"), (dt_bias, "dt_bias")):
-        _dense(t, n)
+    if x.dim() != 4 or Bm.dim() != 4:
+        raise ValueError("x must be [B,L,H,P] and Bm [B,L,G,N]")
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
     code = _dtype_code(x)
+    f32, dv = torch.float32, x.device
+    _want(x, "x", (B, L, H, P), x.dtype, dv)
+    _want(dt, "dt", (B, L, H), f32, dv)
+    _want(A_log, "A_log", (H,), f32, dv)
+    _want(Bm, "Bm", (B, L, G, N), x.dtype, dv)
+    _want(Cm, "Cm", (B, L, G, N), x.dtype, dv)
+    _want(D, "D", (H,), f32, dv)
+    _want(init_state, "init_state", (B, H, P, N), f32, dv)
+    _want(y, "y", (B, L, H, P), x.dtype, dv)
+    _want(final_state, "final_state", (B, H, P, N), f32, dv)
+    _want(dt_bias, "dt_bias", (H,), f32, dv)
+    need = ssd_prefill_workspace_bytes(B, L, H, P, G, N, Q, code)
+    _want_workspace(workspace, need, dv)
     if y is None:
         y = torch.empty_like(x)
     if final_state is None and want_final_state:
         final_state = torch.empty((B, H, P, N), dtype=torch.float32, device=x.device)
-    need = ssd_prefill_workspace_bytes(B, L, H, P, G, N, Q, code)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -160,18 +220,28 @@ def ssd_prefill_varlen(x, dt, A_log, Bm, Cm, D, cu_seqlens, init_state=None, *, 
     cu_seqlens[b] .. cu_seqlens[b+1]).  init_state / final_state [B,H,P,N].
     With ``dt_raw`` the step is clamp(softplus(dt + dt_bias), dt_min, dt_max)
     (ssd_prefill_varlen_dt_raw).  Returns (y [T,H,P], final_state)."""
-    for t, n in ((x, "x"), (dt, "dt"), (A_log, "A_log"), (Bm, "Bm"), (Cm, "Cm"), (D, "D"),
-                 (init_state, "init_state"), (y, "y"), (final_state, "final_state"), (cu_seqlens, "cu_seqlens"),
-                 (dt_bias, "dt_bias")):
-        _dense(t, n)
     if dt_bias is not None and not dt_raw:
         raise ValueError("dt_bias is used only with dt_raw=True")
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    if x.dim() != 3 or Bm.dim() != 3 or cu_seqlens.dim() != 1:
+        raise ValueError("x must be [T,H,P], Bm [T,G,N] and cu_seqlens [B+1]")
     T, H, P = x.shape
     G, N = Bm.shape[1], Bm.shape[2]
     B = cu_seqlens.numel() - 1
     code = _dtype_code(x)
+    f32, dv = torch.float32, x.device
+    _want(x, "x", (T, H, P), x.dtype, dv)
+    _want(dt, "dt", (T, H), f32, dv)
+    _want(A_log, "A_log", (H,), f32, dv)
+    _want(Bm, "Bm", (T, G, N), x.dtype, dv)
+    _want(Cm, "Cm", (T, G, N), x.dtype, dv)
+    _want(D, "D", (H,), f32, dv)
+    _want(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32, dv)
+    _want(init_state, "init_state", (B, H, P, N), f32, dv)
+    _want(y, "y", (T, H, P), x.dtype, dv)
+    _want(final_state, "final_state", (B, H, P, N), f32, dv)
+    _want(dt_bias, "dt_bias", (H,), f32, dv)
     if y is None:
         y = torch.empty_like(x)
     if final_state is None:
@@ -179,6 +249,7 @@ def ssd_prefill_varlen(x, dt, A_log, Bm, Cm, D, cu_seqlens, init_state=None, *, 
     nws = lib().ssd_prefill_varlen_workspace_bytes(B, T, H, P, G, N, Q, code)
     if nws == ctypes.c_size_t(-1).value:
         raise ValueError("ssd_prefill_varlen would reject these arguments")
+    _want_workspace(workspace, nws, dv)
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -205,17 +276,38 @@ def ssd_decode_step(x_t, dt_t, A_log, B_t, C_t, D, ssm_state, *, y_t=None, in_st
     x_t [B,H*P], dt_t [B,H], B_t/C_t [B,G*N] (or views into one [B,C] row with
     ``in_stride`` = C).  With ``dt_raw`` the step is clamp(softplus(dt_t +
     dt_bias), dt_min, dt_max) (ssd_decode_step_dt_raw).  Returns y_t [B,H,P]."""
+    if ssm_state.dim() != 4:
+        raise ValueError("ssm_state must be [B,H,P,N]")
     Bsz, H_, P_, N_ = ssm_state.shape
-    H, P, N = H or H_, P or P_, N or N_
-    G = G or (B_t.shape[-1] // N if in_stride == 0 else None)
+    if (H or H_, P or P_, N or N_) != (H_, P_, N_):
+        raise ValueError(f"H, P, N given as {(H, P, N)} but ssm_state is {tuple(ssm_state.shape)}")
+    H, P, N = H_, P_, N_
+    G = G or (B_t.numel() // (Bsz * N) if in_stride == 0 else None)
     if G is None:
         raise ValueError("G must be given when in_stride is set")
-    _dense(ssm_state, "ssm_state")
     code = _dtype_code(x_t)
+    f32, dv, adt = torch.float32, x_t.device, x_t.dtype
+    stride = int(in_stride)
+    _want_rows(x_t, "x_t", Bsz, H * P, adt, dv, stride)
+    _want_rows(B_t, "B_t", Bsz, G * N, adt, dv, stride)
+    _want_rows(C_t, "C_t", Bsz, G * N, adt, dv, stride)
+    _want(dt_t, "dt_t", (Bsz, H), f32, dv)
+    _want(A_log, "A_log", (H,), f32, dv)
+    _want(D, "D", (H,), f32, dv)
+    _want(ssm_state, "ssm_state", (Bsz, H, P, N), f32, dv)
+    _want(y_t, "y_t", (Bsz, H, P), adt, dv)
+    _want(dt_bias, "dt_bias", (H,), f32, dv)
+    if conv_state_in is not None:
+        C = H * P + 2 * G * N
+        _want(conv_state_in, "conv_state_in", (Bsz, C, int(K) - 1), adt, dv)
+        if conv_state_out is None or conv_w is None:
+            raise ValueError("conv_state_out and conv_w are needed with conv_state_in")
+        _want(conv_state_out, "conv_state_out", (Bsz, C, int(K) - 1), adt, dv)
+        _want(conv_w, "conv_w", (C, int(K)), adt, dv)
+        _want(conv_b, "conv_b", (C,), adt, dv)
     if y_t is None:
         y_t = torch.empty((Bsz, H, P), dtype=x_t.dtype, device=x_t.device)
     if dt_raw:
-        _dense(dt_bias, "dt_bias")
         rc = lib().ssd_decode_step_dt_raw(Bsz, H, P, G, N, code, _ptr(x_t), _ptr(dt_t), _ptr(dt_bias),
                                           float(dt_min), float(dt_max), _ptr(A_log), _ptr(B_t), _ptr(C_t),
                                           _ptr(D), _ptr(ssm_state), _ptr(y_t), int(in_stride),
@@ -237,11 +329,17 @@ def conv_state_update(conv_state, xBC, conv_w, conv_b=None, *, activation=0, out
                       want_out=True, stream=None):
     """Depthwise causal conv over T tokens; conv_state [B,C,K-1] updated in
     place.  xBC [B,T,C], conv_w [C,K].  Returns out [B,T,C] (or None)."""
-    for t, n in ((conv_state, "conv_state"), (xBC, "xBC"), (conv_w, "conv_w"), (conv_b, "conv_b"), (out, "out")):
-        _dense(t, n)
+    if conv_state.dim() != 3 or xBC.dim() != 3:
+        raise ValueError("conv_state must be [B,C,K-1] and xBC [B,T,C]")
     B, C, Km1 = conv_state.shape
     T = xBC.shape[1]
     code = _dtype_code(conv_state)
+    adt, dv = conv_state.dtype, conv_state.device
+    _want(conv_state, "conv_state", (B, C, Km1), adt, dv)
+    _want(xBC, "xBC", (B, T, C), adt, dv)
+    _want(conv_w, "conv_w", (C, Km1 + 1), adt, dv)
+    _want(conv_b, "conv_b", (C,), adt, dv)
+    _want(out, "out", (B, T, C), adt, dv)
     if out is None and want_out:
         out = torch.empty_like(xBC)
     rc = lib().conv_state_update(B, T, C, Km1 + 1, code, _ptr(conv_state), _ptr(xBC), _ptr(conv_w),
@@ -282,9 +380,9 @@ def ssd_gated_rmsnorm(y, z=None, norm_w=None, *, group, eps=1e-5, out=None, stre
         z_stride = _row_stride(z, D, "z")
     if norm_w is not None and (norm_w.dtype != torch.float32 or tuple(norm_w.shape) != (D,)):
         raise ValueError("norm_w must be fp32 [D]")
+    _want(out, "out", tuple(y.shape), y.dtype, y.device)
     if out is None:
         out = torch.empty_like(y)
-    _dense(out, "out")
     rc = lib().ssd_gated_rmsnorm(rows, D, int(group), _dtype_code(y), _ptr(y), _ptr(z), z_stride, _ptr(norm_w),
                                  float(eps), _ptr(out), _stream(stream))
     _check("ssd_gated_rmsnorm", rc)
@@ -296,17 +394,24 @@ def conv_state_update_varlen(conv_state, xBC, cu_seqlens, conv_w, conv_b=None, *
     """conv_state_update over packed sequences: xBC [T,C], cu_seqlens [B+1]
     int32 on the GPU, conv_state [B,C,K-1] updated in place.  Returns out
     [T,C] (or None)."""
-    for t, n in ((conv_state, "conv_state"), (xBC, "xBC"), (conv_w, "conv_w"), (conv_b, "conv_b"), (out, "out"),
-                 (cu_seqlens, "cu_seqlens")):
-        _dense(t, n)
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    if conv_state.dim() != 3 or xBC.dim() != 2:
+        raise ValueError("conv_state must be [B,C,K-1] and xBC [T,C]")
     B, C, Km1 = conv_state.shape
     T = xBC.shape[0]
     code = _dtype_code(conv_state)
+    adt, dv = conv_state.dtype, conv_state.device
+    _want(conv_state, "conv_state", (B, C, Km1), adt, dv)
+    _want(xBC, "xBC", (T, C), adt, dv)
+    _want(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32, dv)
+    _want(conv_w, "conv_w", (C, Km1 + 1), adt, dv)
+    _want(conv_b, "conv_b", (C,), adt, dv)
+    _want(out, "out", (T, C), adt, dv)
     if out is None and want_out:
         out = torch.empty_like(xBC)
     nws = lib().conv_state_update_varlen_workspace_bytes(B, T)
+    _want_workspace(workspace, nws, dv)
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=xBC.device)
     rc = lib().conv_state_update_varlen(B, T, C, Km1 + 1, code, _ptr(cu_seqlens), _ptr(conv_state), _ptr(xBC),
