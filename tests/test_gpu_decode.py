@@ -131,18 +131,31 @@ def test_decode_dense_separate_inputs(oracle, dtype):
     assert rel_err(state, st_ref) <= TOL_STATE
 
 
+# (batch, sampled (b, h) pairs).  B = 2 runs the 16-row workgroup instance of
+# the decode kernel (B*H*ceil(P/64) = 160 < 1024 blocks); B = 16, the batch
+# the decode bench times, runs the 64-row instance (1280 blocks), whose pairs
+# include heads in the first and the last workgroup of each batch element's
+# group, the first and the last batch element, and workgroups on each of the
+# eight XCDs (workgroup b*80 + h runs on XCD h mod 8).
+DECODE_4096 = [
+    (2, [(0, 0), (0, 37), (1, 79), (1, 5)]),
+    (16, [(0, 0), (0, 79), (3, 41), (7, 78), (8, 2), (11, 61), (15, 79), (15, 0), (5, 11), (12, 68)]),
+]
+
+
 @pytest.mark.parametrize("variant", ["spec", "slow"])
-def test_decode_4096_steps_2p7b_shape(oracle, variant):
+@pytest.mark.parametrize("B,pairs", DECODE_4096, ids=["b2", "b16"])
+def test_decode_4096_steps_2p7b_shape(oracle, variant, B, pairs):
     """4096 consecutive fused decode steps of a 2.7B-shaped layer (H=80, P=64,
     N=128, conv C=5376, K=4, bf16 activations, fp32 state).  The oracle starts
     from the same initial state bits and replays the same raw tokens for
     sampled (batch, head) pairs; the final fp32 state must agree to 1e-5."""
-    B, H, P, G, N, K, steps = 2, 80, 64, 1, 128, 4, 4096
+    H, P, G, N, K, steps = 80, 64, 1, 128, 4, 4096
     w_ = synth.WORKLOADS["mamba2-2.7b-decode-b16"]
     assert (w_.H, w_.P, w_.N, w_.conv_channels) == (H, P, N, 5376)
-    s = _setup(B, H, P, G, N, K, "bf16", steps, seed=300 + (variant == "slow"), variant=variant)
+    s = _setup(B, H, P, G, N, K, "bf16", steps, seed=300 + (variant == "slow") + 2 * (B == 16), variant=variant)
     C = s["C"]
-    announce("decode 4096", variant)
+    announce("decode 4096", variant, f"B={B}")
     state = s["state0"].cuda()
     cin = torch.zeros_like(s["conv0"]).cuda()
     cout = torch.empty_like(cin)
@@ -158,7 +171,7 @@ def test_decode_4096_steps_2p7b_shape(oracle, variant):
     torch.cuda.synchronize()
     # oracle: conv over the whole token stream (a FIR, so equal to stepping),
     # then the recurrence for sampled heads from the same initial state
-    for b, h in [(0, 0), (0, 37), (1, 79), (1, 5)]:
+    for b, h in pairs:
         stream = s["xbc"][:, b:b + 1, :].transpose(0, 1)  # [1, steps, C]
         _, out = oracle.conv_update(np.zeros((1, C, K - 1)), stream, s["w"], None, True)
         xs = out[:, :, h * P:(h + 1) * P].reshape(1, steps, 1, P)
@@ -247,3 +260,48 @@ def test_conv_cache_only(oracle):
     assert bd.conv_state_update(st, xbc.cuda(), w.cuda(), want_out=False) is None
     torch.cuda.synchronize()
     np.testing.assert_array_equal(f64(st), f64(xbc.transpose(1, 2)))
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_cache_save_restore_continues_bit_for_bit(B):
+    """The O(1) cache (ssm_state and conv_state) is the whole state of a
+    generation: copied to the host after k decode steps, restored into fresh
+    device buffers and continued for m more steps, it gives the outputs and
+    the final cache of the uninterrupted k + m steps bit for bit (the
+    functional cache and its update of bqwf.cn article §2.1-§2.2)."""
+    H, P, G, N, K, k, m = 80, 64, 1, 128, 4, 7, 9
+    s = _setup(B, H, P, G, N, K, "bf16", k + m, seed=340 + B)
+    C = s["C"]
+    xbc, dts = s["xbc"].cuda(), s["dts"].cuda()
+    w, A_log, D = s["w"].cuda(), s["A_log"].cuda(), s["D"].cuda()
+
+    def steps(state, cin, cout, t0, t1, ys):
+        for t in range(t0, t1):
+            row = xbc[t]
+            bd.ssd_decode_step(row[:, :H * P], dts[t], A_log, row[:, H * P:H * P + N], row[:, H * P + N:], D,
+                               state, y_t=ys[t], in_stride=C, G=G, conv_state_in=cin, conv_state_out=cout,
+                               conv_w=w, K=K, activation=1)
+            cin, cout = cout, cin
+        return cin, cout
+
+    announce("decode save/restore", f"B={B}")
+    ys_a = torch.empty((k + m, B, H, P), dtype=torch.bfloat16, device="cuda")
+    st_a = s["state0"].cuda()
+    cin_a, _ = steps(st_a, s["conv0"].cuda(), torch.empty_like(s["conv0"]).cuda(), 0, k + m, ys_a)
+
+    ys_b = torch.empty_like(ys_a)
+    st_b = s["state0"].cuda()
+    cin_b, _ = steps(st_b, s["conv0"].cuda(), torch.empty_like(s["conv0"]).cuda(), 0, k, ys_b)
+    torch.cuda.synchronize()
+    saved_state, saved_conv = st_b.cpu(), cin_b.cpu()  # the whole cache, on the host
+    del st_b, cin_b
+    torch.cuda.synchronize()
+    st_c = torch.empty((B, H, P, N), dtype=torch.float32, device="cuda")
+    st_c.copy_(saved_state)
+    cin_c = torch.empty_like(s["conv0"]).cuda()
+    cin_c.copy_(saved_conv)
+    cin_c, _ = steps(st_c, cin_c, torch.empty_like(cin_c), k, k + m, ys_b)
+    torch.cuda.synchronize()
+    assert torch.equal(ys_b, ys_a)
+    assert torch.equal(st_c, st_a)
+    assert torch.equal(cin_c, cin_a)

@@ -2,14 +2,16 @@
 
 Each graph is captured once and replayed several times, with the program's
 own eager work and synchronisations between replays; every replay must equal
-the eager result bit for bit (the kernels are deterministic).
+the eager result bit for bit (the kernels are deterministic) and the CPU
+oracle's result within the tolerance of its dtype.
 """
+import numpy as np
 import pytest
 import torch
 
 from mamba_ssd_scan_chunk_amd import binding as bd
 from mamba_ssd_scan_chunk_amd import synth
-from tests.gpu_utils import announce
+from tests.gpu_utils import TOL_BF16, TOL_STATE, announce, f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -35,9 +37,26 @@ def _run_steps(s, state, conv, ys):
                            activation=1)
 
 
-def test_decode_loop_graph_replays_match_eager():
+def _decode_oracle(oracle, s):
+    """The oracle's run of the same steps: outputs [steps, B, H, P], the
+    final state and the final conv window."""
+    H, P, G, N, C = s["H"], s["P"], s["G"], s["N"], s["C"]
+    xbc, dts = s["xbc"].cpu(), s["dts"].cpu()
+    st, cv = f64(s["state0"]), f64(s["conv0"])
+    ys = []
+    for i in range(s["steps"]):
+        r = xbc[i]
+        y, st, cv = oracle.decode_step(r[:, :H * P], dts[i], s["A_log"].cpu(), r[:, H * P:H * P + G * N],
+                                       r[:, H * P + G * N:], s["D"].cpu(), st, conv_state=cv,
+                                       conv_w=s["w"].cpu(), activation=True)
+        ys.append(y)
+    return np.stack(ys), st, cv
+
+
+def test_decode_loop_graph_replays_match_eager(oracle):
     s = _decode_setup()
     announce("graph decode")
+    ys_o, st_o, cv_o = _decode_oracle(oracle, s)
     ys_ref = torch.empty((s["steps"], s["B"], s["H"], s["P"]), dtype=torch.bfloat16, device="cuda")
     st_ref = s["state0"].clone()
     cv_ref = [s["conv0"].clone(), torch.empty_like(s["conv0"])]
@@ -70,12 +89,17 @@ def test_decode_loop_graph_replays_match_eager():
         assert torch.equal(state, st_ref), rep
         final = conv[s["steps"] & 1]
         assert torch.equal(final, cv_ref[s["steps"] & 1]), rep
+        assert rel_err(ys, ys_o) <= TOL_BF16, rep
+        assert rel_err(state, st_o) <= TOL_STATE, rep
+        np.testing.assert_array_equal(f64(final), cv_o)
 
 
-def test_prefill_graph_replays_match_eager():
+def test_prefill_graph_replays_match_eager(oracle):
     w = synth.WORKLOADS["mamba2-130m-prefill"]
-    d = {k: v.cuda() for k, v in synth.make_prefill(w.B, 1000, w.H, w.P, w.G, w.N, w.dtype, seed=75).items()}
+    dc = synth.make_prefill(w.B, 1000, w.H, w.P, w.G, w.N, w.dtype, seed=75)
+    d = {k: v.cuda() for k, v in dc.items()}
     announce("graph prefill")
+    y_o, fs_o = oracle.ssd_scan(dc["x"], dc["dt"], dc["A_log"], dc["Bm"], dc["Cm"], dc["D"])
     y_ref, fs_ref = bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=w.Q)
     torch.cuda.synchronize()
     y = torch.empty_like(y_ref)
@@ -105,6 +129,8 @@ def test_prefill_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), rep
         assert torch.equal(fs, fs_ref), rep
+        assert rel_err(y, y_o) <= TOL_BF16, rep
+        assert rel_err(fs, fs_o) <= TOL_BF16, rep
 
 
 def _capture(call):
@@ -119,18 +145,28 @@ def _capture(call):
     return g
 
 
-def test_packed_serving_graph_replays_match_eager():
+def test_packed_serving_graph_replays_match_eager(oracle):
     """conv over packed prompts, the packed prefill (its chunk tables built on
     the device inside the graph) and the gated normalisation of its output,
-    captured as one graph: every replay equals the eager result."""
+    captured as one graph: every replay equals the eager result, and the
+    oracle's conv, scan and normalisation (the last on the GPU's y, its
+    exact input)."""
     H, P, G, N, K = 4, 64, 1, 128, 4
     lengths = [300, 0, 1, 513, 40]
     T, C = sum(lengths), H * P + 2 * G * N
-    d = {k: v.cuda() for k, v in synth.make_varlen(lengths, H, P, G, N, "bf16", seed=76).items()}
-    xbc = synth.make_tokens(1, T, C, "bf16", seed=77)[0].cuda()
-    cw, cb = (t.cuda() for t in synth.make_conv(C, K, "bf16", seed=78, with_bias=True))
-    z, nw = (t.cuda() for t in synth.make_gate((T,), H * P, "bf16", seed=79))
-    cst0 = synth.make_tokens(len(lengths), K - 1, C, "bf16", seed=80).transpose(1, 2).contiguous().cuda()
+    dc = synth.make_varlen(lengths, H, P, G, N, "bf16", seed=76)
+    d = {k: v.cuda() for k, v in dc.items()}
+    xbc_c = synth.make_tokens(1, T, C, "bf16", seed=77)[0]
+    xbc = xbc_c.cuda()
+    cw_c, cb_c = synth.make_conv(C, K, "bf16", seed=78, with_bias=True)
+    cw, cb = cw_c.cuda(), cb_c.cuda()
+    z_c, nw_c = synth.make_gate((T,), H * P, "bf16", seed=79)
+    z, nw = z_c.cuda(), nw_c.cuda()
+    cst0_c = synth.make_tokens(len(lengths), K - 1, C, "bf16", seed=80).transpose(1, 2).contiguous()
+    cst0 = cst0_c.cuda()
+    cst_o, xc_o = oracle.conv_update_varlen(cst0_c, xbc_c, dc["cu_seqlens"], cw_c, cb_c, True)
+    y_o, fs_o = oracle.ssd_scan_varlen(dc["x"], dc["dt"], dc["A_log"], dc["Bm"], dc["Cm"], dc["cu_seqlens"],
+                                       dc["D"])
     cu = d["cu_seqlens"]
     B = len(lengths)
     cws = torch.empty(bd.lib().conv_state_update_varlen_workspace_bytes(B, T), dtype=torch.uint8, device="cuda")
@@ -166,3 +202,9 @@ def test_packed_serving_graph_replays_match_eager():
         torch.cuda.synchronize()
         for got, want in zip((cst, xc, y, fs, out), ref):
             assert torch.equal(got, want), rep
+        np.testing.assert_array_equal(f64(cst), cst_o)
+        assert rel_err(xc, xc_o) <= 8e-3, rep
+        assert rel_err(y, y_o) <= TOL_BF16, rep
+        assert rel_err(fs, fs_o) <= TOL_BF16, rep
+        out_o = oracle.gated_rmsnorm(y.reshape(T, H * P).cpu(), z_c, nw_c, group=H * P)
+        assert rel_err(out, out_o) <= 8e-3, rep
