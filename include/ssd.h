@@ -30,7 +30,8 @@
  *     row stride argument says otherwise.
  *   - Ownership: every pointer is a device pointer owned by the caller.  The
  *     library allocates nothing, frees nothing and keeps no pointer after the
- *     call returns.  Scratch memory is the caller's `workspace`.
+ *     call returns.  Scratch memory is the caller's `workspace` (except for
+ *     ssd_prefill_noalloc, which uses a fixed buffer of the library's own).
  *   - Asynchrony: calls only enqueue kernels on `stream` (0 = the null
  *     stream) and return without synchronising.  Results are valid once the
  *     caller has synchronised with the stream.
@@ -42,9 +43,10 @@
  *     next synchronisation, as for any HIP library.  No C++ exception crosses
  *     this interface.
  *   - Re-entrancy: no global mutable state apart from two per-host-thread
- *     records (the last HIP error and the optional stage timing below);
- *     calls on different streams may run concurrently as long as their
- *     buffers do not overlap.
+ *     records (the last HIP error and the optional stage timing below) and
+ *     the per-GPU scratch address of ssd_prefill_noalloc (set once per GPU
+ *     under a lock); calls on different streams may run concurrently as long
+ *     as their buffers do not overlap (ssd_prefill_noalloc: see there).
  *   - dtype: SSD_F32 or SSD_BF16, the storage type of the activations named
  *     "void*" below (x, Bm, Cm, y and the conv data).  dt, A_log, D and the
  *     SSM state are always fp32; all arithmetic accumulates in fp32 (the
@@ -72,7 +74,11 @@ enum {
     SSD_ERR_ALIGNMENT = -3,   /* a pointer or row stride breaks the documented alignment */
     SSD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query returned */
     SSD_ERR_HIP = -5,         /* a HIP call failed; see ssd_last_hip_error() */
+    SSD_ERR_TOO_LARGE = -6,   /* ssd_prefill_noalloc: the call needs more scratch than its fixed buffer */
 };
+
+/* Size of the fixed per-GPU scratch buffer of ssd_prefill_noalloc. */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * ssd_prefill -- chunked SSD scan over a whole sequence.
@@ -138,6 +144,31 @@ int ssd_prefill_dt_raw(int B, int L, int H, int P, int G, int N, int Q, int dtyp
                        const void *Bm, const void *Cm, const float *D,
                        const float *init_state, void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssd_prefill_noalloc -- ssd_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  It takes no workspace: the scratch is a buffer of
+ * SSD_NOALLOC_SCRATCH_BYTES that the library holds in a static device array,
+ * one copy per GPU (each GPU the library runs on holds it until the process
+ * ends).  Its device address is looked up once per GPU, on the first call
+ * made while that GPU is current; no call allocates or frees anything.
+ *
+ * Every argument, limit and result is as for ssd_prefill (same kernels, same
+ * bits).  `stream` must belong to the current device (else
+ * SSD_ERR_INVALID_ARG).  A call whose ssd_prefill_workspace_bytes(...)
+ * exceeds SSD_NOALLOC_SCRATCH_BYTES returns SSD_ERR_TOO_LARGE before any HIP
+ * call (the 2.7B-shaped layer at B = 1, L = 4096 needs 63.2 MiB and fits).
+ * The buffer keeps the last call's contents; nothing in it needs to start at
+ * zero.  All calls on one GPU share the one buffer: calls that overlap in
+ * time on one GPU (different streams, or different host threads without
+ * ordering between their streams) race on it and give undefined results.
+ */
+int ssd_prefill_noalloc(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                        const void *x, const float *dt, const float *A_log,
+                        const void *Bm, const void *Cm, const float *D,
+                        const float *init_state, void *y, float *final_state,
+                        hipStream_t stream);
 
 /* Bytes of workspace ssd_prefill needs for these arguments (0 if none).
  * Returns (size_t)-1 for arguments ssd_prefill would reject. */

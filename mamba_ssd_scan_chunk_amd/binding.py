@@ -24,6 +24,8 @@ SSD_ERR_UNSUPPORTED = -2
 SSD_ERR_ALIGNMENT = -3
 SSD_ERR_WORKSPACE = -4
 SSD_ERR_HIP = -5
+SSD_ERR_TOO_LARGE = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
 
 # (name, restype, argtypes) of every entry point in include/ssd.h
 _i, _p, _l, _sz, _f = ctypes.c_int, ctypes.c_void_p, ctypes.c_long, ctypes.c_size_t, ctypes.c_float
@@ -31,6 +33,7 @@ SIGNATURES = {
     "ssd_prefill": (_i, [_i] * 8 + [_p] * 10 + [_sz, _p]),
     "ssd_prefill_dt_raw": (_i, [_i] * 8 + [_p] * 3 + [_f, _f] + [_p] * 8 + [_sz, _p]),
     "ssd_prefill_workspace_bytes": (_sz, [_i] * 8),
+    "ssd_prefill_noalloc": (_i, [_i] * 8 + [_p] * 9 + [_p]),
     "ssd_prefill_varlen": (_i, [_i] * 8 + [_p] * 11 + [_sz, _p]),
     "ssd_prefill_varlen_workspace_bytes": (_sz, [_i] * 8),
     "ssd_prefill_varlen_dt_raw": (_i, [_i] * 8 + [_p] * 4 + [_f, _f] + [_p] * 8 + [_sz, _p]),
@@ -210,6 +213,34 @@ def ssd_prefill(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y=None,
                                _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
                                _ptr(workspace), ws_bytes, _stream(stream))
         _check("ssd_prefill", rc)
+    return y, final_state
+
+
+def ssd_prefill_noalloc(x, dt, A_log, Bm, Cm, D=None, init_state=None, *, Q, y, final_state=None, stream=None):
+    """ssd_prefill without a workspace argument: the scratch is the
+    library's fixed per-GPU buffer of NOALLOC_SCRATCH_BYTES (for callers that
+    cannot allocate device memory).  y, and final_state when wanted, are the
+    caller's: this call allocates nothing.  Returns (y, final_state)."""
+    if x.dim() != 4 or Bm.dim() != 4:
+        raise ValueError("x must be [B,L,H,P] and Bm [B,L,G,N]")
+    if y is None:
+        raise ValueError("ssd_prefill_noalloc allocates nothing: pass y")
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    code = _dtype_code(x)
+    f32, dv = torch.float32, x.device
+    _want(x, "x", (B, L, H, P), x.dtype, dv)
+    _want(dt, "dt", (B, L, H), f32, dv)
+    _want(A_log, "A_log", (H,), f32, dv)
+    _want(Bm, "Bm", (B, L, G, N), x.dtype, dv)
+    _want(Cm, "Cm", (B, L, G, N), x.dtype, dv)
+    _want(D, "D", (H,), f32, dv)
+    _want(init_state, "init_state", (B, H, P, N), f32, dv)
+    _want(y, "y", (B, L, H, P), x.dtype, dv)
+    _want(final_state, "final_state", (B, H, P, N), f32, dv)
+    rc = lib().ssd_prefill_noalloc(B, L, H, P, G, N, Q, code, _ptr(x), _ptr(dt), _ptr(A_log), _ptr(Bm), _ptr(Cm),
+                                   _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state), _stream(stream))
+    _check("ssd_prefill_noalloc", rc)
     return y, final_state
 
 

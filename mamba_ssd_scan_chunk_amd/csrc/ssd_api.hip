@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ssd_internal.hpp"
 
 #define SSD_API extern "C" __attribute__((visibility("default")))
@@ -140,14 +142,51 @@ bool valid_dt_prep(float dt_min, float dt_max, const float *dt_bias) {
     return aligned(dt_bias, 4);
 }
 
+// ---- the fixed scratch of ssd_prefill_noalloc
+// One copy per GPU, held until the process ends.  On the host, `scratch` is
+// a stand-in for the symbol, not a device address: host code only ever uses
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // per device, set on its first call
+
+// Device address of the current device's scratch (looked up once per device,
+// with that device current).  `stream` must belong to the current device.
+int noalloc_scratch(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (stream) {
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return hip_status(e);
+        if ((int)sdev != dev) return SSD_ERR_INVALID_ARG;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p || !aligned(p, 256)) return SSD_ERR_ALIGNMENT;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
+
 // L is the per-sequence length, or with cu_seqlens (packed sequences, a
-// device array of B + 1 token offsets) the packed total T.
+// device array of B + 1 token offsets) the packed total T.  With `noalloc`
+// the workspace arguments are ignored and the scratch is the fixed buffer
+// above (after every argument check, so a rejected call makes no HIP call).
 int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, const int *cu_seqlens,
                  const void *x, const float *dt, const float *A_log,
                  const void *Bm, const void *Cm, const float *D,
                  const float *init_state, void *y, float *final_state,
                  void *workspace, size_t workspace_bytes, hipStream_t stream, const ssd::DtPrep &dtp,
-                 bool varlen = false) {
+                 bool varlen = false, bool noalloc = false) {
     const PrefillShape s{B, L, H, P, G, N, Q, dtype, varlen};
     int rc = check_prefill_shape(s);
     if (rc != SSD_OK) return rc;
@@ -189,7 +228,9 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
         if (overlap(final_state, b_state, workspace, b_ws)) return SSD_ERR_INVALID_ARG;
         if (final_state != init_state && overlap(final_state, b_state, init_state, b_state)) return SSD_ERR_INVALID_ARG;
     }
-    if (b_ws > 0) {
+    if (noalloc) {
+        if (b_ws > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+    } else if (b_ws > 0) {
         if (!workspace || workspace_bytes < b_ws) return SSD_ERR_WORKSPACE;
         for (const R &r : ins) if (overlap(workspace, b_ws, r.p, r.n)) return SSD_ERR_INVALID_ARG;
         if (overlap(workspace, b_ws, init_state, b_state)) return SSD_ERR_INVALID_ARG;
@@ -198,6 +239,10 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     if (L == 0) {
         if (!final_state) return SSD_OK;
         return hip_status(ssd::launch_state_copy(init_state, final_state, n_state, stream));
+    }
+    if (noalloc && b_ws > 0) {
+        rc = noalloc_scratch(stream, &workspace);
+        if (rc != SSD_OK) return rc;
     }
 
     ssd::PrefillArgs a;
@@ -296,6 +341,14 @@ SSD_API int ssd_prefill(int B, int L, int H, int P, int G, int N, int Q, int dty
                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return prefill_impl(B, L, H, P, G, N, Q, dtype, nullptr, x, dt, A_log, Bm, Cm, D, init_state, y, final_state,
                         workspace, workspace_bytes, stream, ssd::DtPrep{0, nullptr, 0.0f, 0.0f});
+}
+
+SSD_API int ssd_prefill_noalloc(int B, int L, int H, int P, int G, int N, int Q, int dtype,
+                                const void *x, const float *dt, const float *A_log,
+                                const void *Bm, const void *Cm, const float *D,
+                                const float *init_state, void *y, float *final_state, hipStream_t stream) {
+    return prefill_impl(B, L, H, P, G, N, Q, dtype, nullptr, x, dt, A_log, Bm, Cm, D, init_state, y, final_state,
+                        nullptr, 0, stream, ssd::DtPrep{0, nullptr, 0.0f, 0.0f}, false, true);
 }
 
 SSD_API int ssd_prefill_varlen(int B, int T, int H, int P, int G, int N, int Q, int dtype, const int *cu_seqlens,
@@ -525,6 +578,7 @@ SSD_API const char *ssd_status_string(int status) {
         case SSD_ERR_ALIGNMENT: return "pointer or stride breaks the required alignment";
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_HIP: return "HIP call failed (see ssd_last_hip_error)";
+        case SSD_ERR_TOO_LARGE: return "the call needs more scratch than the fixed no-allocation buffer holds";
         default: return "unknown status";
     }
 }
