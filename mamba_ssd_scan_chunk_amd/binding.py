@@ -15,7 +15,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssd.so")
+# SSD_LIB_PATH names another build of the same library (the tests run the host
+# checks once more under a sanitizer build); by default the in-tree build.
+LIB_PATH = os.environ.get("SSD_LIB_PATH") or os.path.join(_HERE, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_OK = 0

@@ -53,5 +53,41 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side sanitizers for the library's argument checks: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host half of every source only (each flag
+# behind -Xarch_host; the device code is built as usual).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def build_host_sanitized(outdir: str) -> str:
+    """libssd.so with sanitized host code, in `outdir`; load it by setting
+    SSD_LIB_PATH, with clang's ASan runtime (asan_runtime()) preloaded."""
+    objdir = os.path.join(outdir, "objs")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+    def comp(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        subprocess.check_call([HIPCC, *COMMON, *SANITIZE_HOST, "-c", src, "-o", obj],
+                              stderr=subprocess.DEVNULL)
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    lib = os.path.join(outdir, "libssd.so")
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_HOST, "-o", lib, *objs])
+    return lib
+
+
+def asan_runtime() -> str:
+    """clang's shared AddressSanitizer runtime (with UBSan), for LD_PRELOAD."""
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     build()

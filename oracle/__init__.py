@@ -33,14 +33,33 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+# SSD_ORACLE_LIB names a prebuilt copy (the sanitizer build the tests also run
+# the pins against); by default the in-tree build, compiled on demand.
+_ENV_LIB = os.environ.get("SSD_ORACLE_LIB")
+_LIB_PATH = _ENV_LIB or os.path.join(_HERE, "libssd_oracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
 
 
+def build_sanitized(out: str) -> str:
+    """Compile ssd_oracle.c with clang's AddressSanitizer and
+    UndefinedBehaviorSanitizer (any finding aborts) into `out`; load it by
+    setting SSD_ORACLE_LIB, with clang's ASan runtime preloaded."""
+    subprocess.check_call(
+        ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-Wall", "-fno-omit-frame-pointer",
+         "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-o", out, _SRC, "-lm", "-lpthread"]
+    )
+    return out
+
+
 def build(force: bool = False) -> str:
-    """Compile ssd_oracle.c with gcc -O2 (no fast-math) into libssd_oracle.so."""
+    """Compile ssd_oracle.c with gcc -O2 (no fast-math) into libssd_oracle.so
+    (nothing to do when SSD_ORACLE_LIB names a prebuilt copy)."""
+    if _ENV_LIB:
+        if not os.path.exists(_ENV_LIB):
+            raise FileNotFoundError(f"SSD_ORACLE_LIB={_ENV_LIB} does not exist")
+        return _ENV_LIB
     if force or not os.path.exists(_LIB_PATH) or (
         os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
     ):
