@@ -1,0 +1,362 @@
+// prefill_chain.hip -- chained single-pass SSD prefill on bf16 MFMA (gfx950),
+// P = 64, N = 128, 256-token chunks, uniform batches.
+//
+// The chunked scan of arXiv 2603.09555 as the bqwf.cn article on its
+// compiler-first Mamba-2 implementation lays it out: §1.1 (dense work inside
+// fixed chunks, a light sequential scan of the state between chunks) and
+// §1.2 (the intra-chunk product and its fusion into one kernel, which keeps
+// intermediate results out of memory).  The four-kernel form
+// (prefill_mfma.hip) writes every chunk state S_c and every carried state
+// h_{c-1} to memory and reads x twice.  Here one workgroup per item (b, c, h)
+// does all of the item's work in one pass:
+//
+//   1. takes the next item from a ticket counter (items in chunk-major
+//      order, so chunk c of a chain is always taken after chunk c-1).  The
+//      chains are split into eight contiguous shares, one per XCD, each
+//      with its own counter: a workgroup takes from the share of the XCD it
+//      runs on (the heads of a chunk then share one L2 for the chunk's
+//      packed operands), and from the next shares once its own is used up;
+//   2. loads x and dt once, forms x' in LDS, and the chunk state
+//        S_c = exp(cs_last - R_7) sum_k (prod_{j > k} Q_j) x'^T_k B_k
+//      on MFMA (the same tile references R_k and ratios Q_k as the outputs
+//      use: the Horner scheme run to the chunk's end);
+//   3. waits until chunk c-1 of its (b, h) chain has published
+//      h_{c-1}, reads it, forms h_c = h_{c-1} + (expm1(cs_last) h_{c-1} + S_c)
+//      in fp32 and publishes h_c for chunk c+1 (or writes the final state).
+//      The chain's counter is read once at the start as well: when chunk c-1
+//      has already published (the usual case with many chains in flight),
+//      h_{c-1} is requested right away and arrives during the chunk state;
+//   4. forms the outputs from x' (still in LDS), h_{c-1} and the packed
+//      operands exactly as the output kernel does (out_tiles).
+//
+// Only the carried state travels between workgroups, through two slots per
+// chain (chunk c reads slot (c-1) % 2 and writes slot c % 2): 64 KB of
+// traffic per item that stays in the memory-side cache, against 96 KB of
+// chunk and carried states plus a second read of x in the four-kernel form.
+//
+// Hand-off protocol.  The slot is written with agent-scope coherent stores
+// (the cache-policy bits the compiler uses for agent-scope atomic stores, so
+// the data goes past the XCD's own L2), each thread waits for its stores to
+// complete, the workgroup synchronises, and thread 0 then sets the chain's
+// counter to c + 1 with an agent-scope atomic store.  The successor's thread
+// 0 polls the counter with agent-scope atomic loads, the workgroup
+// synchronises, and every thread reads the slot with agent-scope coherent
+// loads (which do not hit a stale line of the reader's L2).  Slot reuse is
+// safe: chunk c+2 writes slot c % 2 only after it has seen the counter of
+// chunk c+1, which chunk c+1 sets after its reads of slot c % 2 returned.
+// No deadlock: tickets are taken by running workgroups only, and an item
+// waits only on chunk c-1 of its chain, which has a smaller ticket of the
+// same counter and so is held by a running or finished workgroup; the
+// unfinished item of smallest chunk index therefore always progresses.
+// Every workgroup takes exactly one item: the grid has one workgroup per
+// item, and a workgroup moves on to another share only when its counter has
+// handed out all of that share.  Every wait is bounded (0.2 s of the 100 MHz wall clock, far
+// beyond the microseconds a hand-off takes): on expiry the workgroup sets the
+// control block's error word and carries NaN, so a broken hand-off shows as
+// NaN outputs instead of a hang.  The pack kernel clears the control block
+// at the start of every call.
+#include "prefill_mfma.hpp"
+
+namespace ssd {
+namespace {
+
+// Cache-policy bits of an agent-scope coherent access (sc1), as the compiler
+// emits them for agent-scope atomic loads and stores on gfx950.
+constexpr int kScopeAgent = 16;
+// Bound of one hand-off wait, in ticks of the 100 MHz wall clock.
+constexpr unsigned long long kHandoffTimeout = 20000000ull;
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
+constexpr int kWaitVmcnt0 = 0x0F70;
+// Chains needed before the chained form pays.  Measured on the 2.7B-shaped
+// layer (one MI355X, against the four-kernel form): 320 chains (B = 4) and
+// more are 17-31% faster chained, 160 and fewer 5-80% slower, because each
+// chain's hand-offs are serial and too few chains leave them exposed.
+constexpr long kChainMinChains = 256;
+
+constexpr int CH_TK = K3_LDS;       // ticket and wait result
+constexpr int CH_LDS = CH_TK + 16;
+
+// Byte offset in a hand-off slot of the 16 bytes (registers 4q .. 4q+3 of
+// accumulator `acc`) that lane `lane` of wave `wave` holds: 1 KiB contiguous
+// per store instruction.
+__device__ __forceinline__ unsigned slot_off(int wave, int acc, int q, int lane) {
+    return (unsigned)((((wave * 2 + acc) * 4 + q) * 64 + lane) * 16);
+}
+
+__device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kScopeAgent);
+}
+
+// XCD of the executing workgroup (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kChainXcds - 1); }
+
+// Chains [lo, hi) of XCD share x: eight contiguous ranges of the B*H chains.
+__device__ __forceinline__ void xcd_share(int x, long BH, int &lo, int &hi) {
+    lo = (int)(x * BH / kChainXcds);
+    hi = (int)((x + 1) * BH / kChainXcds);
+}
+
+// Feature row of register v of accumulator acc (lane half lh): the
+// accumulator order of a 32x32 MFMA tile.
+__device__ __forceinline__ int acc_row(int acc, int v, int lh) { return 32 * acc + (v >> 2) * 8 + lh * 4 + (v & 3); }
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_chain_mfma(PrefillArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char *xt = smem + K3_XT;
+    char *hl = smem + K3_H;
+    float *vt = (float *)(smem + K3_V);
+    float *ut = (float *)(smem + K3_U);
+    float *dtt = (float *)(smem + K3_DT);
+    float *wv = (float *)(smem + K3_W);
+    int *tk = (int *)(smem + CH_TK);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+    int *ctl = a.ws_ctl;
+
+    // ---- the item: the next ticket of this XCD's share (chunk-major over
+    // the share's chains), else of the next shares
+    const long BH = (long)a.B * a.H;
+    if (tid == 0) {
+        int ic = -1, ibh = 0;
+        const int x0 = xcd_id();
+        for (int i = 0; i < kChainXcds && ic < 0; ++i) {
+            const int x = (x0 + i) & (kChainXcds - 1);
+            int lo, hi;
+            xcd_share(x, BH, lo, hi);
+            if (hi == lo) continue;
+            const long k = __hip_atomic_fetch_add(ctl + kChainTicket + x, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+            if (k < (long)(hi - lo) * a.nchunks) {
+                ic = (int)(k / (hi - lo));
+                ibh = lo + (int)(k - (long)ic * (hi - lo));
+            }
+        }
+        tk[0] = ic;
+        tk[1] = ibh;
+    }
+    __syncthreads();
+    const int c = __builtin_amdgcn_readfirstlane(tk[0]);
+    const int bh = __builtin_amdgcn_readfirstlane(tk[1]);
+    if (c < 0) return;  // every share handed out (not reached: one workgroup per item)
+    const int b = bh / a.H, h = bh - b * a.H;
+    const long f = (long)b * a.nchunks + c;
+    const ChunkEntry ch = chunk_at(a, f);
+    const int Qc = ch.Qc;
+    const long tok0 = ch.tok0;
+    const int g = h / (a.H / a.G);
+    const long cg = f * a.G + g;
+
+    // ---- loads: the chain's counter (thread 0), dt (the cumsum waits for
+    // these two only), x, the B operands
+    int *counter = ctl + kChainCtlHeader + bh;
+    int early = 0;
+    if (tid == 0 && c > 0) early = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float dtv = load_dt(a, tok0, Qc, h, tid);
+    u32x4 raw[8];
+    load_x_raw(a, tok0, Qc, h, raw, tid);
+    // B operands of the first two token tiles (the rest are streamed)
+    const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
+    u32x4 bq[4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) bq[gg] = bt[gg * 64];
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    if (tid == 0) tk[2] = early;
+    float total;
+    const bool exact = chunk_decay(dtv, -expf(a.A_log[h]), Dh, Qc, vt, ut, dtt, wv, tid, lane, wave, &total);
+
+    // ---- h_{c-1} requested now if chunk c-1 had published by the start
+    // (the counter was read before the barriers above)
+    const bool ready = c > 0 && tk[2] >= c;
+    float hp[2][16];
+    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(a.ws_ring + ((long)bh * 2 + ((c - 1) & 1)) * kP * kN, kP * kN * 4);
+    auto load_h = [&]() {
+#pragma unroll
+        for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 v = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(hrs, slot_off(wave, acc, q, lane), 0, kScopeAgent));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hp[acc][4 * q + r] = __uint_as_float(v[r]);
+            }
+    };
+    if (ready) load_h();
+
+    // ---- x' into LDS: the outputs' x' on the fast path; on the exact path
+    // first x'' = exp(cs_last - cs_s) dt_s x_s for the chunk state
+    {
+        float sc[8];
+        if (!exact) {
+            x_scales(vt, false, tid, sc);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int s = (tid >> 3) * 8 + r;
+                sc[r] = exp_fast(total - vt[s]) * dtt[s];
+            }
+        }
+        store_xt_korder(raw, sc, xt, tid);
+    }
+    __syncthreads();
+
+    // ---- chunk state S_c, wave w: columns n in [32w, 32w + 32), both
+    // 32-row feature tiles; Horner over the token tiles (Q = 1 and no final
+    // factor on the exact path)
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int k = 0; k < kTiles; ++k) {
+        if (k > 0) {
+            const float q = wv[K3_WQ + k];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s0[v] *= q;
+                s1[v] *= q;
+            }
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const u32x4 a0 = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
+            const u32x4 a1 = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
+            s0 = mfma32(a0, bq[(2 * k + hf) & 3], s0);
+            s1 = mfma32(a1, bq[(2 * k + hf) & 3], s1);
+        }
+        if (k + 2 < kTiles) {  // token tile k + 2 into the registers tile k used
+            bq[(2 * k) & 3] = bt[(2 * k + 4) * 64];
+            bq[(2 * k + 1) & 3] = bt[(2 * k + 5) * 64];
+        }
+    }
+    {
+        const float fin = exact ? 1.0f : exp_fast(wv[3 * 3 + 2] - wv[3 * 3 + 1]);  // exp(cs_last - R_7)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            s0[v] *= fin;
+            s1[v] *= fin;
+        }
+    }
+    if (exact) {
+        // the outputs' exact path takes x' = x
+        __syncthreads();
+        load_x_raw(a, tok0, Qc, h, raw, tid);
+        float sc[8];
+        x_scales(vt, true, tid, sc);
+        store_xt_korder(raw, sc, xt, tid);
+    }
+
+    // ---- first operands of the output phase, in flight during the wait (not
+    // hoisted above the chunk state)
+    __builtin_amdgcn_sched_barrier(0);
+    OutItem it;
+    it.ctp = (const u32x4 *)(a.ws_ct + cg * kBTChunk) + lane;
+    it.gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
+    it.tok0 = tok0;
+    it.Qc = Qc;
+    it.h = h;
+    it.Dh = Dh;
+    it.exact = exact;
+    u32x4 cop[8], gA[2][2], gB[3][2];
+    load_c_tile(it, wave, cop);
+
+    // ---- h_{c-1}: the initial state, or chunk c-1's hand-off
+    if (c == 0) {
+        const float *init = a.init_state ? a.init_state + (long)bh * kP * kN : nullptr;
+#pragma unroll
+        for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                hp[acc][v] = init ? init[acc_row(acc, v, lh) * kN + 32 * wave + li] : 0.0f;
+    } else if (!ready) {
+        if (tid == 0) {
+            const unsigned long long t0 = wall_clock64();
+            int ok = 1;
+            while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c) {
+                __builtin_amdgcn_s_sleep(2);
+                if (wall_clock64() - t0 > kHandoffTimeout) {
+                    ok = 0;
+                    __hip_atomic_fetch_or(ctl + kChainError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            tk[3] = ok;
+        }
+        __syncthreads();
+        load_h();
+        if (!tk[3]) {
+#pragma unroll
+            for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) hp[acc][v] = __builtin_nanf("");
+        }
+    }
+
+    // ---- h_c, rounded once: h + (expm1(cs_last) h + S); h_{c-1} into LDS
+    // as bf16 ([P][N], 16-byte chunks XOR-swizzled by row) for the outputs
+    const float dm1 = expm1f(total);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        s0[v] = hp[0][v] + fmaf(dm1, hp[0][v], s0[v]);
+        s1[v] = hp[1][v] + fmaf(dm1, hp[1][v], s1[v]);
+    }
+#pragma unroll
+    for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int p = acc_row(acc, v, lh), n = 32 * wave + li;
+            *(bf16_t *)(hl + p * 256 + (((n >> 3) ^ (p & 15)) << 4) + (n & 7) * 2) = f32_to_bf16(hp[acc][v]);
+        }
+    if (c + 1 < a.nchunks) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.ws_ring + ((long)bh * 2 + (c & 1)) * kP * kN, kP * kN * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            buf_store16(u32x4{__float_as_uint(s0[4 * q]), __float_as_uint(s0[4 * q + 1]),
+                              __float_as_uint(s0[4 * q + 2]), __float_as_uint(s0[4 * q + 3])},
+                        rs, slot_off(wave, 0, q, lane));
+            buf_store16(u32x4{__float_as_uint(s1[4 * q]), __float_as_uint(s1[4 * q + 1]),
+                              __float_as_uint(s1[4 * q + 2]), __float_as_uint(s1[4 * q + 3])},
+                        rs, slot_off(wave, 1, q, lane));
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this thread's slot stores are complete
+        __syncthreads();                          // ... and every other thread's
+        if (tid == 0) __hip_atomic_store(counter, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (a.final_state) {
+        float *fs = a.final_state + (long)bh * kP * kN + 32 * wave + li;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            fs[acc_row(0, v, lh) * kN] = s0[v];
+            fs[acc_row(1, v, lh) * kN] = s1[v];
+        }
+    }
+
+    {
+        const int ltA = wave, ltB = kTiles - 1 - wave;
+        const u32x4 *pa = gt_tile(it, 0, ltA);
+        const u32x4 *pb = gt_tile(it, 0, ltB);
+        gA[0][0] = pa[0];
+        gA[0][1] = pa[64];
+        gB[0][0] = pb[0];
+        gB[0][1] = pb[64];
+        const u32x4 *pb1 = gt_tile(it, 1, ltB);
+        gB[1][0] = pb1[0];
+        gB[1][1] = pb1[64];
+    }
+    __syncthreads();
+    out_tiles(a, it, smem, cop, gA, gB, tid);
+}
+
+}  // namespace
+
+// The chained form needs enough (b, h) chains to keep the machine busy while
+// each chain waits on its hand-offs.
+bool prefill_uses_chain(int B, int L, int H) { return L > 0 && (long)B * H >= kChainMinChains; }
+
+hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s) {
+    const long nitems = (long)a.B * a.nchunks * a.H;
+    if (nitems > 0x7fffffffL || a.chunks) return hipErrorInvalidConfiguration;
+    stage_begin();
+    hipError_t e = launch_chunk_pack(a, true, a.ws_ctl, s);
+    if (e != hipSuccess) return e;
+    return launch_stage("chunk_chain_mfma", chunk_chain_mfma, dim3((unsigned)nitems), dim3(kThreads), CH_LDS, s, a);
+}
+
+}  // namespace ssd

@@ -76,27 +76,35 @@ bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
     return dtype == SSD_BF16 && P == 64 && N == 128 && Q % kMfmaQ == 0;
 }
 
-WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq) {
-    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0};
+WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq,
+                                         long chains) {
+    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     if (slots <= 0) return w;
     const size_t heads = (size_t)slots * H;
     const size_t groups = (size_t)slots * G;
-    w.off_S = 0;
-    w.off_dec = align_up(w.off_S + heads * P * N * sizeof(float), 256);
-    w.off_cs = align_up(w.off_dec + heads * sizeof(float), 256);
-    const size_t cs_bytes = mfma ? 0 : heads * Q * sizeof(double);
-    w.off_hb = align_up(w.off_cs + cs_bytes, 256);
-    const size_t hb_bytes = mfma ? heads * P * N * sizeof(uint16_t) : 0;
-    w.off_gt = align_up(w.off_hb + hb_bytes, 256);
+    const bool chain = mfma && chains > 0;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, 256);
+        return o;
+    };
+    // chained MFMA path: control block and two hand-off slots per chain
+    // instead of per-chunk states
+    w.off_ctl = take(chain ? (size_t)(kChainCtlHeader + chains) * sizeof(int) : 0);
+    w.off_ring = take(chain ? (size_t)chains * 2 * P * N * sizeof(float) : 0);
+    w.off_S = take(chain ? 0 : heads * P * N * sizeof(float));
+    w.off_dec = take(chain ? 0 : heads * sizeof(float));
+    w.off_cs = take(mfma ? 0 : heads * Q * sizeof(double));
+    w.off_hb = take(mfma && !chain ? heads * P * N * sizeof(uint16_t) : 0);
     // MFMA path: G^T tiles in bf16; vector path: the Q x Q masked C B^T in fp32
-    const size_t gt_bytes = mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t)
-                                 : groups * (size_t)Q * Q * sizeof(float);
-    w.off_bt = align_up(w.off_gt + gt_bytes, 256);
+    w.off_gt = take(mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t)
+                         : groups * (size_t)Q * Q * sizeof(float));
     const size_t bt_bytes = mfma ? groups * prefill_mfma_bt_elems_per_chunk() * sizeof(uint16_t) : 0;
-    w.off_ct = align_up(w.off_bt + bt_bytes, 256);
-    w.off_tab = align_up(w.off_ct + bt_bytes, 256);  // C packed like B
-    const size_t tab_bytes = nseq > 0 ? (size_t)slots * sizeof(ChunkEntry) + (size_t)nseq * sizeof(SeqEntry) : 0;
-    w.total = align_up(w.off_tab + tab_bytes, 256);
+    w.off_bt = take(bt_bytes);
+    w.off_ct = take(bt_bytes);  // C packed like B
+    w.off_tab = take(nseq > 0 ? (size_t)slots * sizeof(ChunkEntry) + (size_t)nseq * sizeof(SeqEntry) : 0);
+    w.total = off;
     return w;
 }
 
@@ -114,11 +122,18 @@ long prefill_slots(const PrefillShape &s) {
     const int q = run_q(s);
     return s.varlen ? ssd::varlen_slots(s.L, s.B, q) : (long)s.B * ((s.L + q - 1) / q);
 }
-size_t workspace_bytes_for(const PrefillShape &s) {
-    return ssd::prefill_workspace_layout(prefill_slots(s), s.H, s.P, s.N, run_q(s), s.G,
-                                         ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype), s.varlen ? s.B : 0)
-        .total;
+// (b, h) chains of the chained MFMA path, 0 when the call takes another path.
+long prefill_chains(const PrefillShape &s) {
+    const bool chain = ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype) && !s.varlen &&
+                       ssd::prefill_uses_chain(s.B, s.L, s.H);
+    return chain ? (long)s.B * s.H : 0;
 }
+ssd::WorkspaceLayout workspace_layout_for(const PrefillShape &s) {
+    return ssd::prefill_workspace_layout(prefill_slots(s), s.H, s.P, s.N, run_q(s), s.G,
+                                         ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype), s.varlen ? s.B : 0,
+                                         prefill_chains(s));
+}
+size_t workspace_bytes_for(const PrefillShape &s) { return workspace_layout_for(s).total; }
 }  // namespace
 
 SSD_API size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N, int Q, int dtype) {
@@ -208,7 +223,8 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     const bool mfma = ssd::prefill_uses_mfma(P, N, Q, dtype);
     const int q = run_q(s);
     const long slots = prefill_slots(s);
-    const ssd::WorkspaceLayout wl = ssd::prefill_workspace_layout(slots, H, P, N, q, G, mfma, varlen ? B : 0);
+    const bool chain = prefill_chains(s) > 0;
+    const ssd::WorkspaceLayout wl = workspace_layout_for(s);
     const size_t b_ws = wl.total;
 
     // outputs may not overlap inputs, workspace or each other
@@ -254,10 +270,12 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     a.dtp = dtp;
     a.init_state = init_state; a.y = y; a.final_state = final_state;
     char *ws = (char *)workspace;
-    a.ws_S = (float *)(ws + wl.off_S);
-    a.ws_dec = (float *)(ws + wl.off_dec);
+    a.ws_S = chain ? nullptr : (float *)(ws + wl.off_S);
+    a.ws_dec = chain ? nullptr : (float *)(ws + wl.off_dec);
     a.ws_cs = mfma ? nullptr : (double *)(ws + wl.off_cs);
-    a.ws_hb = mfma ? (uint16_t *)(ws + wl.off_hb) : nullptr;
+    a.ws_hb = mfma && !chain ? (uint16_t *)(ws + wl.off_hb) : nullptr;
+    a.ws_ctl = chain ? (int *)(ws + wl.off_ctl) : nullptr;
+    a.ws_ring = chain ? (float *)(ws + wl.off_ring) : nullptr;
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
@@ -272,7 +290,9 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
         a.chunks = chunks;
         a.seqs = seqs;
     }
-    hipError_t e = mfma ? ssd::launch_prefill_mfma(a, stream) : ssd::launch_prefill_vector(a, dtype, stream);
+    hipError_t e = chain  ? ssd::launch_prefill_chain(a, stream)
+                   : mfma ? ssd::launch_prefill_mfma(a, stream)
+                          : ssd::launch_prefill_vector(a, dtype, stream);
     return hip_status(e);
 }
 

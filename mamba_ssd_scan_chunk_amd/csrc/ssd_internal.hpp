@@ -58,18 +58,32 @@ struct PrefillArgs {
     uint16_t *ws_bt;  // [B, nchunks, G, Q*N] bf16: B in MFMA operand order (MFMA path)
     uint16_t *ws_ct;  // [B, nchunks, G, Q*N] bf16: C in MFMA operand order (MFMA path)
     float *ws_cb;     // [B, nchunks, G, Q, Q] fp32: C B^T masked to s <= l (vector path)
+    int *ws_ctl;      // chained MFMA path: control block (ticket, error word, per-chain counters)
+    float *ws_ring;   // chained MFMA path: [B*H, 2, P*N] fp32 hand-off slots of the carried state
 };
 
+// Control block of the chained MFMA path: kChainCtlHeader ints (one item
+// ticket counter per XCD, the hand-off error word), then one published-chunk
+// counter per (b, h) chain.  Cleared by the pack kernel at the start of every
+// call.
+constexpr int kChainCtlHeader = 64;
+constexpr int kChainXcds = 8;      // ticket counters: one per XCD of the MI355X
+constexpr int kChainTicket = 0;    // ctl[kChainTicket + x]: tickets taken from XCD x's share
+constexpr int kChainError = 8;
+
 struct WorkspaceLayout {
-    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, off_tab, total;
+    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, off_tab, off_ctl, off_ring, total;
 };
 constexpr int kPrefillMaxQ = 1024;  // largest chunk
 constexpr int kMfmaQ = 256;         // chunk of the MFMA kernels
 long prefill_mfma_gt_elems_per_chunk();
 long prefill_mfma_bt_elems_per_chunk();
 // Workspace for `slots` chunk slots of H heads (and G groups), plus the slot
-// and sequence tables of packed sequences when nseq > 0.
-WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq);
+// and sequence tables of packed sequences when nseq > 0.  `chains` > 0
+// selects the chained MFMA path with that many (b, h) chains: control block,
+// hand-off slots and the packed operands, no per-chunk states.
+WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq,
+                                         long chains = 0);
 // Chunk slots of a packed prefill of T tokens in B sequences: an upper bound
 // of sum over sequences of ceil(L_b / Q).
 inline long varlen_slots(long T, int B, int Q) { return T / Q + B; }
@@ -97,6 +111,13 @@ hipError_t launch_stage(const char *name, Kernel kernel, dim3 grid, dim3 block, 
 
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
+// The pack kernel alone: G^T tiles and B operands, plus C operands with
+// `with_c`; clears the chained path's control block when `ctl` is given.
+hipError_t launch_chunk_pack(const PrefillArgs &a, bool with_c, int *ctl, hipStream_t s);
+// Chained single-pass MFMA prefill (uniform batches of the MFMA shape).
+hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s);
+// Whether a uniform batch of the MFMA shape runs the chained path.
+bool prefill_uses_chain(int B, int L, int H);
 hipError_t launch_state_pass(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, size_t n, hipStream_t s);
 

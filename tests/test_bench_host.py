@@ -45,20 +45,51 @@ def test_prefill_and_decode_bytes():
     assert expect == 85302912  # the per-step figure the decode leg reports at B = 16
 
 
-def test_stage_flops_add_up_to_the_call():
+@pytest.mark.parametrize("shape", [(1, 4096, 80, 64, 1, 128, 256), (8, 16384, 80, 64, 1, 128, 256),
+                                   (2, 700, 6, 64, 3, 128, 256)])
+def test_stage_flops_add_up_to_the_call(shape):
+    four = ("chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma")
+    assert sum(bench.stage_work(k, *shape)[1] for k in four) == bench.prefill_flops(*shape)
+    chained = ("chunk_pack_mfma", "chunk_chain_mfma")
+    assert sum(bench.stage_work(k, *shape, chained=True)[1] for k in chained) == bench.prefill_flops(*shape)
+
+
+def test_stage_bytes():
     shape = (1, 4096, 80, 64, 1, 128, 256)
-    parts = sum(bench.stage_work(k, *shape)[1]
-                for k in ("chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"))
-    assert parts == bench.prefill_flops(*shape)
     assert bench.stage_work("chunk_out_mfma", *shape)[0] == 108396544
+    B, L, H, P, G, N, Q = 8, 16384, 80, 64, 1, 128, 256
+    nch, x = L // Q, B * L * H * P * 2
+    tiles = 36 * 32 * 32 * 2
+    # x and y, dt; G^T, B and C operands of every (batch, chunk); the
+    # carried state out and back in between chunks; the final state
+    expect = 2 * x + 4 * B * L * H + B * nch * (tiles + 2 * Q * N * 2) + 2 * B * H * (nch - 1) * P * N * 4 \
+        + B * H * P * N * 4
+    assert bench.stage_work("chunk_chain_mfma", B, L, H, P, G, N, Q, chained=True)[0] == expect
+
+
+@pytest.mark.parametrize("kernels", [("chunk_pack_mfma", "chunk_chain_mfma"),
+                                     ("chunk_pack_mfma", "state_pass_bf16")])
+def test_algorithmic_bytes_cover_the_call(kernels):
+    """The compulsory bytes of the scan are those of the pack kernel (B, C)
+    and of the kernel that streams x, y, dt and the state; in the four-kernel
+    form x is counted by both the chunk-state and the output kernel."""
+    shape = (8, 16384, 80, 64, 1, 128)
+    B, L, H, P, G, N = shape
+    total = sum(bench.section8d_bytes(k, *shape) for k in kernels)
+    if kernels[1] == "state_pass_bf16":
+        total += bench.section8d_bytes("chunk_out_mfma", *shape)
+    assert total == bench.prefill_bytes(*shape)
 
 
 def test_committed_counter_summaries_are_used():
-    assert bench.measured_traffic("chunk_out_mfma") is not None
-    assert bench.measured_traffic("decode_step_kernel") is not None
-    counted = bench.measured_mfma("mamba2-2.7b-prefill")
-    assert counted["chunk_state_mfma"] == bench.stage_work("chunk_state_mfma", 1, 4096, 80, 64, 1, 128, 256)[1]
-    assert counted["state_pass_bf16"] == 0
+    """The committed rocprofv3 summaries match the kernel sources (else
+    bench.py reports null for them)."""
+    assert bench.measured_traffic("chunk_chain_mfma", "mamba2-2.7b-longctx") is not None
+    assert bench.measured_traffic("chunk_pack_mfma", "mamba2-2.7b-longctx") is not None
+    assert bench.measured_traffic("decode_step_kernel", "mamba2-2.7b-decode-b16") is not None
+    counted = bench.measured_mfma("mamba2-2.7b-longctx")
+    assert counted["chunk_chain_mfma"] >= bench.stage_work("chunk_chain_mfma", 8, 16384, 80, 64, 1, 128, 256,
+                                                           chained=True)[1]
     assert bench.measured_mfma("mamba2-130m-prefill") == {}
 
 

@@ -52,6 +52,15 @@ CASES = [
     ("f32-q1024", 1, 2200, 2, 16, 1, 16, 1024, "f32"),
     ("f32-q384-groups", 2, 900, 4, 8, 2, 32, 384, "f32"),
     ("f32-q1000-eq-l", 1, 1000, 1, 4, 1, 8, 1000, "f32"),
+    # the chained single-pass MFMA path (B*H >= 256 chains): ragged last
+    # chunk, several groups, one chunk per chain (no hand-off), 512-token
+    # chunks as 256-token sub-chunks, a chain count that is not a multiple
+    # of the eight XCD shares
+    ("chain-b16h16", 16, 300, 16, 64, 1, 128, 256, "bf16"),
+    ("chain-groups", 8, 600, 32, 64, 4, 128, 256, "bf16"),
+    ("chain-one-chunk", 32, 200, 8, 64, 1, 128, 256, "bf16"),
+    ("chain-q512", 4, 700, 64, 64, 1, 128, 512, "bf16"),
+    ("chain-b9h29", 9, 777, 29, 64, 1, 128, 256, "bf16"),
 ]
 
 
@@ -70,7 +79,7 @@ def test_prefill_matches_oracle(oracle, case, variant, with_init):
 
 
 RAW_DT_CASES = ["ragged", "q32-groups", "one-token", "odd-dims", "bf16-small", "bf16-q256-ragged",
-                "bf16-mfma-b3g3"]
+                "bf16-mfma-b3g3", "chain-b9h29"]
 
 
 @pytest.mark.parametrize("name", RAW_DT_CASES)
@@ -95,12 +104,13 @@ def test_prefill_dt_raw_matches_oracle(oracle, name, raw_dt):
     assert rel_err(fs, fs_ref) <= _tol(dtype)
 
 
-def test_mfma_longer_chunks_are_256_token_sub_chunks():
+@pytest.mark.parametrize("B,H", [(2, 3), (8, 40)], ids=["four-kernel", "chained"])
+def test_mfma_longer_chunks_are_256_token_sub_chunks(B, H):
     """On the MFMA shape a chunk of 512 or 1024 tokens runs as 256-token
-    sub-chunks linked by the state pass: the same arithmetic as Q = 256, so
-    the same bits."""
-    d = dev(synth.make_prefill(2, 1500, 3, 64, 1, 128, "bf16", seed=460))
-    announce("mfma Q=512/1024 vs 256")
+    sub-chunks linked by the state hand-off: the same arithmetic as Q = 256,
+    so the same bits."""
+    d = dev(synth.make_prefill(B, 1500, H, 64, 1, 128, "bf16", seed=460))
+    announce("mfma Q=512/1024 vs 256", B, H)
     y0, f0 = bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=256)
     for Q in (512, 1024):
         y1, f1 = bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=Q)
@@ -136,18 +146,20 @@ def test_final_state_may_alias_init_state(oracle):
     assert rel_err(st, fs_ref) <= TOL_F32
 
 
-@pytest.mark.parametrize("dtype,P,N,Q", [("f32", 16, 16, 64), ("bf16", 64, 128, 256)])
-def test_prefill_is_deterministic(dtype, P, N, Q):
-    d = synth.make_prefill(1, 1000, 4, P, 1, N, dtype, seed=9)
-    announce("prefill determinism", dtype)
+@pytest.mark.parametrize("dtype,P,N,Q,B,H", [("f32", 16, 16, 64, 1, 4), ("bf16", 64, 128, 256, 1, 4),
+                                            ("bf16", 64, 128, 256, 4, 80)])
+def test_prefill_is_deterministic(dtype, P, N, Q, B, H):
+    d = synth.make_prefill(B, 1000, H, P, 1, N, dtype, seed=9)
+    announce("prefill determinism", dtype, B, H)
     y1, f1 = _run(d, Q)
     y2, f2 = _run(d, Q)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
-@pytest.mark.parametrize("dtype,P,N,Q", [("f32", 16, 16, 64), ("bf16", 64, 128, 256)])
-def test_split_prefill_equals_one_prefill(oracle, dtype, P, N, Q):
-    B, L1, L2, H = 1, 300, 213, 3
+@pytest.mark.parametrize("dtype,P,N,Q,B,H", [("f32", 16, 16, 64, 1, 3), ("bf16", 64, 128, 256, 1, 3),
+                                            ("bf16", 64, 128, 256, 4, 64)])
+def test_split_prefill_equals_one_prefill(oracle, dtype, P, N, Q, B, H):
+    L1, L2 = 300, 213
     d = synth.make_prefill(B, L1 + L2, H, P, 1, N, dtype, seed=10, variant="slow")
     announce("split prefill", dtype)
     y, fs = _run(d, Q)
@@ -161,11 +173,12 @@ def test_split_prefill_equals_one_prefill(oracle, dtype, P, N, Q):
     assert rel_err(torch.cat([y1, y2], 1), y) <= 2 * _tol(dtype)
 
 
-@pytest.mark.parametrize("dtype,P,N,Q", [("f32", 16, 16, 64), ("bf16", 64, 128, 256)])
-def test_prefill_then_decode_equals_longer_prefill(oracle, dtype, P, N, Q):
+@pytest.mark.parametrize("dtype,P,N,Q,B,H", [("f32", 16, 16, 64, 2, 4), ("bf16", 64, 128, 256, 2, 4),
+                                            ("bf16", 64, 128, 256, 8, 32)])
+def test_prefill_then_decode_equals_longer_prefill(oracle, dtype, P, N, Q, B, H):
     """prefill(L) then k decode steps gives the outputs and state of
     prefill(L + k)."""
-    B, L, k, H, G = 2, 520, 24, 4, 1
+    L, k, G = 520, 24, 1
     d = synth.make_prefill(B, L + k, H, P, G, N, dtype, seed=11)
     dd = dev(d)
     announce("prefill+decode", dtype)
@@ -285,12 +298,13 @@ def test_long_context_prefill_then_decode_sampled_heads(oracle):
             assert rel_err(state[b, h], fs_ref[0, j]) <= TOL_BF16, (b, h)
 
 
-@pytest.mark.parametrize("dtype,P,N,Q,kernels", [
-    ("bf16", 64, 128, 256, ["chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]),
-    ("f32", 16, 16, 64, ["chunk_state_vec", "chunk_cb_vec", "state_pass", "chunk_out_vec"]),
+@pytest.mark.parametrize("dtype,P,N,Q,B,H,kernels", [
+    ("bf16", 64, 128, 256, 1, 4, ["chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]),
+    ("bf16", 64, 128, 256, 4, 64, ["chunk_pack_mfma", "chunk_chain_mfma"]),
+    ("f32", 16, 16, 64, 1, 4, ["chunk_state_vec", "chunk_cb_vec", "state_pass", "chunk_out_vec"]),
 ])
-def test_stage_timing_reports_each_kernel(dtype, P, N, Q, kernels):
-    d = synth.make_prefill(1, 700, 4, P, 1, N, dtype, seed=12)
+def test_stage_timing_reports_each_kernel(dtype, P, N, Q, B, H, kernels):
+    d = synth.make_prefill(B, 700, H, P, 1, N, dtype, seed=12)
     announce("stage timing", dtype)
     y0, f0 = _run(d, Q)
     bd.stage_timing(True)
