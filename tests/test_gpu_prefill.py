@@ -316,3 +316,40 @@ def test_stage_timing_reports_each_kernel(dtype, P, N, Q, B, H, kernels):
     assert [name for name, _ in st] == kernels
     assert all(ms > 0.0 for _, ms in st)
     assert torch.equal(y0, y1) and torch.equal(f0, f1)  # timing changes no result
+
+
+def test_stage_timing_is_per_host_thread():
+    # two host threads time different paths at the same time; each reads back
+    # only the kernels of its own last call
+    import threading
+    jobs = {
+        "chain": (synth.make_prefill(4, 700, 64, 64, 1, 128, "bf16", seed=13),
+                  ["chunk_pack_mfma", "chunk_chain_mfma"]),
+        "four": (synth.make_prefill(1, 700, 4, 64, 1, 128, "bf16", seed=14),
+                 ["chunk_pack_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]),
+    }
+    announce("stage timing", "two threads")
+    both = threading.Barrier(2)
+    seen, errors = {}, []
+
+    def work(key):
+        try:
+            d, _ = jobs[key]
+            bd.stage_timing(True)
+            try:
+                _run(d, 256)
+                both.wait(timeout=60)  # the other thread's call is enqueued too
+                _run(d, 256)
+                seen[key] = [name for name, _ in bd.stage_times()]
+            finally:
+                bd.stage_timing(False)
+        except Exception as e:  # reported on the main thread
+            errors.append(f"{key}: {e!r}")
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert errors == []
+    assert {k: v for k, v in seen.items()} == {k: kernels for k, (_, kernels) in jobs.items()}
