@@ -574,11 +574,14 @@ def bench_other_prefills(args):
                            workspace=ws)
 
         ms = _timed(vstep, 5 if dtype == "f32" else 50, 1, key)
-        flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, Q)
         path = "mfma, 256-token sub-chunks" if dtype == "bf16" and Q % 256 == 0 else "vector"
+        # flops of the chunking the kernels evaluate (the MFMA path runs
+        # 256-token sub-chunks, so its intra-chunk work is that of Q = 256)
+        run_q = 256 if path.startswith("mfma") else Q
+        flops = prefill_flops(w.B, w.L, w.H, w.P, w.G, w.N, run_q)
         out[key] = {"dtype": dtype, "chunk": Q, "path": path, "us": round(ms * 1e3, 1),
                     "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
-                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+                    "flop_chunk": run_q, "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
         del d, y, ws
     return {"other_workloads": out}
 

@@ -370,6 +370,22 @@ int ssd_stage_timing(int enable);
 int ssd_stage_times(float *ms, int capacity, int *count);
 const char *ssd_stage_name(int index);
 
+/*
+ * Testing aid, kept per host thread: the bound of each hand-off wait of the
+ * chained single-pass prefill (the path ssd_prefill takes for bf16, P = 64,
+ * N = 128, Q a multiple of 256 and B*H >= 256 chains, where chunk c of a
+ * (batch, head) chain waits for chunk c-1 to publish its carried state), in
+ * ticks of the 100 MHz device clock, for the calling thread's later calls.
+ * ticks < 0 restores the default, 0.2 s (20 000 000 ticks).  A wait that
+ * expires sets an error word in the workspace's control block and carries
+ * NaN as the state, so that chunk's outputs and every later chunk of its
+ * chain come out NaN: a broken hand-off shows in the results instead of
+ * hanging the device.  A bound of 0 makes every wait that does not find its
+ * predecessor already published expire, which is how the tests force that
+ * path.  Returns SSD_OK.
+ */
+int ssd_debug_handoff_ticks(long long ticks);
+
 /* Static, human-readable text for a status code. */
 const char *ssd_status_string(int status);
 

@@ -48,6 +48,7 @@ SIGNATURES = {
     "ssd_stage_timing": (_i, [_i]),
     "ssd_stage_times": (_i, [ctypes.POINTER(ctypes.c_float), _i, ctypes.POINTER(_i)]),
     "ssd_stage_name": (ctypes.c_char_p, [_i]),
+    "ssd_debug_handoff_ticks": (_i, [ctypes.c_longlong]),
     "ssd_status_string": (ctypes.c_char_p, [_i]),
     "ssd_last_hip_error": (_i, []),
 }
@@ -460,6 +461,12 @@ def ssd_status_string(status: int) -> str:
 
 def ssd_last_hip_error() -> int:
     return lib().ssd_last_hip_error()
+
+
+def debug_handoff_ticks(ticks: int) -> None:
+    """Bound of the chained prefill's hand-off waits for later calls of this
+    thread, in 100 MHz device ticks; negative restores the default (0.2 s)."""
+    _check("ssd_debug_handoff_ticks", lib().ssd_debug_handoff_ticks(int(ticks)))
 
 
 def stage_timing(enable: bool) -> None:

@@ -30,9 +30,9 @@
 //      operands exactly as the output kernel does (out_tiles).
 //
 // Only the carried state travels between workgroups, through two slots per
-// chain (chunk c reads slot (c-1) % 2 and writes slot c % 2): 64 KB of
-// traffic per item that stays in the memory-side cache, against 96 KB of
-// chunk and carried states plus a second read of x in the four-kernel form.
+// chain (chunk c reads slot (c-1) % 2 and writes slot c % 2): 32 KB written
+// and 32 KB read per item, against 96 KB of chunk and carried states plus a
+// second read of x in the four-kernel form.
 //
 // Hand-off protocol.  The slot is written with agent-scope coherent stores
 // (the cache-policy bits the compiler uses for agent-scope atomic stores, so
@@ -41,7 +41,10 @@
 // counter to c + 1 with an agent-scope atomic store.  The successor's thread
 // 0 polls the counter with agent-scope atomic loads, the workgroup
 // synchronises, and every thread reads the slot with agent-scope coherent
-// loads (which do not hit a stale line of the reader's L2).  Slot reuse is
+// loads, which do not hit a stale line of the reader's L1 or L2 (loads with
+// workgroup-scope or no cache-policy bits were seen to return the reader's
+// stale L1 copy for milliseconds after another CU had rewritten the line).
+// Slot reuse is
 // safe: chunk c+2 writes slot c % 2 only after it has seen the counter of
 // chunk c+1, which chunk c+1 sets after its reads of slot c % 2 returned.
 // No deadlock: tickets are taken by running workgroups only, and an item
@@ -50,11 +53,13 @@
 // unfinished item of smallest chunk index therefore always progresses.
 // Every workgroup takes exactly one item: the grid has one workgroup per
 // item, and a workgroup moves on to another share only when its counter has
-// handed out all of that share.  Every wait is bounded (0.2 s of the 100 MHz wall clock, far
-// beyond the microseconds a hand-off takes): on expiry the workgroup sets the
-// control block's error word and carries NaN, so a broken hand-off shows as
-// NaN outputs instead of a hang.  The pack kernel clears the control block
-// at the start of every call.
+// handed out all of that share.  Every wait is bounded (by default 0.2 s of
+// the 100 MHz wall clock, far beyond the microseconds a hand-off takes; the
+// bound is a kernel argument that ssd_debug_handoff_ticks sets per host
+// thread for tests): on expiry the workgroup sets the control block's error
+// word and carries NaN, so a broken hand-off shows as NaN outputs instead of
+// a hang.  The pack kernel clears the control block at the start of every
+// call.
 #include "prefill_mfma.hpp"
 
 namespace ssd {
@@ -63,8 +68,6 @@ namespace {
 // Cache-policy bits of an agent-scope coherent access (sc1), as the compiler
 // emits them for agent-scope atomic loads and stores on gfx950.
 constexpr int kScopeAgent = 16;
-// Bound of one hand-off wait, in ticks of the 100 MHz wall clock.
-constexpr unsigned long long kHandoffTimeout = 20000000ull;
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 constexpr int kWaitVmcnt0 = 0x0F70;
 // Chains needed before the chained form pays.  Measured on the 2.7B-shaped
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             int ok = 1;
             while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c) {
                 __builtin_amdgcn_s_sleep(2);
-                if (wall_clock64() - t0 > kHandoffTimeout) {
+                if (wall_clock64() - t0 > a.handoff_ticks) {
                     ok = 0;
                     __hip_atomic_fetch_or(ctl + kChainError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;

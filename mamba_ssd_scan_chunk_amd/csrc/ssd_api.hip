@@ -14,6 +14,9 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+// Bound of the chained prefill's hand-off waits for calls of this thread
+// (ssd_debug_handoff_ticks); negative = the default.
+thread_local long long g_handoff_ticks = -1;
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return SSD_OK;
@@ -276,6 +279,7 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     a.ws_hb = mfma && !chain ? (uint16_t *)(ws + wl.off_hb) : nullptr;
     a.ws_ctl = chain ? (int *)(ws + wl.off_ctl) : nullptr;
     a.ws_ring = chain ? (float *)(ws + wl.off_ring) : nullptr;
+    a.handoff_ticks = g_handoff_ticks < 0 ? ssd::kHandoffTicks : (unsigned long long)g_handoff_ticks;
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
@@ -583,6 +587,11 @@ SSD_API int ssd_stage_times(float *ms, int capacity, int *count) {
         if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_timer.start[i], g_timer.stop[i]);
         if (e != hipSuccess) return hip_status(e);
     }
+    return SSD_OK;
+}
+
+SSD_API int ssd_debug_handoff_ticks(long long ticks) {
+    g_handoff_ticks = ticks < 0 ? -1 : ticks;
     return SSD_OK;
 }
 

@@ -60,7 +60,12 @@ struct PrefillArgs {
     float *ws_cb;     // [B, nchunks, G, Q, Q] fp32: C B^T masked to s <= l (vector path)
     int *ws_ctl;      // chained MFMA path: control block (ticket, error word, per-chain counters)
     float *ws_ring;   // chained MFMA path: [B*H, 2, P*N] fp32 hand-off slots of the carried state
+    unsigned long long handoff_ticks;  // chained MFMA path: bound of each hand-off wait (100 MHz ticks)
 };
+
+// Default bound of a hand-off wait of the chained MFMA path: 0.2 s of the
+// 100 MHz device clock, far beyond the microseconds a hand-off takes.
+constexpr unsigned long long kHandoffTicks = 20000000ull;
 
 // Control block of the chained MFMA path: kChainCtlHeader ints (one item
 // ticket counter per XCD, the hand-off error word), then one published-chunk

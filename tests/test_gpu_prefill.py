@@ -353,3 +353,28 @@ def test_stage_timing_is_per_host_thread():
         t.join(timeout=120)
     assert errors == []
     assert {k: v for k, v in seen.items()} == {k: kernels for k, (_, kernels) in jobs.items()}
+
+
+def test_expired_handoff_shows_as_nan_and_the_next_call_is_clean():
+    # chained single pass (320 chains of 8 chunks); with a bound of 0 every
+    # hand-off that does not find its predecessor already published expires,
+    # which must show as NaN in that chain's state and outputs -- not hang --
+    # and leave every other chain and the next call untouched
+    B, L, H = 4, 2048, 80
+    d = synth.make_prefill(B, L, H, 64, 1, 128, "bf16", seed=15)
+    announce("hand-off expiry", f"B={B} L={L} H={H}")
+    y0, f0 = _run(d, 256)
+    assert torch.isfinite(f0).all() and torch.isfinite(y0.float()).all()
+    bd.debug_handoff_ticks(0)
+    try:
+        y1, f1 = _run(d, 256)
+    finally:
+        bd.debug_handoff_ticks(-1)
+    bad = torch.isnan(f1).flatten(2).any(-1)  # (B, H): chains with an expired wait
+    assert bad.any()
+    assert torch.isnan(y1.float().permute(0, 2, 1, 3)[bad]).any(-1).any(-1).all()
+    good = ~bad
+    assert torch.equal(f1[good], f0[good])
+    assert torch.equal(y1.permute(0, 2, 1, 3)[good], y0.permute(0, 2, 1, 3)[good])
+    y2, f2 = _run(d, 256)
+    assert torch.equal(y2, y0) and torch.equal(f2, f0)
