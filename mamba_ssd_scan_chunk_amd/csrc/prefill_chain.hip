@@ -76,6 +76,12 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // chain's hand-offs are serial and too few chains leave them exposed.
 constexpr long kChainMinChains = 256;
 
+// Size of x above which the chained kernel streams x and y (the MI355X
+// Infinity Cache: 256 MB).  Measured on the 2.7B-shaped layer at B = 8,
+// L = 16384 (x and y 1.34 GB each): 1405 us with cached x and y, 1355 with
+// non-temporal x loads, 1375 with non-temporal y stores, 1316 with both.
+constexpr double kStreamBytes = 256.0 * (1 << 20);
+
 constexpr int CH_TK = K3_LDS;       // ticket and wait result
 constexpr int CH_LDS = CH_TK + 16;
 
@@ -103,6 +109,7 @@ __device__ __forceinline__ void xcd_share(int x, long BH, int &lo, int &hi) {
 // accumulator order of a 32x32 MFMA tile.
 __device__ __forceinline__ int acc_row(int acc, int v, int lh) { return 32 * acc + (v >> 2) * 8 + lh * 4 + (v & 3); }
 
+template <bool kNtX, bool kNtY>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_chain_mfma(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char *xt = smem + K3_XT;
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (tid == 0 && c > 0) early = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float dtv = load_dt(a, tok0, Qc, h, tid);
     u32x4 raw[8];
-    load_x_raw(a, tok0, Qc, h, raw, tid);
+    load_x_raw<kNtX>(a, tok0, Qc, h, raw, tid);
     // B operands of the first two token tiles (the rest are streamed)
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[4];
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (exact) {
         // the outputs' exact path takes x' = x
         __syncthreads();
-        load_x_raw(a, tok0, Qc, h, raw, tid);
+        load_x_raw<kNtX>(a, tok0, Qc, h, raw, tid);
         float sc[8];
         x_scales(vt, true, tid, sc);
         store_xt_korder(raw, sc, xt, tid);
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         gB[1][1] = pb1[64];
     }
     __syncthreads();
-    out_tiles(a, it, smem, cop, gA, gB, tid);
+    out_tiles<kNtY>(a, it, smem, cop, gA, gB, tid);
 }
 
 }  // namespace
@@ -359,7 +366,12 @@ hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s) {
     stage_begin();
     hipError_t e = launch_chunk_pack(a, true, a.ws_ctl, s);
     if (e != hipSuccess) return e;
-    return launch_stage("chunk_chain_mfma", chunk_chain_mfma, dim3((unsigned)nitems), dim3(kThreads), CH_LDS, s, a);
+    // x and y larger than the Infinity Cache cannot stay cached for the next
+    // operation anyway: read and write them non-temporally, so that they do
+    // not push the chunks' shared operand tiles out of the L2s
+    const bool stream = (double)a.B * a.L * a.H * kP * 2 >= (double)kStreamBytes;
+    auto kernel = stream ? chunk_chain_mfma<true, true> : chunk_chain_mfma<false, false>;
+    return launch_stage("chunk_chain_mfma", kernel, dim3((unsigned)nitems), dim3(kThreads), CH_LDS, s, a);
 }
 
 }  // namespace ssd

@@ -53,6 +53,9 @@ __device__ __forceinline__ int xcd_item(int i, int total) {
 // index of causal tile (token tile si, column tile lt), si <= lt
 __device__ __forceinline__ int gt_index(int si, int lt) { return lt * (lt + 1) / 2 + si; }
 
+// Cache-policy operand of the buffer builtins marking an access non-temporal.
+constexpr int kCacheNonTemporal = 2;
+
 // Buffer resource over `bytes` bytes from p: loads at or past the end
 // return zeros, which is how the ragged last chunk reads its missing tokens.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes) {
@@ -61,20 +64,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsig
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Non-temporal form (the line is a candidate for early eviction): for data
+// read once that should not push reused operand tiles out of the L2.
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNonTemporal));
+}
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // Load the x chunk of head h ([Q tokens][P] bf16, row stride H*P) whose
 // first token is row tok0: thread t owns the 8x8 block of tokens 8*(t/8)..
-// and features 8*(t%8)..; tokens at or past Qc read as zero.
+// and features 8*(t%8)..; tokens at or past Qc read as zero.  kNt: with
+// non-temporal loads.
+template <bool kNt = false>
 __device__ __forceinline__ void load_x_raw(const PrefillArgs &a, long tok0, int Qc, int h, u32x4 (&raw)[8], int t) {
     const int sb = t >> 3, pb = t & 7;
     const unsigned rs = (unsigned)a.H * kP * 2;  // row stride in bytes
     const bf16_t *x0 = (const bf16_t *)a.x + (tok0 * a.H + h) * kP;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(x0, (unsigned)(Qc - 1) * rs + kP * 2);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) raw[k] = buf_load16(r, (unsigned)(sb * 8 + k) * rs + pb * 16);
+    for (int k = 0; k < 8; ++k) {
+        const unsigned off = (unsigned)(sb * 8 + k) * rs + pb * 16;
+        raw[k] = kNt ? buf_load16_nt(r, off) : buf_load16(r, off);
+    }
 }
 
 // dt of token tid of the chunk (0 at or past Qc), after the optional
@@ -296,6 +309,8 @@ __device__ __forceinline__ void out_first_loads(const OutItem &it, int wave, u32
     gB[1][1] = pb1[64];
 }
 
+// kNtY: the y rows are written with non-temporal stores.
+template <bool kNtY = false>
 __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &it, char *smem, u32x4 (&cop)[8],
                                           u32x4 (&gA)[2][2], u32x4 (&gB)[3][2], int tid) {
     const char *xt = smem + K3_XT;
@@ -366,7 +381,13 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
             const int r = 8 * i + (lane >> 3);
             const u32x4 v = *(const u32x4 *)(st + r * kYRow + 16 * (lane & 7));
             const int l = lt * 32 + r;
-            if (l < it.Qc) *(u32x4 *)((bf16_t *)a.y + ((it.tok0 + l) * a.H + it.h) * kP + 8 * (lane & 7)) = v;
+            if (l < it.Qc) {
+                u32x4 *dst = (u32x4 *)((bf16_t *)a.y + ((it.tok0 + l) * a.H + it.h) * kP + 8 * (lane & 7));
+                if (kNtY)
+                    __builtin_nontemporal_store(v, dst);
+                else
+                    *dst = v;
+            }
         }
     };
 

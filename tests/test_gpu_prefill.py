@@ -134,16 +134,24 @@ def test_prefill_empty_sequence(with_init):
         assert torch.count_nonzero(fs) == 0
 
 
-def test_final_state_may_alias_init_state(oracle):
-    d = synth.make_prefill(1, 150, 2, 16, 1, 16, "f32", seed=3)
-    init = synth.make_state(1, 2, 16, 16, seed=4)
-    st = init.clone().cuda()
+@pytest.mark.parametrize("dtype,B,L,H,P,N,Q", [
+    ("f32", 1, 150, 2, 16, 16, 64),        # vector path
+    ("bf16", 1, 700, 4, 64, 128, 256),     # four MFMA kernels
+    ("bf16", 4, 700, 64, 64, 128, 256),    # chained single pass: chunk 0 reads, the last chunk writes
+    ("bf16", 4, 200, 64, 64, 128, 256),    # chained, one chunk: one workgroup reads and writes
+], ids=["vector", "mfma", "chain", "chain-one-chunk"])
+def test_final_state_may_alias_init_state(oracle, dtype, B, L, H, P, N, Q):
+    d = synth.make_prefill(B, L, H, P, 1, N, dtype, seed=3)
+    init = synth.make_state(B, H, P, N, seed=4)
     dd = dev(d)
-    announce("prefill alias")
-    bd.ssd_prefill(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], st, Q=64, final_state=st)
+    announce("prefill alias", dtype, B, L, H)
+    y_sep, fs_sep = bd.ssd_prefill(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], init.cuda(), Q=Q)
+    st = init.clone().cuda()
+    y = bd.ssd_prefill(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], st, Q=Q, final_state=st)[0]
     torch.cuda.synchronize()
+    assert torch.equal(st, fs_sep) and torch.equal(y, y_sep)
     _, fs_ref = oracle.ssd_scan(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], init)
-    assert rel_err(st, fs_ref) <= TOL_F32
+    assert rel_err(st, fs_ref) <= _tol(dtype)
 
 
 @pytest.mark.parametrize("dtype,P,N,Q,B,H", [("f32", 16, 16, 64, 1, 4), ("bf16", 64, 128, 256, 1, 4),
