@@ -513,7 +513,8 @@ def _prefill_rec(r):
 def bench_other_prefills(args):
     """The other prefill workloads: the 2.7B-shaped layer at B=1, L=4096 in
     place and over rotated inputs, the 130M-shaped layer (B=1, L=4096, H=24),
-    the 2.7B-shaped layer with 512-token chunks and with fp32 activations, and
+    one 65536-token sequence of the 2.7B-shaped layer, the 2.7B-shaped layer
+    with 512-token chunks and with fp32 activations, and
     the B=8 cached decode steps that follow the long-context prefill (a HIP
     graph of 256 steps)."""
     import torch
@@ -522,7 +523,7 @@ def bench_other_prefills(args):
     from mamba_ssd_scan_chunk_amd import synth
 
     out = {}
-    for name in ("mamba2-2.7b-prefill", "mamba2-130m-prefill", "mamba2-2.7b-longctx"):
+    for name in ("mamba2-2.7b-prefill", "mamba2-130m-prefill", "mamba2-2.7b-longctx", "mamba2-2.7b-prefill-64k"):
         if name == args.workload:
             continue
         r = bench_prefill(args, name, extras=False)

@@ -76,12 +76,6 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // chain's hand-offs are serial and too few chains leave them exposed.
 constexpr long kChainMinChains = 256;
 
-// Size of x above which the chained kernel streams x and y (the MI355X
-// Infinity Cache: 256 MB).  Measured on the 2.7B-shaped layer at B = 8,
-// L = 16384 (x and y 1.34 GB each): 1405 us with cached x and y, 1355 with
-// non-temporal x loads, 1375 with non-temporal y stores, 1316 with both.
-constexpr double kStreamBytes = 256.0 * (1 << 20);
-
 constexpr int CH_TK = K3_LDS;       // ticket and wait result
 constexpr int CH_LDS = CH_TK + 16;
 
@@ -366,11 +360,11 @@ hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s) {
     stage_begin();
     hipError_t e = launch_chunk_pack(a, true, a.ws_ctl, s);
     if (e != hipSuccess) return e;
-    // x and y larger than the Infinity Cache cannot stay cached for the next
-    // operation anyway: read and write them non-temporally, so that they do
-    // not push the chunks' shared operand tiles out of the L2s
-    const bool stream = (double)a.B * a.L * a.H * kP * 2 >= (double)kStreamBytes;
-    auto kernel = stream ? chunk_chain_mfma<true, true> : chunk_chain_mfma<false, false>;
+    // streamed x and y (prefill_streams).  Measured on the 2.7B-shaped layer
+    // at B = 8, L = 16384 (x and y 1.34 GB each): 1405 us with cached x and
+    // y, 1355 with non-temporal x loads, 1375 with non-temporal y stores,
+    // 1316 with both
+    auto kernel = prefill_streams(a) ? chunk_chain_mfma<true, true> : chunk_chain_mfma<false, false>;
     return launch_stage("chunk_chain_mfma", kernel, dim3((unsigned)nitems), dim3(kThreads), CH_LDS, s, a);
 }
 

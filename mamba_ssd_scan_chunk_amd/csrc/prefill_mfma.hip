@@ -192,6 +192,7 @@ constexpr int K1_V = K1_XT + kP * kXRow;
 constexpr int K1_W = K1_V + kQ * 4;
 constexpr int K1_LDS = K1_W + 16 * 4;
 
+template <bool kNt>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char *xt = smem + K1_XT;
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     // first: loads retire in issue order, so the cumsum waits for dt only
     const float dtv = load_dt(a, tok0, Qc, h, tid);
     u32x4 raw[8];
-    load_x_raw(a, tok0, Qc, h, raw, tid);
+    load_x_raw<kNt>(a, tok0, Qc, h, raw, tid);
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[kQ / 16];
 #pragma unroll
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
 // chunk, head) in the XCD-aware order, h fastest: the decay bookkeeping of
 // chunk_decay, x' and h_{c-1} into LDS, then out_tiles.
 // ------------------------------------------------------------------------
+template <bool kNt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_out_mfma(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char *xt = smem + K3_XT;
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // dt first: loads retire in issue order, so the cumsum waits for dt only
     const float dtv = load_dt(a, tok0, Qc, h, tid);
     u32x4 raw[8], hv[4];
-    load_x_raw(a, tok0, Qc, h, raw, tid);
+    load_x_raw<kNt>(a, tok0, Qc, h, raw, tid);
     {
         const bf16_t *hg = a.ws_hb + (long)item * kP * kN;
 #pragma unroll
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
     }
     __syncthreads();
-    out_tiles(a, it, smem, cop, gA, gB, tid);
+    out_tiles<kNt>(a, it, smem, cop, gA, gB, tid);
 }
 
 // ------------------------------------------------------------------------
@@ -396,7 +398,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     stage_begin();
     hipError_t e = launch_chunk_pack(a, false, nullptr, s);
     if (e != hipSuccess) return e;
-    e = launch_stage("chunk_state_mfma", chunk_state_mfma, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
+    // streamed x and y (prefill_streams): at B = 1, L = 65536 and B = 2,
+    // L = 32768 (x 671 MB) 959 and 951 us against 971 and 964 with cached x and y
+    const bool stream = prefill_streams(a);
+    e = launch_stage("chunk_state_mfma", stream ? chunk_state_mfma<true> : chunk_state_mfma<false>, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
     const long state_blocks = (total + kThreads - 1) / kThreads;
@@ -405,7 +410,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)(state_blocks + pack_blocks)),
                      dim3(kThreads), 0, s, a, total, state_blocks);
     if (e != hipSuccess) return e;
-    return launch_stage("chunk_out_mfma", chunk_out_mfma, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
+    return launch_stage("chunk_out_mfma", stream ? chunk_out_mfma<true> : chunk_out_mfma<false>, dim3((unsigned)nitems), dim3(kThreads), K3_LDS, s, a);
 }
 
 }  // namespace ssd

@@ -56,6 +56,15 @@ __device__ __forceinline__ int gt_index(int si, int lt) { return lt * (lt + 1) /
 // Cache-policy operand of the buffer builtins marking an access non-temporal.
 constexpr int kCacheNonTemporal = 2;
 
+// x (and so y) larger than the Infinity Cache (256 MB on MI355X) cannot stay
+// cached for the operation after the prefill anyway: the kernels then read x
+// and write y with non-temporal accesses, so that they do not push the
+// chunks' shared operand tiles out of the L2s.
+constexpr double kStreamBytes = 256.0 * (1 << 20);
+__host__ __device__ inline bool prefill_streams(const PrefillArgs &a) {
+    return (double)a.B * a.L * a.H * kP * 2 >= kStreamBytes;
+}
+
 // Buffer resource over `bytes` bytes from p: loads at or past the end
 // return zeros, which is how the ragged last chunk reads its missing tokens.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes) {

@@ -65,6 +65,8 @@ WORKLOADS = {
         Workload("mamba2-130m-decode-b1", 1, 4096, 24, 64, 128, 1, 256, "bf16", decode_steps=4096),
         Workload("mamba2-130m-decode-b16", 16, 4096, 24, 64, 128, 1, 256, "bf16", decode_steps=4096),
         Workload("mamba2-2.7b-longctx", 8, 16384, 80, 64, 128, 1, 256, "bf16", decode_steps=1024),
+        # one long sequence: the four-kernel form (80 chains) at 256 chunks each
+        Workload("mamba2-2.7b-prefill-64k", 1, 65536, 80, 64, 128, 1, 256, "bf16"),
     ]
 }
 
