@@ -28,6 +28,10 @@
 //      h_{c-1} is requested right away and arrives during the chunk state;
 //   4. forms the outputs from x' (still in LDS), h_{c-1} and the packed
 //      operands exactly as the output kernel does (out_tiles).
+// When x exceeds the Infinity Cache (prefill_streams), x is read and y
+// written with non-temporal accesses: the chunks' packed operands, which the
+// heads of a chunk share, then stay in the L2 (one instantiation per
+// policy).
 //
 // Only the carried state travels between workgroups, through two slots per
 // chain (chunk c reads slot (c-1) % 2 and writes slot c % 2): 32 KB written
