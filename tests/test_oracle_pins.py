@@ -352,6 +352,45 @@ def test_decode_with_conv_matches_conv_then_scan(oracle):
     np.testing.assert_allclose(st, fs_ref, rtol=1e-13, atol=1e-13)
 
 
+def test_decode_cache_save_restore_continues_bit_for_bit(oracle):
+    """The O(1) cache (ssm_state, conv_state) is the whole state of a
+    generation (bqwf.cn article §2.1-§2.2): written out as bytes after k
+    steps, read back and continued for m steps, the oracle gives the outputs
+    and the final cache of the uninterrupted k + m steps bit for bit -- the
+    same check the GPU decode runs, on the CPU."""
+    Bsz, H, P, G, N, K, k, m = 2, 3, 4, 1, 8, 4, 5, 6
+    C = H * P + 2 * G * N
+    xbc, dts = synth.make_decode_stream(k + m, Bsz, H, P, G, N, "f32", seed=46)
+    xbc, dts = xbc.numpy().astype(np.float64), dts.numpy().astype(np.float64)
+    w, _ = synth.make_conv(C, K, "f32", seed=47)
+    w = w.numpy().astype(np.float64)
+    d = _inputs(B=Bsz, L=1, H=H, P=P, G=G, N=N, seed=48)
+
+    def steps(st, cst, t0, t1):
+        ys = []
+        for t in range(t0, t1):
+            y, st, cst = oracle.decode_step(xbc[t, :, :H * P], dts[t], d["A_log"], xbc[t, :, H * P:H * P + G * N],
+                                            xbc[t, :, H * P + G * N:], d["D"], st, conv_state=cst, conv_w=w,
+                                            activation=True)
+            ys.append(y)
+        return ys, st, cst
+
+    st0 = synth.make_state(Bsz, H, P, N, seed=49).numpy().astype(np.float64)
+    cst0 = synth.make_conv(C, K, "f32", seed=50)[0].numpy().astype(np.float64)[None, :, :K - 1].repeat(Bsz, 0)
+    ys_a, st_a, cst_a = steps(st0, cst0, 0, k + m)
+    ys_b, st_b, cst_b = steps(st0, cst0, 0, k)
+    blob = (st_b.tobytes(), cst_b.tobytes())  # the whole cache, as bytes
+    st_r = np.frombuffer(blob[0], dtype=np.float64).reshape(st_b.shape).copy()
+    cst_r = np.frombuffer(blob[1], dtype=np.float64).reshape(cst_b.shape).copy()
+    ys_c, st_c, cst_c = steps(st_r, cst_r, k, k + m)
+    assert all(np.array_equal(a, b) for a, b in zip(ys_a, ys_b + ys_c))
+    assert np.array_equal(st_a, st_c) and np.array_equal(cst_a, cst_c)
+    # the cache is not a function of fewer steps: a perturbed restore diverges
+    st_r[0, 0, 0, 0] += 1.0
+    ys_d, _, _ = steps(st_r, cst_r, k, k + m)
+    assert not np.array_equal(ys_d[0], ys_c[0])
+
+
 def test_oracle_rejects_bad_groups(oracle):
     d = _inputs(B=1, L=4, H=3, P=2, G=2, N=2, seed=44)  # G does not divide H
     with pytest.raises(ValueError):
