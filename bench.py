@@ -689,11 +689,16 @@ def main():
     steps = [("prefill", prefill_record), ("decode", decode_record), ("conv", conv_record), ("norm", norm_record),
              ("varlen", varlen_record), ("other", bench_other_prefills), ("copy", copy_record),
              ("gemm", gemm_record)]
+    clocks = {}
     for leg, fn in steps:
         if leg in legs:
             print(f"[bench] {leg}", file=sys.stderr, flush=True)
             out.update(fn(args))
+            if leg in ("prefill", "decode"):
+                clocks[f"after_{leg}"] = gpu_clocks()
             torch.cuda.empty_cache()
+    if clocks:
+        out["clocks"] = clocks
     if HOST_BOUND:
         out["host_bound_legs"] = HOST_BOUND
     if not args.no_cpu_baseline:
@@ -701,6 +706,28 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def gpu_clocks():
+    """Shader (sclk) and memory (mclk) clock levels the GPU is at, in MHz, from
+    the driver's sysfs DPM tables (the level marked '*'), or None where they
+    cannot be read; sampled right after a timed leg, they show the clocks that
+    leg ran at."""
+    import glob
+
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for key in ("sclk", "mclk"):
+            try:
+                with open(os.path.join(dev, f"pp_dpm_{key}")) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            out[f"{key}_mhz"] = int(line.split(":")[1].strip().lower().split("mhz")[0])
+            except (OSError, ValueError, IndexError):
+                pass
+        if out:
+            return out
+    return None
 
 
 def prefill_record(args):

@@ -386,6 +386,19 @@ const char *ssd_stage_name(int index);
  */
 int ssd_debug_handoff_ticks(long long ticks);
 
+/*
+ * Testing aid, kept per host thread: delays at the chained prefill's
+ * hand-off points, to shuffle the order in which workgroups reach them.  For
+ * the calling thread's later calls each workgroup of the chained pass sleeps,
+ * at its start, before it reads the carried state and between writing its
+ * own and publishing it, for a pseudo-random number (a hash of its item) of
+ * rounds of s_sleep 8 (about 0.2 us each) between 0 and max_rounds.  The
+ * results do not depend on the timing, so they must not change.  0 (the
+ * default) turns it off.  Errors: SSD_ERR_INVALID_ARG for max_rounds outside
+ * [0, 100000].
+ */
+int ssd_debug_handoff_jitter(int max_rounds);
+
 /* Static, human-readable text for a status code. */
 const char *ssd_status_string(int status);
 

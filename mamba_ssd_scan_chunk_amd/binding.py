@@ -49,6 +49,7 @@ SIGNATURES = {
     "ssd_stage_times": (_i, [ctypes.POINTER(ctypes.c_float), _i, ctypes.POINTER(_i)]),
     "ssd_stage_name": (ctypes.c_char_p, [_i]),
     "ssd_debug_handoff_ticks": (_i, [ctypes.c_longlong]),
+    "ssd_debug_handoff_jitter": (_i, [_i]),
     "ssd_status_string": (ctypes.c_char_p, [_i]),
     "ssd_last_hip_error": (_i, []),
 }
@@ -467,6 +468,12 @@ def debug_handoff_ticks(ticks: int) -> None:
     """Bound of the chained prefill's hand-off waits for later calls of this
     thread, in 100 MHz device ticks; negative restores the default (0.2 s)."""
     _check("ssd_debug_handoff_ticks", lib().ssd_debug_handoff_ticks(int(ticks)))
+
+
+def debug_handoff_jitter(max_rounds: int) -> None:
+    """Random delays (0 .. max_rounds rounds of s_sleep 8 per point) at the
+    chained prefill's hand-off points for later calls of this thread; 0 = off."""
+    _check("ssd_debug_handoff_jitter", lib().ssd_debug_handoff_jitter(int(max_rounds)))
 
 
 def stage_timing(enable: bool) -> None:

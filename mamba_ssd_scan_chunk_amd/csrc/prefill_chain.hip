@@ -103,6 +103,19 @@ __device__ __forceinline__ void xcd_share(int x, long BH, int &lo, int &hi) {
     hi = (int)((x + 1) * BH / kChainXcds);
 }
 
+// Testing aid (ssd_debug_handoff_jitter): a delay of 0 .. a.handoff_jitter
+// rounds of s_sleep 8, from a hash of `seed`; the seed is uniform, so the
+// whole workgroup sleeps alike.
+__device__ __forceinline__ void jitter_sleep(const PrefillArgs &a, unsigned seed) {
+    if (!a.handoff_jitter) return;
+    unsigned v = seed * 2654435761u;
+    v ^= v >> 15;
+    v *= 2246822519u;
+    v ^= v >> 13;
+    const unsigned n = v % (a.handoff_jitter + 1);
+    for (unsigned i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+}
+
 // Feature row of register v of accumulator acc (lane half lh): the
 // accumulator order of a 32x32 MFMA tile.
 __device__ __forceinline__ int acc_row(int acc, int v, int lh) { return 32 * acc + (v >> 2) * 8 + lh * 4 + (v & 3); }
@@ -155,6 +168,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const long tok0 = ch.tok0;
     const int g = h / (a.H / a.G);
     const long cg = f * a.G + g;
+
+    jitter_sleep(a, (unsigned)bh * 131u + (unsigned)c * 7u + 1u);
 
     // ---- loads: the chain's counter (thread 0), dt (the cumsum waits for
     // these two only), x, the B operands
@@ -267,6 +282,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     load_c_tile(it, wave, cop);
 
     // ---- h_{c-1}: the initial state, or chunk c-1's hand-off
+    jitter_sleep(a, (unsigned)bh * 131u + (unsigned)c * 7u + 2u);
     if (c == 0) {
         const float *init = a.init_state ? a.init_state + (long)bh * kP * kN : nullptr;
 #pragma unroll
@@ -324,6 +340,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                               __float_as_uint(s1[4 * q + 2]), __float_as_uint(s1[4 * q + 3])},
                         rs, slot_off(wave, 1, q, lane));
         }
+        jitter_sleep(a, (unsigned)bh * 131u + (unsigned)c * 7u + 3u);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this thread's slot stores are complete
         __syncthreads();                          // ... and every other thread's
         if (tid == 0) __hip_atomic_store(counter, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

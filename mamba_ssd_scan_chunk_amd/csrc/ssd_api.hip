@@ -17,6 +17,9 @@ thread_local int g_last_hip_error = 0;
 // Bound of the chained prefill's hand-off waits for calls of this thread
 // (ssd_debug_handoff_ticks); negative = the default.
 thread_local long long g_handoff_ticks = -1;
+// Random delays at the chained prefill's hand-off points for calls of this
+// thread (ssd_debug_handoff_jitter); 0 = none.
+thread_local unsigned g_handoff_jitter = 0;
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return SSD_OK;
@@ -280,6 +283,7 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     a.ws_ctl = chain ? (int *)(ws + wl.off_ctl) : nullptr;
     a.ws_ring = chain ? (float *)(ws + wl.off_ring) : nullptr;
     a.handoff_ticks = g_handoff_ticks < 0 ? ssd::kHandoffTicks : (unsigned long long)g_handoff_ticks;
+    a.handoff_jitter = g_handoff_jitter;
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
@@ -592,6 +596,12 @@ SSD_API int ssd_stage_times(float *ms, int capacity, int *count) {
 
 SSD_API int ssd_debug_handoff_ticks(long long ticks) {
     g_handoff_ticks = ticks < 0 ? -1 : ticks;
+    return SSD_OK;
+}
+
+SSD_API int ssd_debug_handoff_jitter(int max_rounds) {
+    if (max_rounds < 0 || max_rounds > 100000) return SSD_ERR_INVALID_ARG;
+    g_handoff_jitter = (unsigned)max_rounds;
     return SSD_OK;
 }
 

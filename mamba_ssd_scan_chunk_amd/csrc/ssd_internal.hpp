@@ -61,6 +61,7 @@ struct PrefillArgs {
     int *ws_ctl;      // chained MFMA path: control block (ticket, error word, per-chain counters)
     float *ws_ring;   // chained MFMA path: [B*H, 2, P*N] fp32 hand-off slots of the carried state
     unsigned long long handoff_ticks;  // chained MFMA path: bound of each hand-off wait (100 MHz ticks)
+    unsigned handoff_jitter;           // chained MFMA path, testing: most s_sleep(8) rounds added per point
 };
 
 // Default bound of a hand-off wait of the chained MFMA path: 0.2 s of the

@@ -43,6 +43,13 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name)
 
 
+def test_debug_knobs_validate_their_arguments(lib):
+    assert lib.ssd_debug_handoff_jitter(-1) == bd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_debug_handoff_jitter(100001) == bd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_debug_handoff_jitter(0) == 0
+    assert lib.ssd_debug_handoff_ticks(-1) == 0
+
+
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert bd.ssd_status_string(code)

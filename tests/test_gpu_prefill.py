@@ -386,3 +386,21 @@ def test_expired_handoff_shows_as_nan_and_the_next_call_is_clean():
     assert torch.equal(y1.permute(0, 2, 1, 3)[good], y0.permute(0, 2, 1, 3)[good])
     y2, f2 = _run(d, 256)
     assert torch.equal(y2, y0) and torch.equal(f2, f0)
+
+
+@pytest.mark.parametrize("B,L,H", [(4, 2048, 80), (9, 777, 29)])
+def test_handoff_jitter_changes_no_result(B, L, H):
+    # the chained single pass with random delays at every hand-off point: the
+    # order in which workgroups start, wait and publish changes, the results
+    # must not (they depend on no timing)
+    d = synth.make_prefill(B, L, H, 64, 1, 128, "bf16", seed=16)
+    init = synth.make_state(B, H, 64, 128, seed=17, scale=0.5)
+    announce("hand-off jitter", f"B={B} L={L} H={H}")
+    y0, f0 = _run(d, 256, init)
+    for rounds in (40, 400):
+        bd.debug_handoff_jitter(rounds)
+        try:
+            y1, f1 = _run(d, 256, init)
+        finally:
+            bd.debug_handoff_jitter(0)
+        assert torch.equal(y1, y0) and torch.equal(f1, f0), rounds
