@@ -388,15 +388,20 @@ hipError_t launch_nr(const DecodeArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Rows per workgroup: 16-row blocks while the grid is small (more
-// workgroups in flight), 4x larger blocks once there are enough of them to
-// fill the machine (measured at B=16, H=80, P=64, N=128: 64-row blocks take
-// 17.5 us per step, 32-row 23.9 us, 16-row 35 us, 128-row 18.3 us).
+// Rows per workgroup, from the number of workgroups the largest blocks
+// (4x the smallest) would make: the smallest blocks below 64 such
+// workgroups (more workgroups in flight), twice the smallest below 128, the
+// largest from there.  Measured per step in a HIP graph, conv on, P = 64,
+// N = 128 (16-, 32- and 64-row blocks), at B = 1 .. 32 on the 2.7B-shaped
+// (H = 80) and 130M-shaped (H = 24) layers: e.g. H = 80, B = 1 (80):
+// 3.99 / 3.81 / 3.98 us; B = 8 (640): 9.53 / 7.90 / 7.53 us; H = 24, B = 2
+// (48): 3.57 / 3.64 / 3.87 us; B = 4 (96): 4.33 / 3.84 / 4.06 us.
 template <typename T, int N>
 hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
     constexpr int base = DecodeShape<N, 1>::ROWS_PER_PASS >= 16 ? 1 : 16 / DecodeShape<N, 1>::ROWS_PER_PASS;
     const long big = (long)a.B * a.H * ((a.P + DecodeShape<N, 4 * base>::PBLK - 1) / DecodeShape<N, 4 * base>::PBLK);
-    if (big >= 1024) return launch_nr<T, N, 4 * base>(a, s);
+    if (big >= 128) return launch_nr<T, N, 4 * base>(a, s);
+    if (big >= 64) return launch_nr<T, N, 2 * base>(a, s);
     return launch_nr<T, N, base>(a, s);
 }
 

@@ -114,6 +114,17 @@ def test_decode_large_grid(oracle, dtype, N, K):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("conv", [False, True])
+def test_decode_mid_grid(oracle, dtype, N, conv):
+    """Between 64 and 128 workgroups of the largest blocks: the launch with
+    blocks twice the smallest (B=5, H=16, P=20: heads cross blocks, the last
+    block of each group is ragged, two groups)."""
+    announce("decode mid grid", dtype, f"N={N}", f"conv={conv}")
+    _run_steps(oracle, 5, 16, 20, 2, N, 4, dtype, 3, 400 + N + conv, conv)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_dense_separate_inputs(oracle, dtype):
     """in_stride = 0: x_t, B_t, C_t are separate dense tensors, no conv."""
     B, H, P, G, N = 3, 6, 64, 3, 128
@@ -131,29 +142,35 @@ def test_decode_dense_separate_inputs(oracle, dtype):
     assert rel_err(state, st_ref) <= TOL_STATE
 
 
-# (batch, sampled (b, h) pairs).  B = 2 runs the 16-row workgroup instance of
-# the decode kernel (B*H*ceil(P/64) = 160 < 1024 blocks); B = 16, the batch
-# the decode bench times, runs the 64-row instance (1280 blocks), whose pairs
-# include heads in the first and the last workgroup of each batch element's
-# group, the first and the last batch element, and workgroups on each of the
-# eight XCDs (workgroup b*80 + h runs on XCD h mod 8).
+# (batch, heads, sampled (b, h) pairs), one case per workgroup instance of
+# the decode kernel: B*H*ceil(P/64) workgroups of 64 rows would be 24 for the
+# 130M-shaped layer at B = 1 (16-row instance), 80 for the 2.7B-shaped layer
+# at B = 1 (32-row instance), 160 at B = 2 and 1280 at B = 16 (64-row
+# instance).  B = 16 is the batch the decode bench times; its pairs include
+# heads in the first and the last workgroup of each batch element's group,
+# the first and the last batch element, and workgroups on each of the eight
+# XCDs (workgroup b*80 + h runs on XCD h mod 8).
 DECODE_4096 = [
-    (2, [(0, 0), (0, 37), (1, 79), (1, 5)]),
-    (16, [(0, 0), (0, 79), (3, 41), (7, 78), (8, 2), (11, 61), (15, 79), (15, 0), (5, 11), (12, 68)]),
+    (1, 24, [(0, 0), (0, 13), (0, 23)]),
+    (1, 80, [(0, 0), (0, 37), (0, 79)]),
+    (2, 80, [(0, 0), (0, 37), (1, 79), (1, 5)]),
+    (16, 80, [(0, 0), (0, 79), (3, 41), (7, 78), (8, 2), (11, 61), (15, 79), (15, 0), (5, 11), (12, 68)]),
 ]
 
 
 @pytest.mark.parametrize("variant", ["spec", "slow"])
-@pytest.mark.parametrize("B,pairs", DECODE_4096, ids=["b2", "b16"])
-def test_decode_4096_steps_2p7b_shape(oracle, variant, B, pairs):
+@pytest.mark.parametrize("B,H,pairs", DECODE_4096, ids=["b1-h24", "b1", "b2", "b16"])
+def test_decode_4096_steps_2p7b_shape(oracle, variant, B, H, pairs):
     """4096 consecutive fused decode steps of a 2.7B-shaped layer (H=80, P=64,
-    N=128, conv C=5376, K=4, bf16 activations, fp32 state).  The oracle starts
-    from the same initial state bits and replays the same raw tokens for
-    sampled (batch, head) pairs; the final fp32 state must agree to 1e-5."""
-    H, P, G, N, K, steps = 80, 64, 1, 128, 4, 4096
-    w_ = synth.WORKLOADS["mamba2-2.7b-decode-b16"]
-    assert (w_.H, w_.P, w_.N, w_.conv_channels) == (H, P, N, 5376)
-    s = _setup(B, H, P, G, N, K, "bf16", steps, seed=300 + (variant == "slow") + 2 * (B == 16), variant=variant)
+    N=128, conv C=5376, K=4, bf16 activations, fp32 state), and of the
+    130M-shaped one (H=24).  The oracle starts from the same initial state
+    bits and replays the same raw tokens for sampled (batch, head) pairs; the
+    final fp32 state must agree to 1e-5."""
+    P, G, N, K, steps = 64, 1, 128, 4, 4096
+    w_ = synth.WORKLOADS["mamba2-2.7b-decode-b16" if H == 80 else "mamba2-130m-decode-b16"]
+    assert (w_.H, w_.P, w_.N, w_.conv_channels) == (H, P, N, H * P + 2 * N)
+    seed = 300 + (variant == "slow") + 2 * (B == 16) + 4 * (B == 1) + 8 * (H == 24)
+    s = _setup(B, H, P, G, N, K, "bf16", steps, seed=seed, variant=variant)
     C = s["C"]
     announce("decode 4096", variant, f"B={B}")
     state = s["state0"].cuda()
