@@ -373,7 +373,7 @@ const char *ssd_stage_name(int index);
 /*
  * Testing aid, kept per host thread: the bound of each hand-off wait of the
  * chained single-pass prefill (the path ssd_prefill takes for bf16, P = 64,
- * N = 128, Q a multiple of 256 and B*H >= 256 chains, where chunk c of a
+ * N = 128, Q a multiple of 256 and B*H >= 192 chains, where chunk c of a
  * (batch, head) chain waits for chunk c-1 to publish its carried state), in
  * ticks of the 100 MHz device clock, for the calling thread's later calls.
  * ticks < 0 restores the default, 0.2 s (20 000 000 ticks).  A wait that

@@ -74,11 +74,13 @@ namespace {
 constexpr int kScopeAgent = 16;
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 constexpr int kWaitVmcnt0 = 0x0F70;
-// Chains needed before the chained form pays.  Measured on the 2.7B-shaped
-// layer (one MI355X, against the four-kernel form): 320 chains (B = 4) and
-// more are 17-31% faster chained, 160 and fewer 5-80% slower, because each
-// chain's hand-offs are serial and too few chains leave them exposed.
-constexpr long kChainMinChains = 256;
+// Chains needed before the chained form pays.  Measured on one MI355X
+// against the four-kernel form: 192 chains (B = 8 of the 130M-shaped layer,
+// H = 24) 160 vs 176 us; 240 (B = 3, H = 80, L = 4096 / 16384) 176 vs 196 and
+// 603 vs 723 us; 320 and more 17-31% faster chained; 160 and fewer 2-80%
+// slower (B = 2, H = 80, L = 8192: 271 vs 251 us), because each chain's
+// hand-offs are serial and too few chains leave them exposed.
+constexpr long kChainMinChains = 192;
 
 constexpr int CH_TK = K3_LDS;       // ticket and wait result
 constexpr int CH_LDS = CH_TK + 16;

@@ -52,7 +52,7 @@ CASES = [
     ("f32-q1024", 1, 2200, 2, 16, 1, 16, 1024, "f32"),
     ("f32-q384-groups", 2, 900, 4, 8, 2, 32, 384, "f32"),
     ("f32-q1000-eq-l", 1, 1000, 1, 4, 1, 8, 1000, "f32"),
-    # the chained single-pass MFMA path (B*H >= 256 chains): ragged last
+    # the chained single-pass MFMA path (B*H >= 192 chains): ragged last
     # chunk, several groups, one chunk per chain (no hand-off), 512-token
     # chunks as 256-token sub-chunks, a chain count that is not a multiple
     # of the eight XCD shares
@@ -61,6 +61,7 @@ CASES = [
     ("chain-one-chunk", 32, 200, 8, 64, 1, 128, 256, "bf16"),
     ("chain-q512", 4, 700, 64, 64, 1, 128, 512, "bf16"),
     ("chain-b9h29", 9, 777, 29, 64, 1, 128, 256, "bf16"),
+    ("chain-b8h24-fewest", 8, 400, 24, 64, 1, 128, 256, "bf16"),  # 192 chains: the fewest that take it
 ]
 
 

@@ -52,7 +52,7 @@ def test_noalloc_rejects_before_any_hip_call():
 PAIRS = [
     [("mamba2-2.7b-prefill", 1, 4096, 80, 64, 1, 128, 256, "bf16"), ("mfma-small", 2, 700, 3, 64, 1, 128, 256, "bf16")],
     [("vector-f32", 2, 900, 4, 16, 2, 32, 64, "f32"), ("vector-f32-small", 1, 130, 2, 16, 1, 32, 64, "f32")],
-    # the chained single pass (B*H >= 256): control block and hand-off slots in the scratch
+    # the chained single pass (B*H >= 192): control block and hand-off slots in the scratch
     [("chain-b4h80", 4, 2048, 80, 64, 1, 128, 256, "bf16"), ("chain-b16h16", 16, 300, 16, 64, 1, 128, 256, "bf16")],
 ]
 
