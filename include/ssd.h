@@ -197,8 +197,12 @@ size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N,
  *   T            total tokens (0 allowed: final_state receives init_state)
  * Empty sequences are allowed (their final state is their initial state).
  * The workspace (ssd_prefill_varlen_workspace_bytes) also holds the chunk
- * table the library builds on the device.  Every other argument, limit,
- * alignment rule and error is as for ssd_prefill; T < 2^31.
+ * table the library builds on the device.  For the chained shape (bf16,
+ * P = 64, N = 128, Q a multiple of 256, B*H >= 192) the call launches both
+ * prefill forms and that table's kernel picks, from the lengths, the one
+ * that does the work (see ssd_debug_packed_form); the workspace then holds
+ * both forms' buffers.  Every other argument, limit, alignment rule and
+ * error is as for ssd_prefill; T < 2^31.
  */
 int ssd_prefill_varlen(int B, int T, int H, int P, int G, int N, int Q, int dtype,
                        const int *cu_seqlens, const void *x, const float *dt, const float *A_log,
@@ -373,7 +377,8 @@ const char *ssd_stage_name(int index);
 /*
  * Testing aid, kept per host thread: the bound of each hand-off wait of the
  * chained single-pass prefill (the path ssd_prefill takes for bf16, P = 64,
- * N = 128, Q a multiple of 256 and B*H >= 192 chains, where chunk c of a
+ * N = 128, Q a multiple of 256 and B*H >= 192 chains, and packed sequences
+ * of that shape whose lengths give enough chains, where chunk c of a
  * (batch, head) chain waits for chunk c-1 to publish its carried state), in
  * ticks of the 100 MHz device clock, for the calling thread's later calls.
  * ticks < 0 restores the default, 0.2 s (20 000 000 ticks).  A wait that
@@ -398,6 +403,22 @@ int ssd_debug_handoff_ticks(long long ticks);
  * [0, 100000].
  */
 int ssd_debug_handoff_jitter(int max_rounds);
+
+/*
+ * Testing aid, kept per host thread: the form of a packed prefill
+ * (ssd_prefill_varlen, ssd_prefill_varlen_dt_raw) that would take the
+ * chained single pass (bf16, P = 64, N = 128, Q a multiple of 256,
+ * B * H >= 192).  Such a call launches both forms and the chunk-table kernel
+ * chooses on the device, from the sequence lengths, which one does the work:
+ * the chained pass when H * (total chunks) / (most chunks of one sequence)
+ * >= 192, else the four-kernel form (a batch dominated by one long sequence
+ * would expose that sequence's hand-offs).  form = -1 (the default) keeps
+ * that choice; 0 forces the four-kernel form and 1 the chained pass, for the
+ * calling thread's later calls.  Both give results within the same bound of
+ * the exact scan; which form ran shows in the output bits only.  Errors:
+ * SSD_ERR_INVALID_ARG for form outside [-1, 1].
+ */
+int ssd_debug_packed_form(int form);
 
 /* Static, human-readable text for a status code. */
 const char *ssd_status_string(int status);

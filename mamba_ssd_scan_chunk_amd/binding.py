@@ -50,6 +50,7 @@ SIGNATURES = {
     "ssd_stage_name": (ctypes.c_char_p, [_i]),
     "ssd_debug_handoff_ticks": (_i, [ctypes.c_longlong]),
     "ssd_debug_handoff_jitter": (_i, [_i]),
+    "ssd_debug_packed_form": (_i, [_i]),
     "ssd_status_string": (ctypes.c_char_p, [_i]),
     "ssd_last_hip_error": (_i, []),
 }
@@ -474,6 +475,12 @@ def debug_handoff_jitter(max_rounds: int) -> None:
     """Random delays (0 .. max_rounds rounds of s_sleep 8 per point) at the
     chained prefill's hand-off points for later calls of this thread; 0 = off."""
     _check("ssd_debug_handoff_jitter", lib().ssd_debug_handoff_jitter(int(max_rounds)))
+
+
+def debug_packed_form(form: int) -> None:
+    """Form of later packed prefills of this thread that may take the chained
+    pass: -1 = chosen on the device from the lengths, 0 = four-kernel, 1 = chained."""
+    _check("ssd_debug_packed_form", lib().ssd_debug_packed_form(int(form)))
 
 
 def stage_timing(enable: bool) -> None:

@@ -74,16 +74,9 @@ namespace {
 constexpr int kScopeAgent = 16;
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 constexpr int kWaitVmcnt0 = 0x0F70;
-// Chains needed before the chained form pays.  Measured on one MI355X
-// against the four-kernel form: 192 chains (B = 8 of the 130M-shaped layer,
-// H = 24) 160 vs 176 us; 240 (B = 3, H = 80, L = 4096 / 16384) 176 vs 196 and
-// 603 vs 723 us; 320 and more 17-31% faster chained; 160 and fewer 2-80%
-// slower (B = 2, H = 80, L = 8192: 271 vs 251 us), because each chain's
-// hand-offs are serial and too few chains leave them exposed.
-constexpr long kChainMinChains = 192;
 
-constexpr int CH_TK = K3_LDS;       // ticket and wait result
-constexpr int CH_LDS = CH_TK + 16;
+constexpr int CH_TK = K3_LDS;       // the item, early counter, wait result
+constexpr int CH_LDS = CH_TK + 48;
 
 // Byte offset in a hand-off slot of the 16 bytes (registers 4q .. 4q+3 of
 // accumulator `acc`) that lane `lane` of wave `wave` holds: 1 KiB contiguous
@@ -99,7 +92,8 @@ __device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, u
 // XCD of the executing workgroup (hardware register XCC_ID, bits 3:0).
 __device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kChainXcds - 1); }
 
-// Chains [lo, hi) of XCD share x: eight contiguous ranges of the B*H chains.
+// Chains [lo, hi) of XCD share x of a uniform batch: eight contiguous ranges
+// of the B*H chains.
 __device__ __forceinline__ void xcd_share(int x, long BH, int &lo, int &hi) {
     lo = (int)(x * BH / kChainXcds);
     hi = (int)((x + 1) * BH / kChainXcds);
@@ -138,36 +132,108 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int li = lane & 31, lh = lane >> 5;
     int *ctl = a.ws_ctl;
 
-    // ---- the item: the next ticket of this XCD's share (chunk-major over
-    // the share's chains), else of the next shares
-    const long BH = (long)a.B * a.H;
+    // ---- the item: the next ticket of this XCD's share, else of the next
+    // shares.  Uniform batches: shares of the (b, h) chains, tickets
+    // chunk-major over the share's chains.  Packed sequences: shares of the
+    // sequences (the chunk table deals them out), tickets over the share's
+    // item order (round c: chunk c of each of its sequences with more than c
+    // chunks) times the H heads, so a chunk's heads follow each other.
+    // Thread 0 names the item by its slot (for an empty sequence, the
+    // sequence), its head and its flags.
     if (tid == 0) {
-        int ic = -1, ibh = 0;
+        int fi = -1, hh = 0, seq = 0, tok = 0, cc = 0, qc = 0;
+        unsigned fl = 0;
         const int x0 = xcd_id();
-        for (int i = 0; i < kChainXcds && ic < 0; ++i) {
+        const bool packed = a.chunks != nullptr;
+        // packed: the header (groups and list start of each share), in flight
+        // with the first ticket
+        u32x4 hdr[5] = {};
+        if (packed)
+#pragma unroll
+            for (int q = 0; q < 5; ++q) hdr[q] = ((const u32x4 *)a.ws_items)[q];
+        static_assert(kItemForm == 16, "the form is the first int of the header's fifth 16 bytes");
+        // The grid of packed sequences is an upper bound of the items.  Exactly
+        // as many workgroups as there are items take tickets (each then gets
+        // one): those below ceil(T / Q) * H always (every sequence has at least
+        // ceil(its length / Q) chunks), the rest only below the header's total
+        // (the last share's list start plus its groups, times H).  The rest exit
+        // without touching the ticket counters, which every real item contends for.
+        // With packed sequences the four-kernel form may run the call instead
+        // (the chunk table's choice): then no workgroup takes a ticket.
+        bool take = true;
+        if (packed && (long)blockIdx.x >= ((long)a.T + a.Q - 1) / a.Q * a.H)
+            take = (long)blockIdx.x < ((long)hdr[3][3] + hdr[1][3]) * a.H;
+        if (packed && hdr[4][0] != 1u) take = false;
+        for (int i = 0; take && i < kChainXcds && fi < 0; ++i) {
             const int x = (x0 + i) & (kChainXcds - 1);
-            int lo, hi;
-            xcd_share(x, BH, lo, hi);
-            if (hi == lo) continue;
+            int lo = 0, hi = a.H;
+            if (!packed) {
+                xcd_share(x, (long)a.B * a.H, lo, hi);
+                if (hi == lo) continue;
+            }
             const long k = __hip_atomic_fetch_add(ctl + kChainTicket + x, 1, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (k < (long)(hi - lo) * a.nchunks) {
-                ic = (int)(k / (hi - lo));
-                ibh = lo + (int)(k - (long)ic * (hi - lo));
+            const long groups = packed ? (long)hdr[x >> 2][x & 3] : a.nchunks;
+            if (k < (long)(hi - lo) * groups) {
+                const long u = k / (hi - lo);
+                const int unit = lo + (int)(k - u * (hi - lo));
+                if (packed) {
+                    const unsigned start = hdr[2 + (x >> 2)][x & 3];
+                    const u32x4 r = ((const u32x4 *)(a.ws_items + kItemHeader))[start + u];
+                    fi = (int)(r[0] & kItemIndex);
+                    fl = (r[0] & kItemLast) | (r[1] & kItemEmpty);
+                    seq = (int)(r[1] & kItemIndex);
+                    tok = (int)r[2];
+                    cc = (int)(r[3] >> kItemQcBits);
+                    qc = (int)(r[3] & ((1u << kItemQcBits) - 1));
+                    hh = unit;
+                } else {
+                    const int b = unit / a.H;
+                    fi = (int)((long)b * a.nchunks + u);
+                    fl = u + 1 == a.nchunks ? kItemLast : 0u;
+                    seq = b;
+                    tok = (int)((long)b * a.L + u * a.Q);
+                    cc = (int)u;
+                    qc = min((long)a.Q, a.L - u * a.Q);
+                    hh = unit - b * a.H;
+                }
             }
         }
-        tk[0] = ic;
-        tk[1] = ibh;
+        if (packed && fi >= 0 && (seq >= a.B || (!(fl & kItemEmpty) && fi >= a.nchunks))) {
+            // never for a table the chunk-table kernel wrote
+            __hip_atomic_fetch_or(ctl + kChainError, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fi = -1;
+        }
+        tk[0] = fi;
+        tk[1] = hh;
+        tk[4] = (int)fl;
+        tk[5] = seq;
+        tk[6] = tok;
+        tk[7] = cc;
+        tk[8] = qc;
     }
     __syncthreads();
-    const int c = __builtin_amdgcn_readfirstlane(tk[0]);
-    const int bh = __builtin_amdgcn_readfirstlane(tk[1]);
-    if (c < 0) return;  // every share handed out (not reached: one workgroup per item)
-    const int b = bh / a.H, h = bh - b * a.H;
-    const long f = (long)b * a.nchunks + c;
-    const ChunkEntry ch = chunk_at(a, f);
-    const int Qc = ch.Qc;
-    const long tok0 = ch.tok0;
+    const int fi = __builtin_amdgcn_readfirstlane(tk[0]);
+    const int h = __builtin_amdgcn_readfirstlane(tk[1]);
+    const unsigned fl = (unsigned)__builtin_amdgcn_readfirstlane(tk[4]);
+    const int b = __builtin_amdgcn_readfirstlane(tk[5]);
+    if (fi < 0) return;  // every share handed out
+    if (fl & kItemEmpty) {
+        // an empty sequence: its state is carried over unchanged
+        if (a.final_state) {
+            const long o = ((long)b * a.H + h) * kP * kN;
+            const float4 *src = (const float4 *)(a.init_state + o);
+            float4 *dst = (float4 *)(a.final_state + o);
+            for (int i = tid; i < kP * kN / 4; i += kThreads) dst[i] = a.init_state ? src[i] : make_float4(0, 0, 0, 0);
+        }
+        return;
+    }
+    const bool last = (fl & kItemLast) != 0;
+    const long f = fi;
+    const int c = __builtin_amdgcn_readfirstlane(tk[7]);
+    const int Qc = __builtin_amdgcn_readfirstlane(tk[8]);
+    const long tok0 = __builtin_amdgcn_readfirstlane(tk[6]);
+    const int bh = b * a.H + h;
     const int g = h / (a.H / a.G);
     const long cg = f * a.G + g;
 
@@ -331,7 +397,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const int p = acc_row(acc, v, lh), n = 32 * wave + li;
             *(bf16_t *)(hl + p * 256 + (((n >> 3) ^ (p & 15)) << 4) + (n & 7) * 2) = f32_to_bf16(hp[acc][v]);
         }
-    if (c + 1 < a.nchunks) {
+    if (!last) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.ws_ring + ((long)bh * 2 + (c & 1)) * kP * kN, kP * kN * 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -378,8 +444,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 bool prefill_uses_chain(int B, int L, int H) { return L > 0 && (long)B * H >= kChainMinChains; }
 
 hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s) {
-    const long nitems = (long)a.B * a.nchunks * a.H;
-    if (nitems > 0x7fffffffL || a.chunks) return hipErrorInvalidConfiguration;
+    // one workgroup per item: B * nchunks * H for a uniform batch; for packed
+    // sequences at most (slots + sequences) * H (an empty sequence counts as
+    // one chunk), and the workgroups past the actual items exit at once
+    const long nitems = (a.chunks ? (long)a.nchunks + a.B : (long)a.B * a.nchunks) * a.H;
+    if (nitems > 0x7fffffffL || (a.chunks && !a.ws_items)) return hipErrorInvalidConfiguration;
     stage_begin();
     hipError_t e = launch_chunk_pack(a, true, a.ws_ctl, s);
     if (e != hipSuccess) return e;

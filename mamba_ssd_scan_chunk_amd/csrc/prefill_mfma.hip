@@ -92,9 +92,11 @@ __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a, int k
     const int part = blockIdx.y % kb, g = blockIdx.y / kb;
     if (ctl && blockIdx.x == 0 && blockIdx.y == 0) {
         // hand-off control block of the chained form: ticket and error word
-        // (once), then the published-chunk counter of each (b, h) chain
+        // (once), then the published-chunk counter of each (b, h) chain (all
+        // B * H of them from the one grid row of packed sequences)
         if (blockIdx.z == 0 && threadIdx.x < kChainCtlHeader) ctl[threadIdx.x] = 0;
-        for (int j = threadIdx.x; j < a.H; j += kThreads) ctl[kChainCtlHeader + blockIdx.z * a.H + j] = 0;
+        const long n = a.chunks ? (long)a.B * a.H : a.H;
+        for (long j = threadIdx.x; j < n; j += kThreads) ctl[kChainCtlHeader + (long)blockIdx.z * a.H + j] = 0;
     }
     const ChunkEntry ch = chunk_at(a, f);
     const int Qc = ch.Qc;
@@ -201,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
+    if (chained_runs(a)) return;
     const int item = xcd_item(blockIdx.x, gridDim.x);  // grid = one workgroup per item
     const int h = item % a.H, bc = item / a.H;
     const ChunkEntry ch = chunk_at(a, bc);
@@ -277,6 +280,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (chained_runs(a)) return;
     const int item = xcd_item(blockIdx.x, gridDim.x);  // grid = one workgroup per item
     const int h = item % a.H, bc = item / a.H;
     const ChunkEntry ch = chunk_at(a, bc);
@@ -333,6 +337,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // past the state blocks pack C for K3 (pack_c).
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long total, long state_blocks) {
+    if (chained_runs(a)) return;
     if ((long)blockIdx.x >= state_blocks) {
         pack_c(a, (long)blockIdx.x - state_blocks);
         return;
@@ -391,13 +396,16 @@ hipError_t launch_chunk_pack(const PrefillArgs &a, bool with_c, int *ctl, hipStr
                         a, kb, ctl);
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s, bool after_chain) {
     const int gridB = a.chunks ? 1 : a.B;  // packed sequences: nchunks slots in all
     const long nitems = (long)gridB * a.nchunks * a.H;
     if (nitems > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    stage_begin();
-    hipError_t e = launch_chunk_pack(a, false, nullptr, s);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!after_chain) {  // else the chained launch has packed the operands, C included
+        stage_begin();
+        e = launch_chunk_pack(a, false, nullptr, s);
+        if (e != hipSuccess) return e;
+    }
     // streamed x and y (prefill_streams): at B = 1, L = 65536 and B = 2,
     // L = 32768 (x 671 MB) 959 and 951 us against 971 and 964 with cached x and y
     const bool stream = prefill_streams(a);
@@ -405,7 +413,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
     const long state_blocks = (total + kThreads - 1) / kThreads;
-    const long pack_blocks = (long)gridB * a.nchunks * a.G * kCBlocks;
+    const long pack_blocks = after_chain ? 0 : (long)gridB * a.nchunks * a.G * kCBlocks;
     if (state_blocks + pack_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)(state_blocks + pack_blocks)),
                      dim3(kThreads), 0, s, a, total, state_blocks);

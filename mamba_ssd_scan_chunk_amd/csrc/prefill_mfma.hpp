@@ -62,7 +62,14 @@ constexpr int kCacheNonTemporal = 2;
 // chunks' shared operand tiles out of the L2s.
 constexpr double kStreamBytes = 256.0 * (1 << 20);
 __host__ __device__ inline bool prefill_streams(const PrefillArgs &a) {
-    return (double)a.B * a.L * a.H * kP * 2 >= kStreamBytes;
+    return (double)a.T * a.H * kP * 2 >= kStreamBytes;  // T token rows: B L, or the packed total
+}
+
+// Packed sequences where the chunk table chooses the form: whether the
+// chained form runs the call, so that the four-kernel form's workgroups exit
+// at once (one scalar load, before any store of the kernel).
+__device__ __forceinline__ bool chained_runs(const PrefillArgs &a) {
+    return a.ws_items && a.ws_items[kItemForm] == 1u;
 }
 
 // Buffer resource over `bytes` bytes from p: loads at or past the end

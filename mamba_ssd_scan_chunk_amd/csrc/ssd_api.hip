@@ -20,6 +20,9 @@ thread_local long long g_handoff_ticks = -1;
 // Random delays at the chained prefill's hand-off points for calls of this
 // thread (ssd_debug_handoff_jitter); 0 = none.
 thread_local unsigned g_handoff_jitter = 0;
+// Form of a packed prefill on the chained path, for this host thread
+// (ssd_debug_packed_form): -1 = the chunk table chooses, 0 = four-kernel, 1 = chained.
+thread_local int g_packed_form = -1;
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return SSD_OK;
@@ -84,11 +87,14 @@ bool prefill_uses_mfma(int P, int N, int Q, int dtype) {
 
 WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q, int G, bool mfma, int nseq,
                                          long chains) {
-    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     if (slots <= 0) return w;
     const size_t heads = (size_t)slots * H;
     const size_t groups = (size_t)slots * G;
     const bool chain = mfma && chains > 0;
+    // packed sequences on the chained path: the chunk table chooses the form
+    // on the device, so the four-kernel form's per-chunk states are there too
+    const bool four = !chain || nseq > 0;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -99,10 +105,10 @@ WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q,
     // instead of per-chunk states
     w.off_ctl = take(chain ? (size_t)(kChainCtlHeader + chains) * sizeof(int) : 0);
     w.off_ring = take(chain ? (size_t)chains * 2 * P * N * sizeof(float) : 0);
-    w.off_S = take(chain ? 0 : heads * P * N * sizeof(float));
-    w.off_dec = take(chain ? 0 : heads * sizeof(float));
+    w.off_S = take(four ? heads * P * N * sizeof(float) : 0);
+    w.off_dec = take(four ? heads * sizeof(float) : 0);
     w.off_cs = take(mfma ? 0 : heads * Q * sizeof(double));
-    w.off_hb = take(mfma && !chain ? heads * P * N * sizeof(uint16_t) : 0);
+    w.off_hb = take(mfma && four ? heads * P * N * sizeof(uint16_t) : 0);
     // MFMA path: G^T tiles in bf16; vector path: the Q x Q masked C B^T in fp32
     w.off_gt = take(mfma ? groups * prefill_mfma_gt_elems_per_chunk() * sizeof(uint16_t)
                          : groups * (size_t)Q * Q * sizeof(float));
@@ -110,6 +116,11 @@ WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q,
     w.off_bt = take(bt_bytes);
     w.off_ct = take(bt_bytes);  // C packed like B
     w.off_tab = take(nseq > 0 ? (size_t)slots * sizeof(ChunkEntry) + (size_t)nseq * sizeof(SeqEntry) : 0);
+    // chained path over packed sequences: the item order, then the chunk-table
+    // kernel's scratch for building it
+    w.off_items = take(chain && nseq > 0 ? (size_t)(chunk_table_item_ints(slots, nseq) +
+                                                    chunk_table_scratch_ints(slots, nseq)) * sizeof(int)
+                                         : 0);
     w.total = off;
     return w;
 }
@@ -130,8 +141,7 @@ long prefill_slots(const PrefillShape &s) {
 }
 // (b, h) chains of the chained MFMA path, 0 when the call takes another path.
 long prefill_chains(const PrefillShape &s) {
-    const bool chain = ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype) && !s.varlen &&
-                       ssd::prefill_uses_chain(s.B, s.L, s.H);
+    const bool chain = ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype) && ssd::prefill_uses_chain(s.B, s.L, s.H);
     return chain ? (long)s.B * s.H : 0;
 }
 ssd::WorkspaceLayout workspace_layout_for(const PrefillShape &s) {
@@ -276,31 +286,44 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
     a.dtp = dtp;
     a.init_state = init_state; a.y = y; a.final_state = final_state;
     char *ws = (char *)workspace;
-    a.ws_S = chain ? nullptr : (float *)(ws + wl.off_S);
-    a.ws_dec = chain ? nullptr : (float *)(ws + wl.off_dec);
+    const bool four = !chain || varlen;  // packed sequences: either form may run
+    a.ws_S = four ? (float *)(ws + wl.off_S) : nullptr;
+    a.ws_dec = four ? (float *)(ws + wl.off_dec) : nullptr;
     a.ws_cs = mfma ? nullptr : (double *)(ws + wl.off_cs);
-    a.ws_hb = mfma && !chain ? (uint16_t *)(ws + wl.off_hb) : nullptr;
+    a.ws_hb = mfma && four ? (uint16_t *)(ws + wl.off_hb) : nullptr;
     a.ws_ctl = chain ? (int *)(ws + wl.off_ctl) : nullptr;
     a.ws_ring = chain ? (float *)(ws + wl.off_ring) : nullptr;
     a.handoff_ticks = g_handoff_ticks < 0 ? ssd::kHandoffTicks : (unsigned long long)g_handoff_ticks;
     a.handoff_jitter = g_handoff_jitter;
+    a.packed_form = g_packed_form;
     a.ws_gt = mfma ? (uint16_t *)(ws + wl.off_gt) : nullptr;
     a.ws_bt = mfma ? (uint16_t *)(ws + wl.off_bt) : nullptr;
     a.ws_ct = mfma ? (uint16_t *)(ws + wl.off_ct) : nullptr;
     a.ws_cb = mfma ? nullptr : (float *)(ws + wl.off_gt);
     a.chunks = nullptr;
     a.seqs = nullptr;
+    a.ws_items = nullptr;
     if (varlen) {
         ssd::ChunkEntry *chunks = (ssd::ChunkEntry *)(ws + wl.off_tab);
         ssd::SeqEntry *seqs = (ssd::SeqEntry *)(ws + wl.off_tab + (size_t)slots * sizeof(ssd::ChunkEntry));
-        hipError_t e = ssd::launch_chunk_table(a, chunks, seqs, stream);
+        unsigned *items = chain ? (unsigned *)(ws + wl.off_items) : nullptr;
+        int *scratch = chain ? (int *)(items + ssd::chunk_table_item_ints(slots, B)) : nullptr;
+        hipError_t e = ssd::launch_chunk_table(a, chunks, seqs, stream, items, scratch);
         if (e != hipSuccess) return hip_status(e);
         a.chunks = chunks;
         a.seqs = seqs;
+        a.ws_items = items;
     }
-    hipError_t e = chain  ? ssd::launch_prefill_chain(a, stream)
-                   : mfma ? ssd::launch_prefill_mfma(a, stream)
-                          : ssd::launch_prefill_vector(a, dtype, stream);
+    hipError_t e;
+    if (chain && varlen) {
+        // both forms; the chunk table's choice runs, the other exits at once
+        e = ssd::launch_prefill_chain(a, stream);
+        if (e == hipSuccess) e = ssd::launch_prefill_mfma(a, stream, true);
+    } else {
+        e = chain  ? ssd::launch_prefill_chain(a, stream)
+            : mfma ? ssd::launch_prefill_mfma(a, stream)
+                   : ssd::launch_prefill_vector(a, dtype, stream);
+    }
     return hip_status(e);
 }
 
@@ -602,6 +625,12 @@ SSD_API int ssd_debug_handoff_ticks(long long ticks) {
 SSD_API int ssd_debug_handoff_jitter(int max_rounds) {
     if (max_rounds < 0 || max_rounds > 100000) return SSD_ERR_INVALID_ARG;
     g_handoff_jitter = (unsigned)max_rounds;
+    return SSD_OK;
+}
+
+SSD_API int ssd_debug_packed_form(int form) {
+    if (form < -1 || form > 1) return SSD_ERR_INVALID_ARG;
+    g_packed_form = form;
     return SSD_OK;
 }
 

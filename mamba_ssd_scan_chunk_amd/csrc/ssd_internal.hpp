@@ -62,6 +62,34 @@ struct PrefillArgs {
     float *ws_ring;   // chained MFMA path: [B*H, 2, P*N] fp32 hand-off slots of the carried state
     unsigned long long handoff_ticks;  // chained MFMA path: bound of each hand-off wait (100 MHz ticks)
     unsigned handoff_jitter;           // chained MFMA path, testing: most s_sleep(8) rounds added per point
+    const unsigned *ws_items;  // chained MFMA path over packed sequences: header + ItemEntry records (chunk-table kernel)
+    int packed_form;           // packed sequences, testing: -1 = the chunk table chooses, 0 = four-kernel, 1 = chained
+};
+
+// Item order of the chained MFMA path over packed sequences, written by the
+// chunk-table kernel.  The sequences, in order of decreasing chunk count, are
+// dealt to the kChainXcds shares in snake order (0..7, 7..0, ...).  Header:
+// items[x] = item groups of share x, items[kChainXcds + x] = where its list
+// starts among the ItemEntry records that follow the header, items[kItemForm]
+// = 1 when the chained form runs the call and 0 when the four-kernel form
+// does (both are launched; the other one's workgroups exit at once).  Record
+// R_x[c] + j of share x's list is chunk c of the share's j-th sequence
+// (R_x[c]: groups in the share's rounds before c); an empty sequence counts as
+// one chunk.
+constexpr unsigned kItemLast = 1u << 31;   // in ItemEntry::f: the sequence's last chunk
+constexpr unsigned kItemEmpty = 1u << 30;  // in ItemEntry::seq: an empty sequence (no slot)
+constexpr unsigned kItemIndex = kItemEmpty - 1;
+constexpr int kItemHeader = 32;            // header ints: 2 kChainXcds, the form, reserved
+constexpr int kItemForm = 16;
+constexpr int kItemQcBits = 9;             // ItemEntry::cq = c << kItemQcBits | Qc, Qc <= 256
+constexpr long kItemMaxSlots = 1L << (31 - kItemQcBits);
+// One item group, read with one 16-byte load: chunk c of sequence seq, in
+// slot f, from token row tok0, Qc tokens.
+struct ItemEntry {
+    unsigned f;    // slot | kItemLast
+    unsigned seq;  // sequence | kItemEmpty
+    int tok0;
+    int cq;
 };
 
 // Default bound of a hand-off wait of the chained MFMA path: 0.2 s of the
@@ -74,11 +102,22 @@ constexpr unsigned long long kHandoffTicks = 20000000ull;
 // call.
 constexpr int kChainCtlHeader = 64;
 constexpr int kChainXcds = 8;      // ticket counters: one per XCD of the MI355X
+static_assert(kItemForm >= 2 * kChainXcds && kItemForm < kItemHeader && kItemHeader % 4 == 0,
+              "item header: groups and list start of each share, then the form");
+// Chains needed before the chained form pays.  Measured on one MI355X
+// against the four-kernel form: 192 chains (B = 8 of the 130M-shaped layer,
+// H = 24) 160 vs 176 us; 240 (B = 3, H = 80, L = 4096 / 16384) 176 vs 196 and
+// 603 vs 723 us; 320 and more 17-31% faster chained; 160 and fewer 2-80%
+// slower (B = 2, H = 80, L = 8192: 271 vs 251 us), because each chain's
+// hand-offs are serial and too few chains leave them exposed.  For packed
+// sequences the chunk-table kernel applies the same bound to the effective
+// chains H * (sum of chunks) / (most chunks of one sequence).
+constexpr long kChainMinChains = 192;
 constexpr int kChainTicket = 0;    // ctl[kChainTicket + x]: tickets taken from XCD x's share
-constexpr int kChainError = 8;
+constexpr int kChainError = 8;     // bit 0: a hand-off wait expired; bit 1: an item index out of range
 
 struct WorkspaceLayout {
-    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, off_tab, off_ctl, off_ring, total;
+    size_t off_S, off_dec, off_cs, off_hb, off_gt, off_bt, off_ct, off_tab, off_ctl, off_ring, off_items, total;
 };
 constexpr int kPrefillMaxQ = 1024;  // largest chunk
 constexpr int kMfmaQ = 256;         // chunk of the MFMA kernels
@@ -93,7 +132,12 @@ WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q,
 // Chunk slots of a packed prefill of T tokens in B sequences: an upper bound
 // of sum over sequences of ceil(L_b / Q).
 inline long varlen_slots(long T, int B, int Q) { return T / Q + B; }
-hipError_t launch_chunk_table(const PrefillArgs &a, ChunkEntry *chunks, SeqEntry *seqs, hipStream_t s);
+// `items` (nullable): also the item order of the chained path, built with
+// `scratch` (chunk_table_scratch_ints(slots, nseq) ints).
+hipError_t launch_chunk_table(const PrefillArgs &a, ChunkEntry *chunks, SeqEntry *seqs, hipStream_t s,
+                              unsigned *items = nullptr, int *scratch = nullptr);
+inline long chunk_table_item_ints(long slots, long nseq) { return kItemHeader + 4 * (slots + nseq); }
+inline long chunk_table_scratch_ints(long slots, long nseq) { return (2 + 2 * kChainXcds) * (slots + 2) + nseq; }
 bool prefill_uses_mfma(int P, int N, int Q, int dtype);
 
 // Stage timing (profiling aid, per host thread).  stage_begin starts a new
@@ -116,13 +160,17 @@ hipError_t launch_stage(const char *name, Kernel kernel, dim3 grid, dim3 block, 
 }
 
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s);
-hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
+// `after_chain`: the call of packed sequences where the chunk table chooses
+// the form; the chained launch before it has run the pack kernel (with C).
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s, bool after_chain = false);
 // The pack kernel alone: G^T tiles and B operands, plus C operands with
 // `with_c`; clears the chained path's control block when `ctl` is given.
 hipError_t launch_chunk_pack(const PrefillArgs &a, bool with_c, int *ctl, hipStream_t s);
-// Chained single-pass MFMA prefill (uniform batches of the MFMA shape).
+// Chained single-pass MFMA prefill (the MFMA shape; for packed sequences
+// followed by launch_prefill_mfma(..., true)).
 hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s);
-// Whether a uniform batch of the MFMA shape runs the chained path.
+// Whether a batch of the MFMA shape runs the chained path (packed sequences:
+// may run it, the chunk table decides).  L: tokens per sequence or the packed total.
 bool prefill_uses_chain(int B, int L, int H);
 hipError_t launch_state_pass(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, size_t n, hipStream_t s);

@@ -48,6 +48,10 @@ def test_debug_knobs_validate_their_arguments(lib):
     assert lib.ssd_debug_handoff_jitter(100001) == bd.SSD_ERR_INVALID_ARG
     assert lib.ssd_debug_handoff_jitter(0) == 0
     assert lib.ssd_debug_handoff_ticks(-1) == 0
+    for bad in (-2, 2):
+        assert lib.ssd_debug_packed_form(bad) == bd.SSD_ERR_INVALID_ARG
+    for ok in (0, 1, -1):
+        assert lib.ssd_debug_packed_form(ok) == 0
 
 
 def test_status_strings(lib):

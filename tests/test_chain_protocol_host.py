@@ -19,7 +19,11 @@ with host threads, one thread per resident workgroup slot:
 The checks: every item runs exactly once, every wait ends, each chunk reads
 the state its predecessor wrote, and no slot is overwritten before its reader
 has read it -- for any placement of workgroups on XCDs, any dispatch timing,
-and any number of resident workgroups down to one.  Planted mistakes must be
+and any number of resident workgroups down to one.  The same holds for the
+item order over packed sequences (PackedProtocol): sequences sorted by chunk
+count and dealt to the shares in snake order, each share's items round by
+round with a chunk's heads on consecutive tickets, and a grid sized to the
+bound (slots + B) * H whose surplus workgroups take no ticket.  Planted mistakes must be
 caught: chunks numbered in reverse (an item then waits on a larger ticket,
 which with one resident workgroup never runs: the bounded wait expires) and a
 read of the wrong slot.
@@ -64,6 +68,12 @@ class Protocol:
                 return k % self.nchunks, lo + k // self.nchunks  # chain-major order
         return None
 
+    def is_last(self, c, bh):
+        return c + 1 == self.nchunks
+
+    def may_take(self, wg):
+        return True
+
     def run_item(self, c, bh, rng, bound_s):
         time.sleep(rng.random() * 2e-4)  # loads and chunk state
         if c > 0:
@@ -83,7 +93,7 @@ class Protocol:
             if got != (bh, c - 1):
                 self.errors.append(f"chunk {c} of chain {bh} read {got}")
         time.sleep(rng.random() * 1e-4)
-        if c + 1 < self.nchunks:
+        if not self.is_last(c, bh):
             with self.lock:
                 if not self.slot_read[bh][c % 2]:
                     self.errors.append(f"chunk {c} of chain {bh} overwrote an unread slot")
@@ -98,19 +108,27 @@ class Protocol:
 
 
 def run_grid(proto, resident, seed, placement, bound_s=2.0):
-    """One workgroup per item, `resident` of them at a time; returns after all ran."""
-    nitems = proto.BH * proto.nchunks
+    """One workgroup per grid entry, `resident` of them at a time; returns after all ran."""
+    nitems = proto.grid_size() if hasattr(proto, "grid_size") else proto.BH * proto.nchunks
     rng_master = random.Random(seed)
     launch = iter(range(nitems))
     launch_lock = threading.Lock()
 
     def slot(sid):
+        try:
+            run_slot(sid)
+        except Exception as e:  # a broken model must fail the test, not just its thread
+            proto.errors.append(repr(e))
+
+    def run_slot(sid):
         rng = random.Random(rng_master.random() + sid)
         while True:
             with launch_lock:
                 wg = next(launch, None)
             if wg is None:
                 return
+            if not proto.may_take(wg):
+                continue
             x = wg % XCDS if placement == "round-robin" else rng.randrange(XCDS)
             item = proto.take(x)
             if item is None:
@@ -178,3 +196,90 @@ def test_planted_mistakes_are_caught(mistake, resident, expect):
     bad = mistake(1, 16, 4)
     run_grid(bad, resident=resident, seed=7, placement="round-robin", bound_s=0.05)
     assert bad.errors and expect in bad.errors[0]
+
+
+class PackedProtocol(Protocol):
+    """The item order over packed sequences: chains are (sequence, head); a
+    sequence of n chunks is a chain of n items (an empty one: one item that
+    neither waits nor publishes)."""
+
+    def __init__(self, lengths, H, Q=256):
+        self.n = [(L + Q - 1) // Q for L in lengths]
+        self.B, self.H, self.Q, self.T = len(lengths), H, Q, sum(lengths)
+        super().__init__(len(lengths), H, 1)
+        order = sorted(range(len(lengths)), key=lambda b: -max(self.n[b], 1))  # any order among equal counts
+        shares = [[] for _ in range(XCDS)]
+        for j, b in enumerate(order):
+            q, r = divmod(j, XCDS)
+            shares[XCDS - 1 - r if q & 1 else r].append(b)
+        self.lists = []
+        for seqs in shares:
+            rounds = max([max(self.n[b], 1) for b in seqs], default=0)
+            self.lists.append([(b, c) for c in range(rounds) for b in seqs if c < max(self.n[b], 1)])
+        self.total = sum(len(lst) for lst in self.lists)
+        self.nslots = self.T // Q + len(lengths)  # chunk slots the workspace is sized for
+
+    def grid_size(self):
+        return (self.nslots + self.B) * self.H
+
+    def may_take(self, wg):
+        # below ceil(T / Q) * H always; above, only below the item count
+        return wg < -(-self.T // self.Q) * self.H or wg < self.total * self.H
+
+    def take(self, x0):
+        for i in range(XCDS):
+            x = (x0 + i) % XCDS
+            with self.lock:
+                k = self.tickets[x]
+                self.tickets[x] += 1
+            if k < len(self.lists[x]) * self.H:
+                b, c = self.lists[x][k // self.H]
+                return c, b * self.H + k % self.H
+        return None
+
+    def is_last(self, c, bh):
+        return c + 1 >= self.n[bh // self.H]
+
+
+@pytest.mark.parametrize("lengths,H", [
+    ([2388, 211, 786, 1624, 0, 2881, 71, 394, 66, 3821, 1672], 3),
+    ([0, 1, 255, 256, 257, 0, 700, 31], 4),
+    ([5000, 3, 0, 1300], 5),
+    ([300] * 17, 2),
+])
+@pytest.mark.parametrize("resident", [1, 3, 17])
+@pytest.mark.parametrize("placement", ["round-robin", "random"])
+def test_packed_items_run_once_and_read_their_predecessor(lengths, H, resident, placement):
+    proto = PackedProtocol(lengths, H)
+    run_grid(proto, resident, seed=len(lengths) * 100 + H * 10 + resident, placement=placement)
+    assert proto.errors == []
+    want = {(c, b * H + h) for b, n in enumerate(proto.n) for c in range(max(n, 1)) for h in range(H)}
+    assert set(proto.done) == want and set(proto.done.values()) == {1}
+    # no surplus workgroup of the bound grid took a ticket: exactly one per item
+    assert sum(min(t, len(lst) * H) for t, lst in zip(proto.tickets, proto.lists)) == len(want)
+    assert proto.counter == [max(n - 1, 0) for n in proto.n for _ in range(H)]
+
+
+class PackedRoundsReversed(PackedProtocol):
+    """Planted mistake: each share lists its rounds last first, so chunk c of
+    a sequence comes before its chunk c-1."""
+
+    def __init__(self, lengths, H):
+        super().__init__(lengths, H)
+        self.lists = [sorted(lst, key=lambda bc: -bc[1]) for lst in self.lists]
+
+
+class PackedSurplusTakes(PackedProtocol):
+    """Planted mistake: every workgroup of the bound grid tries the counters."""
+
+    def may_take(self, wg):
+        return True
+
+
+def test_packed_planted_mistakes_are_caught():
+    bad = PackedRoundsReversed([600, 300, 1000], 2)
+    run_grid(bad, resident=1, seed=3, placement="round-robin", bound_s=0.05)
+    assert bad.errors and "expired" in bad.errors[0]
+    surplus = PackedSurplusTakes([600, 300, 1000], 2)
+    run_grid(surplus, resident=3, seed=3, placement="round-robin")
+    assert any("found no item" in e for e in surplus.errors)

@@ -145,14 +145,16 @@ def _capture(call):
     return g
 
 
-def test_packed_serving_graph_replays_match_eager(oracle):
+@pytest.mark.parametrize("H,lengths", [(4, [300, 0, 1, 513, 40]), (64, [300, 0, 1, 513, 40, 700, 260])],
+                         ids=["four-kernel-h4", "chained-h64"])
+def test_packed_serving_graph_replays_match_eager(oracle, H, lengths):
     """conv over packed prompts, the packed prefill (its chunk tables built on
     the device inside the graph) and the gated normalisation of its output,
     captured as one graph: every replay equals the eager result, and the
     oracle's conv, scan and normalisation (the last on the GPU's y, its
-    exact input)."""
-    H, P, G, N, K = 4, 64, 1, 128, 4
-    lengths = [300, 0, 1, 513, 40]
+    exact input).  At H = 64 the prefill launches both forms and the chunk
+    table picks the chained pass (64 * 12 chunks / 3 >= 192)."""
+    P, G, N, K = 64, 1, 128, 4
     T, C = sum(lengths), H * P + 2 * G * N
     dc = synth.make_varlen(lengths, H, P, G, N, "bf16", seed=76)
     d = {k: v.cuda() for k, v in dc.items()}
@@ -183,7 +185,7 @@ def test_packed_serving_graph_replays_match_eager(oracle):
                               final_state=fs, workspace=pws)
         bd.ssd_gated_rmsnorm(y.reshape(T, H * P), z, nw, group=H * P, out=out)
 
-    announce("graph packed serving")
+    announce("graph packed serving", H)
     call()
     torch.cuda.synchronize()
     ref = [t.clone() for t in (cst, xc, y, fs, out)]

@@ -1,5 +1,7 @@
 """GPU parity of ssd_prefill_varlen (sequences packed without padding)
 against the CPU oracle, through the C ABI."""
+import contextlib
+
 import numpy as np
 import pytest
 import torch
@@ -57,11 +59,110 @@ def test_varlen_matches_oracle(oracle, path, mix, with_init):
                 assert torch.equal(fs[b].cpu(), init[b])
 
 
-@pytest.mark.parametrize("path", PATHS[:2], ids=[p[0] for p in PATHS[:2]])
+# Packed sequences of the chained shape (bf16, P = 64, N = 128, a chunk
+# length that is a multiple of 256, sequences x heads >= 192) launch both
+# forms; the chunk-table kernel picks the chained pass when the effective
+# chains H * (total chunks) / (most chunks of one sequence) reach 192, else
+# the four-kernel form.  Each case runs both forms forced and the choice.
+CHAIN_CASES = [
+    # id, lengths, H, G
+    ("edges-h64", MIXES["edges"], 64, 2),  # 64 * 9 / 3 = 192: chained, at the bound
+    ("many-short-h32", MIXES["many-short"], 32, 2),
+    ("one-h192", [600], 192, 2),
+    ("balanced-long-h32", [1500, 1400, 1300, 1536, 0, 1200, 1100, 1000], 32, 2),
+    ("long-and-short-h32", [5000, 3, 0, 1300, 256, 2049], 32, 4),  # 32 * 37 / 20: four-kernel
+    ("one-dominates-h64", [6000, 100, 50, 0], 64, 2),
+]
+DUAL_STAGES = ["chunk_pack_mfma", "chunk_chain_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]
+
+
+def _chained_by_lengths(lengths, H, Q=256):
+    n = [(L + Q - 1) // Q for L in lengths]
+    return max(n) > 0 and H * sum(n) >= 192 * max(n)
+
+
+@contextlib.contextmanager
+def packed_form(form):
+    bd.debug_packed_form(form)
+    try:
+        yield
+    finally:
+        bd.debug_packed_form(-1)
+
+
+def _run_staged(d, Q, init=None, final_state=None):
+    """_run with stage timing on: (y, final_state, kernels that ran)."""
+    dd = dev(d)
+    bd.stage_timing(True)
+    try:
+        y, fs = bd.ssd_prefill_varlen(dd["x"], dd["dt"], dd["A_log"], dd["Bm"], dd["Cm"], dd["D"], dd["cu_seqlens"],
+                                      init, Q=Q, final_state=final_state)
+        torch.cuda.synchronize()
+        st = [name for name, _ in bd.stage_times()]
+    finally:
+        bd.stage_timing(False)
+    return y, fs, st
+
+
+def test_chained_choice_by_lengths():
+    assert [_chained_by_lengths(c[1], c[2]) for c in CHAIN_CASES] == [True, True, True, True, False, False]
+    assert _chained_by_lengths(synth.make_lengths(16, 64, 4096, seed=9), 80)  # the serving mix
+
+
+@pytest.mark.parametrize("case", CHAIN_CASES, ids=[c[0] for c in CHAIN_CASES])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_varlen_chained_matches_oracle(oracle, case, with_init):
+    name, lengths, H, G = case
+    d = synth.make_varlen(lengths, H, 64, G, 128, "bf16", seed=750 + len(lengths))
+    init = synth.make_state(len(lengths), H, 64, 128, seed=751, scale=0.5) if with_init else None
+    y_ref, fs_ref = oracle.ssd_scan_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["cu_seqlens"], d["D"],
+                                           init)
+    out = {}
+    for form in (1, 0, -1):
+        announce("varlen chained", name, with_init, "form", form)
+        with packed_form(form):
+            y, fs, st = _run_staged(d, 256, None if init is None else init.cuda())
+        assert st == DUAL_STAGES, form
+        assert rel_err(y, y_ref) <= TOL_BF16, form
+        assert rel_err(fs, fs_ref) <= TOL_BF16, form
+        for b, n in enumerate(lengths):  # an empty sequence hands its state on unchanged
+            if n == 0:
+                want = init[b] if init is not None else torch.zeros_like(fs[b].cpu())
+                assert torch.equal(fs[b].cpu(), want), form
+        out[form] = (y, fs)
+    chosen = out[1 if _chained_by_lengths(lengths, H) else 0]
+    assert torch.equal(out[-1][0], chosen[0]) and torch.equal(out[-1][1], chosen[1])
+
+
+@pytest.mark.parametrize("form", [1, 0])
+def test_varlen_chained_final_state_may_alias_init_state(oracle, form):
+    """final_state is init_state: the state of an empty sequence is copied
+    onto itself; every other sequence reads its initial state before its
+    last chunk writes the final one."""
+    lengths = [700, 0, 1, 256, 0, 513]
+    H = 48
+    d = synth.make_varlen(lengths, H, 64, 1, 128, "bf16", seed=752)
+    init = synth.make_state(len(lengths), H, 64, 128, seed=753, scale=0.5)
+    announce("varlen chained alias", form)
+    with packed_form(form):
+        y_sep, fs_sep, st = _run_staged(d, 256, init.cuda())
+        assert st == DUAL_STAGES
+        buf = init.clone().cuda()
+        y, _, _ = _run_staged(d, 256, buf, final_state=buf)
+    assert torch.equal(buf, fs_sep) and torch.equal(y, y_sep)
+    _, fs_ref = oracle.ssd_scan_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["cu_seqlens"], d["D"], init)
+    assert rel_err(buf, fs_ref) <= TOL_BF16
+
+
+EQUAL_PATHS = PATHS[:2] + [("chain", 64, 64, 2, 128, 256, "bf16")]
+
+
+@pytest.mark.parametrize("path", EQUAL_PATHS, ids=[p[0] for p in EQUAL_PATHS])
 def test_varlen_equal_lengths_bitwise_equals_batched(path):
-    """Equal lengths: the same chunks as the batched call, the same bits."""
+    """Equal lengths: the same chunks as the batched call, the same bits (on
+    the chained path, packed item order against the batched one)."""
     name, H, P, G, N, Q, dtype = path
-    B, L = 3, 520
+    B, L = 4, 520
     d = synth.make_prefill(B, L, H, P, G, N, dtype, seed=702)
     init = synth.make_state(B, H, P, N, seed=703, scale=0.5).cuda()
     dd = dev(d)
