@@ -1,5 +1,5 @@
 // prefill_chain.hip -- chained single-pass SSD prefill on bf16 MFMA (gfx950),
-// P = 64, N = 128, 256-token chunks, uniform batches.
+// P = 64, N = 128, 256-token chunks, uniform batches and packed sequences.
 //
 // The chunked scan of arXiv 2603.09555 as the bqwf.cn article on its
 // compiler-first Mamba-2 implementation lays it out: §1.1 (dense work inside
@@ -15,7 +15,12 @@
 //      chains are split into eight contiguous shares, one per XCD, each
 //      with its own counter: a workgroup takes from the share of the XCD it
 //      runs on (the heads of a chunk then share one L2 for the chunk's
-//      packed operands), and from the next shares once its own is used up;
+//      packed operands), and from the next shares once its own is used up.
+//      Packed sequences: the chunk-table kernel deals the sequences (by
+//      chunk count, snake order) to the shares and lists each share's items
+//      round by round, one 16-byte record per chunk; a chunk's heads take
+//      consecutive tickets.  The grid is then an upper bound of the items,
+//      and the workgroups past the item count exit without a ticket;
 //   2. loads x and dt once, forms x' in LDS, and the chunk state
 //        S_c = exp(cs_last - R_7) sum_k (prod_{j > k} Q_j) x'^T_k B_k
 //      on MFMA (the same tile references R_k and ratios Q_k as the outputs
@@ -56,8 +61,11 @@
 // same counter and so is held by a running or finished workgroup; the
 // unfinished item of smallest chunk index therefore always progresses.
 // Every workgroup takes exactly one item: the grid has one workgroup per
-// item, and a workgroup moves on to another share only when its counter has
-// handed out all of that share.  Every wait is bounded (by default 0.2 s of
+// item (packed sequences: exactly as many workgroups as items try), and a
+// workgroup moves on to another share only when its counter has handed out
+// all of that share.  Packed sequences launch the four-kernel form after this
+// kernel as well; the chunk table chooses which of the two does the work,
+// and the other's workgroups exit at once.  Every wait is bounded (by default 0.2 s of
 // the 100 MHz wall clock, far beyond the microseconds a hand-off takes; the
 // bound is a kernel argument that ssd_debug_handoff_ticks sets per host
 // thread for tests): on expiry the workgroup sets the control block's error
