@@ -70,8 +70,11 @@
 // bound is a kernel argument that ssd_debug_handoff_ticks sets per host
 // thread for tests): on expiry the workgroup sets the control block's error
 // word and carries NaN, so a broken hand-off shows as NaN outputs instead of
-// a hang.  The pack kernel clears the control block at the start of every
-// call.
+// a hang.  It also sets a sticky bit in the chain's counter (counters are
+// only raised: publishing is an atomic max), and every later chunk of the
+// chain that sees the bit carries NaN as well, whatever its slot holds: a
+// late predecessor may still overwrite a slot after its successor gave up.
+// The pack kernel clears the control block at the start of every call.
 #include "prefill_mfma.hpp"
 
 namespace ssd {
@@ -82,6 +85,9 @@ namespace {
 constexpr int kScopeAgent = 16;
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 constexpr int kWaitVmcnt0 = 0x0F70;
+// Bit of a chain's counter set when one of its waits expired (sticky: the
+// counter is only ever raised, by atomic max and OR).
+constexpr int kChainPoison = 1 << 30;
 
 constexpr int CH_TK = K3_LDS;       // the item, early counter, wait result
 constexpr int CH_LDS = CH_TK + 48;
@@ -268,6 +274,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // ---- h_{c-1} requested now if chunk c-1 had published by the start
     // (the counter was read before the barriers above)
     const bool ready = c > 0 && tk[2] >= c;
+    const bool early_poison = (tk[2] & kChainPoison) != 0;
     float hp[2][16];
     const __amdgpu_buffer_rsrc_t hrs = make_rsrc(a.ws_ring + ((long)bh * 2 + ((c - 1) & 1)) * kP * kN, kP * kN * 4);
     auto load_h = [&]() {
@@ -369,16 +376,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     } else if (!ready) {
         if (tid == 0) {
             const unsigned long long t0 = wall_clock64();
-            int ok = 1;
-            while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c) {
+            int ok = 1, seen;
+            while ((seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < c) {
                 __builtin_amdgcn_s_sleep(2);
                 if (wall_clock64() - t0 > a.handoff_ticks) {
+                    // expired: mark the chain, so that every later chunk takes
+                    // NaN as well (a late predecessor may still write its slot)
                     ok = 0;
+                    __hip_atomic_fetch_or(counter, kChainPoison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_fetch_or(ctl + kChainError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
-            tk[3] = ok;
+            tk[3] = ok && !(seen & kChainPoison);
         }
         __syncthreads();
         load_h();
@@ -388,6 +398,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
                 for (int v = 0; v < 16; ++v) hp[acc][v] = __builtin_nanf("");
         }
+    }
+
+    if (ready && early_poison) {  // an earlier chunk of the chain expired
+#pragma unroll
+        for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) hp[acc][v] = __builtin_nanf("");
     }
 
     // ---- h_c, rounded once: h + (expm1(cs_last) h + S); h_{c-1} into LDS
@@ -419,7 +436,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         jitter_sleep(a, (unsigned)bh * 131u + (unsigned)c * 7u + 3u);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this thread's slot stores are complete
         __syncthreads();                          // ... and every other thread's
-        if (tid == 0) __hip_atomic_store(counter, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the counter only grows: a predecessor that publishes after this
+        // chunk's wait expired cannot move it back
+        if (tid == 0) __hip_atomic_fetch_max(counter, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (a.final_state) {
         float *fs = a.final_state + (long)bh * kP * kN + 32 * wave + li;
 #pragma unroll

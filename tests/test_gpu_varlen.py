@@ -323,3 +323,59 @@ def test_varlen_dt_raw_matches_oracle(oracle, path):
     y_ref, fs_ref = oracle.ssd_scan_varlen(d["x"], dt_ref, d["A_log"], d["Bm"], d["Cm"], d["cu_seqlens"], d["D"], init)
     assert rel_err(y, y_ref) <= _tol(dtype)
     assert rel_err(fs, fs_ref) <= _tol(dtype)
+
+
+JITTER_MIX = [1500, 1400, 0, 1300, 1536, 1200, 1100, 1000, 3]  # 32 * 39 / 6 = 208 chains: chained
+
+
+def test_varlen_chained_handoff_jitter_changes_no_result():
+    """The packed item order with random delays at every hand-off point: the
+    order in which workgroups start, wait and publish changes, the results
+    must not."""
+    H = 32
+    assert _chained_by_lengths(JITTER_MIX, H)
+    d = synth.make_varlen(JITTER_MIX, H, 64, 2, 128, "bf16", seed=760)
+    init = synth.make_state(len(JITTER_MIX), H, 64, 128, seed=761, scale=0.5).cuda()
+    announce("varlen hand-off jitter")
+    y0, f0, st = _run_staged(d, 256, init)
+    assert st == DUAL_STAGES
+    for rounds in (40, 400):
+        bd.debug_handoff_jitter(rounds)
+        try:
+            y1, f1, _ = _run_staged(d, 256, init)
+        finally:
+            bd.debug_handoff_jitter(0)
+        assert torch.equal(y1, y0) and torch.equal(f1, f0), rounds
+
+
+def test_varlen_chained_expired_handoff_shows_as_nan_and_the_next_call_is_clean():
+    """With a wait bound of 0, every hand-off that does not find its
+    predecessor already published expires: NaN in that (sequence, head)
+    chain, never a hang.  Sequences of one chunk (and empty ones) never wait,
+    so their results are untouched, and the next call is clean."""
+    H = 32
+    d = synth.make_varlen(JITTER_MIX, H, 64, 2, 128, "bf16", seed=762)
+    announce("varlen hand-off expiry")
+    with packed_form(1):
+        y0, f0, _ = _run_staged(d, 256)
+        bd.debug_handoff_ticks(0)
+        try:
+            y1, f1, _ = _run_staged(d, 256)
+        finally:
+            bd.debug_handoff_ticks(-1)
+        y2, f2, _ = _run_staged(d, 256)
+    assert torch.isfinite(f0).all() and torch.isfinite(y0.float()).all()
+    bad = torch.isnan(f1).flatten(2).any(-1)  # (sequence, head): chains with an expired wait
+    assert bad.any()
+    cu = d["cu_seqlens"].tolist()
+    for b, n in enumerate(JITTER_MIX):
+        rows = slice(cu[b], cu[b + 1])
+        if n <= 256:  # one chunk or empty: nothing to wait for
+            assert not bad[b].any()
+            assert torch.equal(f1[b], f0[b]) and torch.equal(y1[rows], y0[rows])
+        for h in range(H):
+            if bad[b, h]:
+                assert torch.isnan(y1[rows, h].float()).any()
+            else:
+                assert torch.equal(f1[b, h], f0[b, h]) and torch.equal(y1[rows, h], y0[rows, h])
+    assert torch.equal(y2, y0) and torch.equal(f2, f0)
