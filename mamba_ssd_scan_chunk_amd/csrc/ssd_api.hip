@@ -141,7 +141,11 @@ long prefill_slots(const PrefillShape &s) {
 }
 // (b, h) chains of the chained MFMA path, 0 when the call takes another path.
 long prefill_chains(const PrefillShape &s) {
-    const bool chain = ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype) && ssd::prefill_uses_chain(s.B, s.L, s.H);
+    bool chain = ssd::prefill_uses_mfma(s.P, s.N, s.Q, s.dtype) && ssd::prefill_uses_chain(s.B, s.L, s.H);
+    // packed sequences: the item records hold a slot below kItemMaxSlots and a
+    // sequence index below kItemIndex; beyond that the four-kernel form runs
+    if (chain && s.varlen && (prefill_slots(s) >= ssd::kItemMaxSlots || (long)s.B >= (long)ssd::kItemIndex))
+        chain = false;
     return chain ? (long)s.B * s.H : 0;
 }
 ssd::WorkspaceLayout workspace_layout_for(const PrefillShape &s) {

@@ -399,3 +399,18 @@ def test_stage_timing_queries_without_a_timed_call(lib):
     assert lib.ssd_stage_times(None, 0, None) == bd.SSD_ERR_INVALID_ARG
     assert lib.ssd_stage_times(None, 4, ctypes.byref(n)) == bd.SSD_ERR_INVALID_ARG
     assert lib.ssd_stage_name(0) is None and lib.ssd_stage_name(-1) is None
+
+
+def test_packed_chained_workspace_stops_at_the_item_record_limit(lib):
+    # Packed sequences of the chained shape (B*H >= 192) hold both prefill
+    # forms' buffers and the item order.  An item record holds a slot below
+    # 2^22; from that many slots on the call runs the four-kernel form alone,
+    # so its workspace drops by the chained form's regions, then grows again.
+    H, P, G, N, Q = 192, 64, 1, 128, 256
+    cap_T = ((1 << 22) - 1) * Q  # slots = T / Q + B = 2^22 at B = 1
+    below, at, above = (lib.ssd_prefill_varlen_workspace_bytes(1, T, H, P, G, N, Q, bd.SSD_BF16)
+                        for T in (cap_T - Q, cap_T, cap_T + Q))
+    assert at < below and at < above
+    # below the bound of 192 chains the four-kernel layout alone
+    assert lib.ssd_prefill_varlen_workspace_bytes(1, 4096, 191, P, G, N, Q, bd.SSD_BF16) < \
+        lib.ssd_prefill_varlen_workspace_bytes(1, 4096, 192, P, G, N, Q, bd.SSD_BF16)
