@@ -306,11 +306,15 @@ def test_packed_prompts_then_decode(oracle):
     assert rel_err(state, st2) <= TOL_BF16
 
 
-@pytest.mark.parametrize("path", PATHS[:2], ids=[p[0] for p in PATHS[:2]])
+DT_RAW_PATHS = PATHS[:2] + [("chain", 64, 64, 2, 128, 256, "bf16")]  # edges at H = 64: 192 effective chains
+
+
+@pytest.mark.parametrize("path", DT_RAW_PATHS, ids=[p[0] for p in DT_RAW_PATHS])
 def test_varlen_dt_raw_matches_oracle(oracle, path):
     """Packed sequences with the step preprocessed in the kernels."""
     name, H, P, G, N, Q, dtype = path
     lengths = MIXES["edges"]
+    assert name != "chain" or _chained_by_lengths(lengths, H)
     d = synth.make_varlen(lengths, H, P, G, N, dtype, seed=740)
     raw, dt_bias = synth.make_dt_raw((sum(lengths),), H, seed=741)
     init = synth.make_state(len(lengths), H, P, N, seed=742, scale=0.5)
