@@ -45,6 +45,7 @@ namespace ssd {
 namespace {
 
 constexpr int kCBlocks = kTiles / 2;  // C packing: two token tiles per workgroup
+constexpr long kDualStateBlocks = 4096;  // state-pass grid after the chained launch of packed sequences
 
 // C in the order of the output kernel's operand: block (b, c, g, q) writes
 // token tiles 2q, 2q+1 as [lt][kk][lane] 16 bytes = C[32 lt + li][16 kk +
@@ -90,13 +91,22 @@ __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a, int k
     __shared__ __attribute__((aligned(16))) char bl[kQ * 64];  // B[:, 32 columns] as [token][32] bf16
     const long f = (long)blockIdx.z * a.nchunks + blockIdx.x;
     const int part = blockIdx.y % kb, g = blockIdx.y / kb;
-    if (ctl && blockIdx.x == 0 && blockIdx.y == 0) {
+    if (ctl && blockIdx.y == 0) {
         // hand-off control block of the chained form: ticket and error word
-        // (once), then the published-chunk counter of each (b, h) chain (all
-        // B * H of them from the one grid row of packed sequences)
-        if (blockIdx.z == 0 && threadIdx.x < kChainCtlHeader) ctl[threadIdx.x] = 0;
-        const long n = a.chunks ? (long)a.B * a.H : a.H;
-        for (long j = threadIdx.x; j < n; j += kThreads) ctl[kChainCtlHeader + (long)blockIdx.z * a.H + j] = 0;
+        // (once), then the published-chunk counter of each (b, h) chain: the
+        // H of batch element z by block (0, 0, z); for packed sequences (one
+        // grid row) the B * H counters spread over the slots' first blocks
+        if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x < kChainCtlHeader) ctl[threadIdx.x] = 0;
+        long lo = 0, hi = 0;
+        if (a.chunks) {
+            const long n = (long)a.B * a.H, per = (n + a.nchunks - 1) / a.nchunks;
+            lo = min(n, (long)blockIdx.x * per);
+            hi = min(n, lo + per);
+        } else if (blockIdx.x == 0) {
+            lo = (long)blockIdx.z * a.H;
+            hi = lo + a.H;
+        }
+        for (long j = lo + threadIdx.x; j < hi; j += kThreads) ctl[kChainCtlHeader + j] = 0;
     }
     const ChunkEntry ch = chunk_at(a, f);
     const int Qc = ch.Qc;
@@ -336,14 +346,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // state in fp32.  h + (dm1 * h + S) rounds the state once per chunk.  Blocks
 // past the state blocks pack C for K3 (pack_c).
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long total, long state_blocks) {
-    if (chained_runs(a)) return;
-    if ((long)blockIdx.x >= state_blocks) {
-        pack_c(a, (long)blockIdx.x - state_blocks);
-        return;
-    }
-    const long e = (long)blockIdx.x * kThreads + threadIdx.x;  // float4 index
-    if (e >= total) return;
+// The chunks of one (b, h) chain for state float4 e (of B * H * P * N / 4).
+__device__ __forceinline__ void state_walk(const PrefillArgs &a, long e) {
     const long PN4 = (long)kP * kN / 4;
     const long bh = e / PN4;
     const long pn = e - bh * PN4;
@@ -380,6 +384,18 @@ __global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long 
     if (a.final_state) ((float4 *)a.final_state)[bh * PN4 + pn] = hv;
 }
 
+__global__ __launch_bounds__(kThreads) void state_pass_bf16(PrefillArgs a, long total, long state_blocks) {
+    if (chained_runs(a)) return;
+    if ((long)blockIdx.x >= state_blocks) {
+        pack_c(a, (long)blockIdx.x - state_blocks);
+        return;
+    }
+    // one float4 of state per thread; a grid capped below total / kThreads
+    // (the call of packed sequences that launches both forms) loops
+    for (long e = (long)blockIdx.x * kThreads + threadIdx.x; e < total; e += state_blocks * kThreads)
+        state_walk(a, e);
+}
+
 
 
 
@@ -412,7 +428,14 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s, bool after_c
     e = launch_stage("chunk_state_mfma", stream ? chunk_state_mfma<true> : chunk_state_mfma<false>, dim3((unsigned)nitems), dim3(kThreads), K1_LDS, s, a);
     if (e != hipSuccess) return e;
     const long total = (long)a.B * a.H * (kP * kN / 4);
-    const long state_blocks = (total + kThreads - 1) / kThreads;
+    // After the chained launch of packed sequences the chained form usually
+    // runs the call and the state pass's workgroups exit at once; its grid is
+    // then capped (each thread loops), which keeps skipping it cheap for many
+    // sequences: 512 sequences of the 2.7B-shaped layer need 327 680 blocks,
+    // 68 us to dispatch and skip.  (The chunk-state and output kernels keep
+    // one workgroup per item: looping there costs registers, spills in the
+    // output kernel.)
+    const long state_blocks = std::min((total + kThreads - 1) / kThreads, after_chain ? kDualStateBlocks : total);
     const long pack_blocks = after_chain ? 0 : (long)gridB * a.nchunks * a.G * kCBlocks;
     if (state_blocks + pack_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     e = launch_stage("state_pass_bf16", state_pass_bf16, dim3((unsigned)(state_blocks + pack_blocks)),
