@@ -339,6 +339,12 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
     const int ltA = wave, ltB = kTiles - 1 - wave;
+    // A short last chunk: column tiles past its last token are neither
+    // formed nor stored (a wave whose tile ltB is past it forms ltA alone;
+    // token tiles past it add only zeros to the tiles that are formed, which
+    // run every Horner step as in a full chunk)
+    const int ntl = (it.Qc + 31) >> 5;
+    const bool doA = ltA < ntl, doB = ltB < ntl;  // doB implies doA
     const bool exact = it.exact;
     const float *cst = vt;  // cs on the exact path
     const int hrow = li * 256;
@@ -357,21 +363,7 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
             y1 = mfma32(a1, cp[kk], y1);
         }
     };
-    f32x16 yA0, yA1, yB0, yB1;
-    state_term(cop, yA0, yA1);
-    load_c_tile(it, ltB, cop);
-    state_term(cop, yB0, yB1);
     const int lA = ltA * 32 + li, lB = ltB * 32 + li;
-    if (exact) {
-        const float eA = exp_fast(cst[lA]), eB = exp_fast(cst[lB]);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            yA0[v] *= eA;
-            yA1[v] *= eA;
-            yB0[v] *= eB;
-            yB1[v] *= eB;
-        }
-    }
     const float Dh = it.Dh;
     const float dlA = exact ? Dh : (dtt[lA] > 0.0f ? Dh / dtt[lA] : 0.0f);
     const float dlB = exact ? Dh : (dtt[lB] > 0.0f ? Dh / dtt[lB] : 0.0f);
@@ -407,28 +399,100 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
         }
     };
 
-    // ---- intra-chunk term: step k applies token tile k to both column tiles
+    f32x16 yA0 = {}, yA1 = {}, yB0 = {}, yB1 = {};
+    if (doB) {
+        state_term(cop, yA0, yA1);
+        load_c_tile(it, ltB, cop);
+        state_term(cop, yB0, yB1);
+        if (exact) {
+            const float eA = exp_fast(cst[lA]), eB = exp_fast(cst[lB]);
 #pragma unroll
-    for (int k = 0; k < kTiles; ++k) {
-        if (k <= ltB) {
-            if (k + 2 <= ltB) {
-                const u32x4 *pb = gt_tile(it, k + 2, ltB);
-                gB[(k + 2) % 3][0] = pb[0];
-                gB[(k + 2) % 3][1] = pb[64];
+            for (int v = 0; v < 16; ++v) {
+                yA0[v] *= eA;
+                yA1[v] *= eA;
+                yB0[v] *= eB;
+                yB1[v] *= eB;
             }
-            if (k + 1 <= ltA) {
-                const u32x4 *pa = gt_tile(it, k + 1, ltA);
-                gA[(k + 1) & 1][0] = pa[0];
-                gA[(k + 1) & 1][1] = pa[64];
-            }
-            u32x4 xa[2][2];
+        }
+        // ---- intra-chunk term: step k applies token tile k to both column tiles
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                xa[0][hf] = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
-                xa[1][hf] = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
+        for (int k = 0; k < kTiles; ++k) {
+            if (k <= ltB) {
+                if (k + 2 <= ltB) {
+                    const u32x4 *pb = gt_tile(it, k + 2, ltB);
+                    gB[(k + 2) % 3][0] = pb[0];
+                    gB[(k + 2) % 3][1] = pb[64];
+                }
+                if (k + 1 <= ltA) {
+                    const u32x4 *pa = gt_tile(it, k + 1, ltA);
+                    gA[(k + 1) & 1][0] = pa[0];
+                    gA[(k + 1) & 1][1] = pa[64];
+                }
+                u32x4 xa[2][2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    xa[0][hf] = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
+                    xa[1][hf] = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
+                }
+                const float qv = wv[K3_WQ + k];
+                if (k <= ltA) {
+                    u32x4 g2[2] = {gA[k & 1][0], gA[k & 1][1]};
+                    if (exact) scale_tile_exact(g2, cst, dtt, cslA, k, lh);
+                    if (k == ltA) add_diagonal(g2, dlA, li, lh);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        yA0[v] *= qv;
+                        yA1[v] *= qv;
+                    }
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        yA0 = mfma32(xa[0][hf], g2[hf], yA0);
+                        yA1 = mfma32(xa[1][hf], g2[hf], yA1);
+                    }
+                }
+                {
+                    u32x4 g2[2] = {gB[k % 3][0], gB[k % 3][1]};
+                    if (exact) scale_tile_exact(g2, cst, dtt, cslB, k, lh);
+                    if (k == ltB) add_diagonal(g2, dlB, li, lh);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        yB0[v] *= qv;
+                        yB1[v] *= qv;
+                    }
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        yB0 = mfma32(xa[0][hf], g2[hf], yB0);
+                        yB1 = mfma32(xa[1][hf], g2[hf], yB1);
+                    }
+                }
             }
-            const float qv = wv[K3_WQ + k];
+        }
+    } else if (doA) {
+        // column tile ltA alone (its tile ltB is past the chunk's last token)
+        state_term(cop, yA0, yA1);
+        if (exact) {
+            const float eA = exp_fast(cst[lA]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                yA0[v] *= eA;
+                yA1[v] *= eA;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kTiles; ++k) {
             if (k <= ltA) {
+                if (k + 1 <= ltA) {
+                    const u32x4 *pa = gt_tile(it, k + 1, ltA);
+                    gA[(k + 1) & 1][0] = pa[0];
+                    gA[(k + 1) & 1][1] = pa[64];
+                }
+                u32x4 xa[2][2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    xa[0][hf] = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
+                    xa[1][hf] = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
+                }
+                const float qv = wv[K3_WQ + k];
                 u32x4 g2[2] = {gA[k & 1][0], gA[k & 1][1]};
                 if (exact) scale_tile_exact(g2, cst, dtt, cslA, k, lh);
                 if (k == ltA) add_diagonal(g2, dlA, li, lh);
@@ -443,31 +507,16 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
                     yA1 = mfma32(xa[1][hf], g2[hf], yA1);
                 }
             }
-            {
-                u32x4 g2[2] = {gB[k % 3][0], gB[k % 3][1]};
-                if (exact) scale_tile_exact(g2, cst, dtt, cslB, k, lh);
-                if (k == ltB) add_diagonal(g2, dlB, li, lh);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    yB0[v] *= qv;
-                    yB1[v] *= qv;
-                }
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    yB0 = mfma32(xa[0][hf], g2[hf], yB0);
-                    yB1 = mfma32(xa[1][hf], g2[hf], yB1);
-                }
-            }
         }
     }
 
     // ---- outputs: every wave is done with x'^T and h; reuse their LDS
     __syncthreads();
     char *st = smem + wave * 2 * 32 * kYRow;
-    stage_tile(st, lA, yA0, yA1);
-    stage_tile(st + 32 * kYRow, lB, yB0, yB1);
-    store_tile(st, ltA);
-    store_tile(st + 32 * kYRow, ltB);
+    if (doA) stage_tile(st, lA, yA0, yA1);
+    if (doB) stage_tile(st + 32 * kYRow, lB, yB0, yB1);
+    if (doA) store_tile(st, ltA);
+    if (doB) store_tile(st + 32 * kYRow, ltB);
 }
 
 }  // namespace

@@ -383,3 +383,28 @@ def test_varlen_chained_expired_handoff_shows_as_nan_and_the_next_call_is_clean(
             else:
                 assert torch.equal(f1[b, h], f0[b, h]) and torch.equal(y1[rows, h], y0[rows, h])
     assert torch.equal(y2, y0) and torch.equal(f2, f0)
+
+
+@pytest.mark.parametrize("form", [1, 0])
+def test_varlen_every_short_chunk_tile_count(oracle, form):
+    """One-chunk sequences of 1 to 8 token tiles, at both edges of each tile
+    count: the output phase forms only the column tiles that hold a token of
+    the chunk (a wave whose second tile is past the chunk forms its first
+    alone), in both forms."""
+    lengths = [1, 32, 33, 64, 65, 96, 97, 128, 129, 160, 161, 192, 193, 224, 225, 255, 256, 0]
+    H = 16  # 16 * 17 / 1 effective chains: the chained pass when not forced
+    d = synth.make_varlen(lengths, H, 64, 2, 128, "bf16", seed=770)
+    init = synth.make_state(len(lengths), H, 64, 128, seed=771, scale=0.5)
+    announce("varlen short chunk tiles", form)
+    with packed_form(form):
+        y, fs, st = _run_staged(d, 256, init.cuda())
+    assert st == DUAL_STAGES
+    y_ref, fs_ref = oracle.ssd_scan_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["cu_seqlens"], d["D"], init)
+    assert rel_err(y, y_ref) <= TOL_BF16
+    assert rel_err(fs, fs_ref) <= TOL_BF16
+    cu = d["cu_seqlens"].tolist()
+    for b in range(len(lengths)):  # every sequence on its own, not just the batch
+        rows = slice(cu[b], cu[b + 1])
+        if lengths[b]:
+            assert rel_err(y[rows], y_ref[rows]) <= TOL_BF16, b
+        assert rel_err(fs[b:b + 1], fs_ref[b:b + 1]) <= TOL_BF16, b
