@@ -443,7 +443,7 @@ def norm_record(args):
 def bench_varlen(args):
     """Prefill of 16 prompts of the workload's layer packed without padding,
     lengths log-uniform in [64, 4096], against the same prompts padded to the
-    longest one in a uniform batch."""
+    longest one in a uniform batch; 512 prompts of 16-512 tokens packed."""
     import torch
 
     from mamba_ssd_scan_chunk_amd import binding as bd
@@ -465,6 +465,23 @@ def bench_varlen(args):
 
     ms = _timed(step, args.steps, args.warmup, "varlen")
     del d, y, ws
+    # many short prompts: 512 of 16-512 tokens (most chunks short)
+    short = synth.make_lengths(512, 16, 512, seed=3)
+    Ts = sum(short)
+    d = {k: v.cuda() for k, v in synth.make_varlen(short, w.H, w.P, w.G, w.N, w.dtype, seed=10).items()}
+    y = torch.empty_like(d["x"])
+    fs2 = torch.empty((len(short), w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, bd.lib().ssd_prefill_varlen_workspace_bytes(len(short), Ts, w.H, w.P, w.G, w.N, w.Q,
+                                                                        code)), dtype=torch.uint8, device="cuda")
+
+    def short_step(_):
+        bd.ssd_prefill_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], d["cu_seqlens"], None, Q=w.Q,
+                              y=y, final_state=fs2, workspace=ws)
+
+    sms = _timed(short_step, max(5, args.steps // 5), 2, "varlen_many_short")
+    many_short = {"sequences": len(short), "tokens": Ts, "us": round(sms * 1e3, 2),
+                  "tokens_per_s": round(Ts / (sms * 1e-3), 1)}
+    del d, y, ws, fs2
     # the depthwise conv over the same packed prompts (x | B | C channels)
     C = w.conv_channels
     xbc = synth.make_tokens(1, T, C, w.dtype, seed=12)[0].cuda()
@@ -489,13 +506,13 @@ def bench_varlen(args):
         bd.ssd_prefill(p["x"], p["dt"], p["A_log"], p["Bm"], p["Cm"], p["D"], None, Q=w.Q, final_state=fs)
 
     pms = _timed(padded, max(5, args.steps // 5), 2, "varlen_padded")
-    return lengths, T, ms, Lmax, pms, cms, cbytes
+    return lengths, T, ms, Lmax, pms, cms, cbytes, many_short
 
 
 def varlen_record(args):
-    lengths, T, ms, Lmax, pms, cms, cbytes = bench_varlen(args)
+    lengths, T, ms, Lmax, pms, cms, cbytes, many_short = bench_varlen(args)
     return {"varlen": {"sequences": len(lengths), "tokens": T, "lengths": lengths, "us": round(ms * 1e3, 2),
-                       "tokens_per_s": round(T / (ms * 1e-3), 1),
+                       "tokens_per_s": round(T / (ms * 1e-3), 1), "many_short": many_short,
                        "padded": {"batch": len(lengths), "seq_len": Lmax, "us": round(pms * 1e3, 2)},
                        "conv": {"us": round(cms * 1e3, 2), "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1)}}}
 
