@@ -405,3 +405,40 @@ def test_handoff_jitter_changes_no_result(B, L, H):
         finally:
             bd.debug_handoff_jitter(0)
         assert torch.equal(y1, y0) and torch.equal(f1, f0), rounds
+
+
+def test_two_chained_prefills_on_two_streams_at_once():
+    """Two chained single passes with their own workspaces run concurrently on
+    two streams (default priority): each chain's hand-offs use only its own
+    call's control block and slots, so both results equal their solo runs bit
+    for bit."""
+    shapes = [(4, 2048, 80, 20), (3, 1500, 64, 21)]  # 320 and 192 chains
+    runs = []
+    for B, L, H, seed in shapes:
+        d = dev(synth.make_prefill(B, L, H, 64, 1, 128, "bf16", seed=seed))
+        ws = torch.empty(bd.lib().ssd_prefill_workspace_bytes(B, L, H, 64, 1, 128, 256, bd.SSD_BF16),
+                         dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(d["x"])
+        fs = torch.empty((B, H, 64, 128), dtype=torch.float32, device="cuda")
+        runs.append((d, ws, y, fs))
+
+    def call(r, stream=None):
+        d, ws, y, fs = r
+        bd.ssd_prefill(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], Q=256, y=y, final_state=fs,
+                       workspace=ws, stream=stream)
+
+    announce("two chained prefills on two streams")
+    solo = []
+    for r in runs:
+        call(r)
+        torch.cuda.synchronize()
+        solo.append((r[2].clone(), r[3].clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for r, s in zip(runs, streams):
+            call(r, s)
+    torch.cuda.synchronize()
+    for (y0, f0), (_, _, y, fs) in zip(solo, runs):
+        assert torch.equal(y, y0) and torch.equal(fs, f0)
