@@ -152,8 +152,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // sequences (the chunk table deals them out), tickets over the share's
     // item order (round c: chunk c of each of its sequences with more than c
     // chunks) times the H heads, so a chunk's heads follow each other.
-    // Thread 0 names the item by its slot (for an empty sequence, the
-    // sequence), its head and its flags.
+    // Thread 0 hands the item to the workgroup through LDS: slot, head,
+    // flags (last chunk, empty sequence), sequence, first token row, chunk
+    // index and length.
     if (tid == 0) {
         int fi = -1, hh = 0, seq = 0, tok = 0, cc = 0, qc = 0;
         unsigned fl = 0;
