@@ -408,3 +408,23 @@ def test_varlen_every_short_chunk_tile_count(oracle, form):
         if lengths[b]:
             assert rel_err(y[rows], y_ref[rows]) <= TOL_BF16, b
         assert rel_err(fs[b:b + 1], fs_ref[b:b + 1]) <= TOL_BF16, b
+
+
+def test_varlen_many_short_prompts_sampled(oracle):
+    """512 prompts of the 2.7B-shaped layer, 16-512 tokens each (the bench's
+    many-short batch: most chunks short, the chained pass chosen), checked on
+    sampled (sequence, head) pairs, including the first and last sequence."""
+    H, P, G, N = 80, 64, 1, 128
+    lengths = synth.make_lengths(512, 16, 512, seed=3)
+    assert _chained_by_lengths(lengths, H)
+    d = synth.make_varlen(lengths, H, P, G, N, "bf16", seed=10)
+    announce("varlen many short", sum(lengths))
+    y, fs = _run(d, 256)
+    cu = d["cu_seqlens"].numpy()
+    for b, h in [(0, 0), (1, 79), (137, 40), (255, 5), (256, 77), (400, 12), (510, 63), (511, 31)]:
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        sub = dict(x=d["x"][None, lo:hi, h:h + 1], dt=d["dt"][None, lo:hi, h:h + 1], A_log=d["A_log"][h:h + 1],
+                   Bm=d["Bm"][None, lo:hi], Cm=d["Cm"][None, lo:hi], D=d["D"][h:h + 1])
+        y_ref, fs_ref = oracle.ssd_scan(**sub)
+        assert rel_err(y[lo:hi, h:h + 1], y_ref[0]) <= TOL_BF16, (b, h)
+        assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
