@@ -130,7 +130,7 @@ __device__ __forceinline__ void jitter_sleep(const PrefillArgs &a, unsigned seed
 // accumulator order of a 32x32 MFMA tile.
 __device__ __forceinline__ int acc_row(int acc, int v, int lh) { return 32 * acc + (v >> 2) * 8 + lh * 4 + (v & 3); }
 
-template <bool kNtX, bool kNtY>
+template <bool kNtX, bool kNtY, bool kPacked>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_chain_mfma(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char *xt = smem + K3_XT;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         int fi = -1, hh = 0, seq = 0, tok = 0, cc = 0, qc = 0;
         unsigned fl = 0;
         const int x0 = xcd_id();
-        const bool packed = a.chunks != nullptr;
+        constexpr bool packed = kPacked;
         // packed: the header (groups and list start of each share), in flight
         // with the first ticket
         u32x4 hdr[5] = {};
@@ -311,31 +311,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // ---- chunk state S_c, wave w: columns n in [32w, 32w + 32), both
     // 32-row feature tiles; Horner over the token tiles (Q = 1 and no final
     // factor on the exact path)
+    // Packed sequences (most chunks short in a batch of short prompts): the
+    // loop stops at the last token tile K = ntl - 1 (the tiles after it hold
+    // no token) and the closing factor is exp(cs_last - R_K).  A uniform batch
+    // runs all eight tiles (at most its last chunk is short), which keeps its
+    // loop free of the extra branches.
+    const int ntl = kPacked ? (Qc + 31) >> 5 : kTiles;
     f32x16 s0 = {}, s1 = {};
 #pragma unroll
     for (int k = 0; k < kTiles; ++k) {
-        if (k > 0) {
-            const float q = wv[K3_WQ + k];
+        if (k < ntl) {
+            if (k > 0) {
+                const float q = wv[K3_WQ + k];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s0[v] *= q;
-                s1[v] *= q;
+                for (int v = 0; v < 16; ++v) {
+                    s0[v] *= q;
+                    s1[v] *= q;
+                }
             }
-        }
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const u32x4 a0 = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
-            const u32x4 a1 = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
-            s0 = mfma32(a0, bq[(2 * k + hf) & 3], s0);
-            s1 = mfma32(a1, bq[(2 * k + hf) & 3], s1);
-        }
-        if (k + 2 < kTiles) {  // token tile k + 2 into the registers tile k used
-            bq[(2 * k) & 3] = bt[(2 * k + 4) * 64];
-            bq[(2 * k + 1) & 3] = bt[(2 * k + 5) * 64];
+            for (int hf = 0; hf < 2; ++hf) {
+                const u32x4 a0 = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
+                const u32x4 a1 = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
+                s0 = mfma32(a0, bq[(2 * k + hf) & 3], s0);
+                s1 = mfma32(a1, bq[(2 * k + hf) & 3], s1);
+            }
+            if (k + 2 < ntl) {  // token tile k + 2 into the registers tile k used
+                bq[(2 * k) & 3] = bt[(2 * k + 4) * 64];
+                bq[(2 * k + 1) & 3] = bt[(2 * k + 5) * 64];
+            }
         }
     }
     {
-        const float fin = exact ? 1.0f : exp_fast(wv[3 * 3 + 2] - wv[3 * 3 + 1]);  // exp(cs_last - R_7)
+        float rest = wv[3 * 3 + 2] - wv[3 * 3 + 1];  // cs_last - R_7
+        if (kPacked && ntl < kTiles) {
+            // cs_last - R_K: the rest of R_K's wave after it, then the later
+            // waves' totals
+            const int kw = (ntl - 1) >> 1;
+            rest = wv[3 * kw + 2] - wv[3 * kw + ((ntl - 1) & 1)];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) rest += w > kw ? wv[3 * w + 2] : 0.0f;
+        }
+        const float fin = exact ? 1.0f : exp_fast(rest);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             s0[v] *= fin;
@@ -484,7 +501,9 @@ hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s) {
     // at B = 8, L = 16384 (x and y 1.34 GB each): 1405 us with cached x and
     // y, 1355 with non-temporal x loads, 1375 with non-temporal y stores,
     // 1316 with both
-    auto kernel = prefill_streams(a) ? chunk_chain_mfma<true, true> : chunk_chain_mfma<false, false>;
+    const bool stream = prefill_streams(a);
+    auto kernel = a.chunks ? (stream ? chunk_chain_mfma<true, true, true> : chunk_chain_mfma<false, false, true>)
+                           : (stream ? chunk_chain_mfma<true, true, false> : chunk_chain_mfma<false, false, false>);
     return launch_stage("chunk_chain_mfma", kernel, dim3((unsigned)nitems), dim3(kThreads), CH_LDS, s, a);
 }
 
