@@ -78,11 +78,13 @@ __device__ int above_and_rounds(int *hist, int *R, int n) {
 }
 
 // The item-order histograms (hist, cnt, then xhist and xR of each share, slots
-// + 2 ints each) live in LDS up to 48 KB.
+// + 2 ints each) live in LDS up to 40 KB (with the kernel's 16.5 KB of static
+// LDS, under 64 KB per workgroup), else in scratch.
+constexpr size_t kTableHistLds = 40 * 1024;
 __host__ __device__ inline size_t table_hist_bytes(long slots) {
     return (size_t)(2 + 2 * kChainXcds) * (slots + 2) * sizeof(int);
 }
-__host__ __device__ inline bool table_hist_in_lds(long slots) { return table_hist_bytes(slots) <= 48 * 1024; }
+__host__ __device__ inline bool table_hist_in_lds(long slots) { return table_hist_bytes(slots) <= kTableHistLds; }
 
 // Share of the sequence at position j of the sorted order.
 __device__ __forceinline__ int snake_share(int j) {

@@ -428,3 +428,27 @@ def test_varlen_many_short_prompts_sampled(oracle):
         y_ref, fs_ref = oracle.ssd_scan(**sub)
         assert rel_err(y[lo:hi, h:h + 1], y_ref[0]) <= TOL_BF16, (b, h)
         assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
+
+
+def test_varlen_chained_at_the_table_lds_bound(oracle):
+    """16 sequences, 141 000 tokens: 566 chunk slots, whose item-order
+    histograms (18 * 568 ints = 40.9 KB) are the largest the chunk-table
+    kernel keeps in LDS; the chained pass then runs on that order.  Sampled
+    (sequence, head) pairs against the oracle."""
+    H = 12
+    lengths = [8812] * 15 + [8820]
+    assert sum(lengths) == 141000 and _chained_by_lengths(lengths, H)
+    slots = sum(lengths) // 256 + len(lengths)
+    assert 18 * (slots + 2) * 4 <= 40 * 1024 < 18 * (slots + 2 + 5) * 4
+    d = synth.make_varlen(lengths, H, 64, 1, 128, "bf16", seed=780)
+    announce("varlen table LDS bound")
+    y, fs, st = _run_staged(d, 256)
+    assert st == DUAL_STAGES
+    cu = d["cu_seqlens"].numpy()
+    for b, h in [(0, 0), (7, 11), (15, 5)]:
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        sub = dict(x=d["x"][None, lo:hi, h:h + 1], dt=d["dt"][None, lo:hi, h:h + 1], A_log=d["A_log"][h:h + 1],
+                   Bm=d["Bm"][None, lo:hi], Cm=d["Cm"][None, lo:hi], D=d["D"][h:h + 1])
+        y_ref, fs_ref = oracle.ssd_scan(**sub)
+        assert rel_err(y[lo:hi, h:h + 1], y_ref[0]) <= TOL_BF16, (b, h)
+        assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
