@@ -198,7 +198,8 @@ size_t ssd_prefill_workspace_bytes(int B, int L, int H, int P, int G, int N,
  * Empty sequences are allowed (their final state is their initial state).
  * The workspace (ssd_prefill_varlen_workspace_bytes) also holds the chunk
  * table the library builds on the device.  For the chained shape (bf16,
- * P = 64, N = 128, Q a multiple of 256, B*H >= 192) the call launches both
+ * P = 64, N = 128, Q a multiple of 256, B*H >= 192, and fewer than 2^22 chunk
+ * slots T/256 + B) the call launches both
  * prefill forms and that table's kernel picks, from the lengths, the one
  * that does the work (see ssd_debug_packed_form); the workspace then holds
  * both forms' buffers.  Every other argument, limit, alignment rule and
