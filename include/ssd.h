@@ -362,8 +362,10 @@ int ssd_gated_rmsnorm(long rows, int D, int group, int dtype, const void *y, con
 
 /*
  * Stage timing -- a profiling aid, kept per host thread.
- * ssd_stage_timing(1) makes the following ssd_prefill calls of the calling
- * thread launch each kernel with a pair of HIP events stamped when that
+ * ssd_stage_timing(1) makes the following prefill calls (ssd_prefill,
+ * ssd_prefill_varlen and their raw-step forms; for packed sequences the
+ * chunk-table kernel comes first) of the calling thread launch each kernel
+ * with a pair of HIP events stamped when that
  * kernel's dispatch starts and ends (events created once, on the device
  * current at this call); ssd_stage_timing(0) stops it.  ssd_stage_times
  * waits for the last such call, stores in *count the number of kernels it

@@ -77,14 +77,15 @@ __device__ int above_and_rounds(int *hist, int *R, int n) {
     return acc;
 }
 
-// The item-order histograms (hist, cnt, then xhist and xR of each share, slots
-// + 2 ints each) live in LDS up to 40 KB (with the kernel's 16.5 KB of static
-// LDS, under 64 KB per workgroup), else in scratch.
+// The item-order histograms (hist, cnt, then xhist and xR of each share,
+// kmax + 2 ints each for chunk counts up to kmax) live in LDS up to 40 KB
+// (with the kernel's 16.5 KB of static LDS, under 64 KB per workgroup), else
+// in scratch.
 constexpr size_t kTableHistLds = 40 * 1024;
-__host__ __device__ inline size_t table_hist_bytes(long slots) {
-    return (size_t)(2 + 2 * kChainXcds) * (slots + 2) * sizeof(int);
+__host__ __device__ inline size_t table_hist_bytes(long kmax) {
+    return (size_t)(2 + 2 * kChainXcds) * (kmax + 2) * sizeof(int);
 }
-__host__ __device__ inline bool table_hist_in_lds(long slots) { return table_hist_bytes(slots) <= kTableHistLds; }
+__host__ __device__ inline bool table_hist_in_lds(long kmax) { return table_hist_bytes(kmax) <= kTableHistLds; }
 
 // Share of the sequence at position j of the sorted order.
 __device__ __forceinline__ int snake_share(int j) {
@@ -145,12 +146,14 @@ __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(PrefillArgs a,
     if (!items) return;
 
     // ---- item order of the chained single pass.  k(b) = max(chunks of b, 1)
-    // <= slots.  hist and cnt (the sort), per share xhist and xR: in LDS when
-    // they fit (a generic pointer then reaches LDS), else in scratch; pos
-    // (place of b in order of decreasing k) in scratch.
+    // <= max(nmax, 1), so the histograms span n = max(nmax, 1) + 2 counts
+    // (at most slots + 2, what scratch is sized for).  hist and cnt (the
+    // sort), per share xhist and xR: in LDS when they fit (a generic pointer
+    // then reaches LDS), else in scratch; pos (place of b in order of
+    // decreasing k) in scratch.
     extern __shared__ int lds_hist[];
-    const int n = (int)slots + 2;
-    int *hist = table_hist_in_lds(slots) ? lds_hist : scratch;
+    const int n = max(nmax, 1) + 2;
+    int *hist = table_hist_in_lds(n - 2) ? lds_hist : scratch;
     int *cnt = hist + n, *xhist = cnt + n, *xR = xhist + kChainXcds * n;
     int *pos = scratch + (long)(2 + 2 * kChainXcds) * n;
     for (int v = tid; v < (2 + kChainXcds) * n; v += kTabThreads) hist[v] = 0;  // hist, cnt, xhist
@@ -188,29 +191,33 @@ __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(PrefillArgs a,
         items[kChainXcds + tid] = (unsigned)base;
     }
     __syncthreads();
+    // the records: one thread per chunk slot (its entry names the sequence
+    // and the chunk), then one per empty sequence
     ItemEntry *recs = (ItemEntry *)(items + kItemHeader);
-    for (int b = wave; b < a.B; b += kTabThreads / 64) {
-        const SeqEntry e = seqs[b];
+    for (long long f = tid; f < used; f += kTabThreads) {
+        const ChunkEntry ch = chunks[f];
+        const int b = ch.seq, c = ch.c;
         const int j = pos[b], x = snake_share(j), jl = j / kChainXcds;
-        ItemEntry *list = recs + share_base[x];
-        const int *R = xR + x * n;
-        if (e.n == 0) {
-            if (lane == 0) list[R[0] + jl] = ItemEntry{kItemLast, kItemEmpty | (unsigned)b, 0, 0};
-            continue;
-        }
-        for (int c = lane; c < e.n; c += 64)
-            list[R[c] + jl] = ItemEntry{(unsigned)(e.f0 + c) | (c == e.n - 1 ? kItemLast : 0u), (unsigned)b,
-                                        e.tok0 + c * a.Q, (c << kItemQcBits) | min(a.Q, e.len - c * a.Q)};
+        const bool last = c == seqs[b].n - 1;
+        recs[share_base[x] + xR[x * n + c] + jl] =
+            ItemEntry{(unsigned)f | (last ? kItemLast : 0u), (unsigned)b, ch.tok0, (c << kItemQcBits) | ch.Qc};
+    }
+    for (int b = tid; b < a.B; b += kTabThreads) {
+        if (seqs[b].n != 0) continue;
+        const int j = pos[b], x = snake_share(j), jl = j / kChainXcds;
+        recs[share_base[x] + xR[x * n] + jl] = ItemEntry{kItemLast, kItemEmpty | (unsigned)b, 0, 0};
     }
 }
 
 }  // namespace
 
 hipError_t launch_chunk_table(const PrefillArgs &a, ChunkEntry *chunks, SeqEntry *seqs, hipStream_t s,
-                              unsigned *items, int *scratch) {
+                              unsigned *items, int *scratch, bool timed) {
     if (items && (!scratch || a.nchunks >= kItemMaxSlots || a.B > (int)kItemIndex || a.Q >= (1 << kItemQcBits)))
         return hipErrorInvalidValue;
-    const size_t lds = items && table_hist_in_lds(a.nchunks) ? table_hist_bytes(a.nchunks) : 0;
+    const size_t lds = items ? kTableHistLds : 0;  // the kernel uses it when the counts fit
+    if (timed) return launch_stage("chunk_table_kernel", chunk_table_kernel, dim3(1), dim3(kTabThreads), lds, s, a, chunks,
+                                   seqs, items, scratch);
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kTabThreads), lds, s, a, chunks, seqs, items, scratch);
     return hipGetLastError();
 }

@@ -494,7 +494,6 @@ hipError_t launch_prefill_chain(const PrefillArgs &a, hipStream_t s) {
     // one chunk), and the workgroups past the actual items exit at once
     const long nitems = (a.chunks ? (long)a.nchunks + a.B : (long)a.B * a.nchunks) * a.H;
     if (nitems > 0x7fffffffL || (a.chunks && !a.ws_items)) return hipErrorInvalidConfiguration;
-    stage_begin();
     hipError_t e = launch_chunk_pack(a, true, a.ws_ctl, s);
     if (e != hipSuccess) return e;
     // streamed x and y (prefill_streams).  Measured on the 2.7B-shaped layer

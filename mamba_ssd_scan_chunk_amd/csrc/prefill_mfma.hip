@@ -418,7 +418,6 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s, bool after_c
     if (nitems > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipError_t e = hipSuccess;
     if (!after_chain) {  // else the chained launch has packed the operands, C included
-        stage_begin();
         e = launch_chunk_pack(a, false, nullptr, s);
         if (e != hipSuccess) return e;
     }

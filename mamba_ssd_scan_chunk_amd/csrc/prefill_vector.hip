@@ -409,7 +409,6 @@ hipError_t launch_out_p(const PrefillArgs &a, dim3 grid, hipStream_t s) {
 hipError_t launch_prefill_vector(const PrefillArgs &a, int dtype, hipStream_t s) {
     const int gridB = a.chunks ? 1 : a.B;  // packed sequences: nchunks slots in all
     if (gridB > 65535 || a.H > 65535) return hipErrorInvalidConfiguration;
-    stage_begin();
     dim3 g1(a.nchunks, a.H, gridB);
     hipError_t e = dtype == DT_BF16
                        ? launch_stage("chunk_state_vec", chunk_state_vec<bf16_t>, g1, dim3(kThreads), 0, s, a)

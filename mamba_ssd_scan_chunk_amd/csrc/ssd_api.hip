@@ -272,6 +272,7 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
         if (overlap(workspace, b_ws, init_state, b_state)) return SSD_ERR_INVALID_ARG;
     }
 
+    ssd::stage_begin();  // a new stage record for this call (empty when no kernel is timed)
     if (L == 0) {
         if (!final_state) return SSD_OK;
         return hip_status(ssd::launch_state_copy(init_state, final_state, n_state, stream));
@@ -312,7 +313,7 @@ int prefill_impl(int B, int L, int H, int P, int G, int N, int Q, int dtype, con
         ssd::SeqEntry *seqs = (ssd::SeqEntry *)(ws + wl.off_tab + (size_t)slots * sizeof(ssd::ChunkEntry));
         unsigned *items = chain ? (unsigned *)(ws + wl.off_items) : nullptr;
         int *scratch = chain ? (int *)(items + ssd::chunk_table_item_ints(slots, B)) : nullptr;
-        hipError_t e = ssd::launch_chunk_table(a, chunks, seqs, stream, items, scratch);
+        hipError_t e = ssd::launch_chunk_table(a, chunks, seqs, stream, items, scratch, true);
         if (e != hipSuccess) return hip_status(e);
         a.chunks = chunks;
         a.seqs = seqs;

@@ -133,15 +133,17 @@ WorkspaceLayout prefill_workspace_layout(long slots, int H, int P, int N, int Q,
 // of sum over sequences of ceil(L_b / Q).
 inline long varlen_slots(long T, int B, int Q) { return T / Q + B; }
 // `items` (nullable): also the item order of the chained path, built with
-// `scratch` (chunk_table_scratch_ints(slots, nseq) ints).
+// `scratch` (chunk_table_scratch_ints(slots, nseq) ints).  `timed`: a
+// prefill's table, recorded by the stage timing.
 hipError_t launch_chunk_table(const PrefillArgs &a, ChunkEntry *chunks, SeqEntry *seqs, hipStream_t s,
-                              unsigned *items = nullptr, int *scratch = nullptr);
+                              unsigned *items = nullptr, int *scratch = nullptr, bool timed = false);
 inline long chunk_table_item_ints(long slots, long nseq) { return kItemHeader + 4 * (slots + nseq); }
 inline long chunk_table_scratch_ints(long slots, long nseq) { return (2 + 2 * kChainXcds) * (slots + 2) + nseq; }
 bool prefill_uses_mfma(int P, int N, int Q, int dtype);
 
 // Stage timing (profiling aid, per host thread).  stage_begin starts a new
-// record for one ssd_prefill call; stage_events hands out the start/stop
+// record for one ssd_prefill call (the API calls it once per call, before
+// the call's first kernel); stage_events hands out the start/stop
 // events of its next kernel (false when timing is off or the record is
 // full), which launch_stage passes to hipExtLaunchKernelGGL so that they
 // are stamped when that kernel's dispatch starts and ends.

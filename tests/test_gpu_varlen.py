@@ -73,7 +73,8 @@ CHAIN_CASES = [
     ("long-and-short-h32", [5000, 3, 0, 1300, 256, 2049], 32, 4),  # 32 * 37 / 20: four-kernel
     ("one-dominates-h64", [6000, 100, 50, 0], 64, 2),
 ]
-DUAL_STAGES = ["chunk_pack_mfma", "chunk_chain_mfma", "chunk_state_mfma", "state_pass_bf16", "chunk_out_mfma"]
+DUAL_STAGES = ["chunk_table_kernel", "chunk_pack_mfma", "chunk_chain_mfma", "chunk_state_mfma", "state_pass_bf16",
+               "chunk_out_mfma"]
 
 
 def _chained_by_lengths(lengths, H, Q=256):
@@ -430,22 +431,23 @@ def test_varlen_many_short_prompts_sampled(oracle):
         assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
 
 
-def test_varlen_chained_at_the_table_lds_bound(oracle):
-    """16 sequences, 141 000 tokens: 566 chunk slots, whose item-order
-    histograms (18 * 568 ints = 40.9 KB) are the largest the chunk-table
-    kernel keeps in LDS; the chained pass then runs on that order.  Sampled
-    (sequence, head) pairs against the oracle."""
-    H = 12
-    lengths = [8812] * 15 + [8820]
-    assert sum(lengths) == 141000 and _chained_by_lengths(lengths, H)
-    slots = sum(lengths) // 256 + len(lengths)
-    assert 18 * (slots + 2) * 4 <= 40 * 1024 < 18 * (slots + 2 + 5) * 4
+@pytest.mark.parametrize("long_chunks", [566, 567], ids=["lds", "scratch"])
+def test_varlen_chained_at_the_table_lds_bound(oracle, long_chunks):
+    """The chunk-table kernel's item-order histograms span the chunk counts up
+    to the largest one: 18 * (566 + 2) ints = 40.9 KB is the most it keeps in
+    LDS, one chunk more goes to global scratch.  One sequence of that many
+    chunks and 15 short ones, the chained pass forced; sampled (sequence,
+    head) pairs against the oracle."""
+    H = 12  # 16 sequences x 12 heads = 192: both forms launched
+    lengths = [256 * long_chunks - 100] + [300, 1, 0, 257, 64] * 3
+    assert 18 * (566 + 2) * 4 <= 40 * 1024 < 18 * (567 + 2) * 4
     d = synth.make_varlen(lengths, H, 64, 1, 128, "bf16", seed=780)
-    announce("varlen table LDS bound")
-    y, fs, st = _run_staged(d, 256)
+    announce("varlen table LDS bound", long_chunks)
+    with packed_form(1):
+        y, fs, st = _run_staged(d, 256)
     assert st == DUAL_STAGES
     cu = d["cu_seqlens"].numpy()
-    for b, h in [(0, 0), (7, 11), (15, 5)]:
+    for b, h in [(0, 0), (0, 11), (1, 5), (4, 7)]:
         lo, hi = int(cu[b]), int(cu[b + 1])
         sub = dict(x=d["x"][None, lo:hi, h:h + 1], dt=d["dt"][None, lo:hi, h:h + 1], A_log=d["A_log"][h:h + 1],
                    Bm=d["Bm"][None, lo:hi], Cm=d["Cm"][None, lo:hi], D=d["D"][h:h + 1])
