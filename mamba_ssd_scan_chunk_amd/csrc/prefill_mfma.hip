@@ -87,6 +87,7 @@ __device__ __forceinline__ void pack_c(const PrefillArgs &a, long blk) {
 constexpr int kK0Tiles = kGTiles / 4;         // workgroups forming G^T tiles
 constexpr int kK0Blocks = kK0Tiles + kN / 32;  // plus one per 32 columns of B
 
+template <bool kPacked>
 __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a, int kb, int *ctl) {
     __shared__ __attribute__((aligned(16))) char bl[kQ * 64];  // B[:, 32 columns] as [token][32] bf16
     const long f = (long)blockIdx.z * a.nchunks + blockIdx.x;
@@ -129,6 +130,9 @@ __global__ __launch_bounds__(kThreads) void chunk_pack_mfma(PrefillArgs a, int k
         const int tix = part * 4 + wave;  // = gt_index(si, lt)
         int lt = 0;
         while ((lt + 1) * (lt + 2) / 2 <= tix) ++lt;
+        // packed sequences (most chunks short in a batch of short prompts):
+        // a column tile past the chunk's last token is never read
+        if (kPacked && lt * 32 >= Qc) return;
         const int si = tix - lt * (lt + 1) / 2;
         const unsigned oa = (unsigned)(si * 32 + li) * rs + 16 * lh;
         const unsigned ob = (unsigned)(lt * 32 + li) * rs + 16 * lh;
@@ -408,7 +412,8 @@ hipError_t launch_chunk_pack(const PrefillArgs &a, bool with_c, int *ctl, hipStr
     const int gridB = a.chunks ? 1 : a.B;  // packed sequences: nchunks slots in all
     const int kb = kK0Blocks + (with_c ? kCBlocks : 0);
     if ((long)a.G * kb > 65535 || a.nchunks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    return launch_stage("chunk_pack_mfma", chunk_pack_mfma, dim3(a.nchunks, kb * a.G, gridB), dim3(kThreads), 0, s,
+    return launch_stage("chunk_pack_mfma", a.chunks ? chunk_pack_mfma<true> : chunk_pack_mfma<false>,
+                        dim3(a.nchunks, kb * a.G, gridB), dim3(kThreads), 0, s,
                         a, kb, ctl);
 }
 
