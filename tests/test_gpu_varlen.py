@@ -454,3 +454,35 @@ def test_varlen_chained_at_the_table_lds_bound(oracle, long_chunks):
         y_ref, fs_ref = oracle.ssd_scan(**sub)
         assert rel_err(y[lo:hi, h:h + 1], y_ref[0]) <= TOL_BF16, (b, h)
         assert rel_err(fs[b:b + 1, h:h + 1], fs_ref) <= TOL_BF16, (b, h)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_varlen_random_mixes(oracle, seed):
+    """Seeded random packed batches of the chained shape: 1 to 40 sequences
+    of 0 to 1500 tokens (some empty), 16 to 64 heads.  The chained pass
+    (forced) matches the oracle, and the device's own choice gives the bits
+    of the form the length rule names."""
+    rng = np.random.default_rng(900 + seed)
+    nseq = int(rng.integers(1, 41))
+    H = int(rng.choice([16, 24, 32, 48, 64]))
+    if nseq * H < 192:  # below the bound the call never launches the chained pass
+        nseq = -(-192 // H)
+    lengths = [int(v) for v in rng.integers(0, 1501, size=nseq)]
+    lengths = [0 if rng.random() < 0.1 else n for n in lengths]
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    G = 2 if H % 2 == 0 else 1
+    d = synth.make_varlen(lengths, H, 64, G, 128, "bf16", seed=901 + seed)
+    init = synth.make_state(len(lengths), H, 64, 128, seed=902 + seed, scale=0.5)
+    announce("varlen random mix", seed, nseq, H, sum(lengths))
+    out = {}
+    for form in (1, 0, -1):
+        with packed_form(form):
+            out[form] = _run_staged(d, 256, init.cuda())[:2]
+    y_ref, fs_ref = oracle.ssd_scan_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["cu_seqlens"], d["D"],
+                                           init)
+    for form in (1, 0):
+        assert rel_err(out[form][0], y_ref) <= TOL_BF16, form
+        assert rel_err(out[form][1], fs_ref) <= TOL_BF16, form
+    chosen = out[1 if _chained_by_lengths(lengths, H) else 0]
+    assert torch.equal(out[-1][0], chosen[0]) and torch.equal(out[-1][1], chosen[1])
