@@ -486,3 +486,54 @@ def test_varlen_random_mixes(oracle, seed):
         assert rel_err(out[form][1], fs_ref) <= TOL_BF16, form
     chosen = out[1 if _chained_by_lengths(lengths, H) else 0]
     assert torch.equal(out[-1][0], chosen[0]) and torch.equal(out[-1][1], chosen[1])
+
+
+def test_varlen_packed_form_is_per_host_thread():
+    """ssd_debug_packed_form is kept per host thread: two threads forcing
+    different forms on the same packed batch at once (own streams, own
+    outputs and workspaces) each get their own form's bits."""
+    import threading
+
+    lengths = [700, 0, 1, 256, 513, 90, 1200, 31]
+    H = 32
+    d = dev(synth.make_varlen(lengths, H, 64, 2, 128, "bf16", seed=790))
+    T, B = sum(lengths), len(lengths)
+    want = {}
+    for form in (0, 1):
+        with packed_form(form):
+            y, fs = bd.ssd_prefill_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], d["cu_seqlens"],
+                                          Q=256)
+        torch.cuda.synchronize()
+        want[form] = (y, fs)
+    assert not torch.equal(want[0][0], want[1][0])  # the two forms round differently: the check can tell them apart
+    announce("varlen packed form per thread")
+    errors, got = [], {}
+
+    def worker(form):
+        try:
+            bd.debug_packed_form(form)
+            stream = torch.cuda.Stream()
+            ws = torch.empty(bd.lib().ssd_prefill_varlen_workspace_bytes(B, T, H, 64, 2, 128, 256, bd.SSD_BF16),
+                             dtype=torch.uint8, device="cuda")
+            y = torch.empty_like(d["x"])
+            fs = torch.empty((B, H, 64, 128), dtype=torch.float32, device="cuda")
+            stream.wait_stream(torch.cuda.default_stream())
+            with torch.cuda.stream(stream):
+                for _ in range(5):
+                    bd.ssd_prefill_varlen(d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"], d["cu_seqlens"],
+                                          Q=256, y=y, final_state=fs, workspace=ws, stream=stream)
+            stream.synchronize()
+            got[form] = (y, fs)
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+        finally:
+            bd.debug_packed_form(-1)
+
+    threads = [threading.Thread(target=worker, args=(f,)) for f in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert errors == []
+    for form in (0, 1):
+        assert torch.equal(got[form][0], want[form][0]) and torch.equal(got[form][1], want[form][1]), form
