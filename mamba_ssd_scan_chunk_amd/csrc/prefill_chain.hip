@@ -254,12 +254,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
     jitter_sleep(a, (unsigned)bh * 131u + (unsigned)c * 7u + 1u);
 
-    // ---- loads: the chain's counter (thread 0), dt (the cumsum waits for
-    // these two only), x, the B operands
+    // ---- loads: the chain's counter (thread 0), the step, A_log and D (the
+    // cumsum waits for these only), x, the B operands
     int *counter = ctl + kChainCtlHeader + bh;
     int early = 0;
     if (tid == 0 && c > 0) early = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float dtv = load_dt(a, tok0, Qc, h, tid);
+    const DecayIn din = load_decay_in(a, tok0, Qc, h, tid);
     u32x4 raw[8];
     load_x_raw<kNtX>(a, tok0, Qc, h, raw, tid);
     // B operands of the first two token tiles (the rest are streamed)
@@ -267,18 +267,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     u32x4 bq[4];
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) bq[gg] = bt[gg * 64];
-    const float Dh = a.D ? a.D[h] : 0.0f;
+    const float Dh = din.D;
     if (tid == 0) tk[2] = early;
     float total;
-    const bool exact = chunk_decay(dtv, -expf(a.A_log[h]), Dh, Qc, vt, ut, dtt, wv, tid, lane, wave, &total);
+    const float dtv = step_of(a, din, Qc, tid);
+    const bool exact = chunk_decay(dtv, -expf(din.alog), Dh, Qc, vt, ut, dtt, wv, tid, lane, wave, &total);
 
     // ---- h_{c-1} requested now if chunk c-1 had published by the start
-    // (the counter was read before the barriers above)
+    // (the counter was read before the barriers above).  The loads are issued
+    // on every path, against an empty range when chunk c-1 had not published
+    // (they then return zeros without touching memory): loads retire in issue
+    // order, and with the same loads in the same order on every path the
+    // waits before the x' store and the chunk state need not cover them.
     const bool ready = c > 0 && tk[2] >= c;
     const bool early_poison = (tk[2] & kChainPoison) != 0;
     float hp[2][16];
-    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(a.ws_ring + ((long)bh * 2 + ((c - 1) & 1)) * kP * kN, kP * kN * 4);
-    auto load_h = [&]() {
+    const float *slot = a.ws_ring + ((long)bh * 2 + ((c - 1) & 1)) * kP * kN;
+    auto load_h = [&](__amdgpu_buffer_rsrc_t hrs) {
 #pragma unroll
         for (int acc = 0; acc < 2; ++acc)
 #pragma unroll
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 for (int r = 0; r < 4; ++r) hp[acc][4 * q + r] = __uint_as_float(v[r]);
             }
     };
-    if (ready) load_h();
+    load_h(make_rsrc(slot, ready ? kP * kN * 4 : 0));
 
     // ---- x' into LDS: the outputs' x' on the fast path; on the exact path
     // first x'' = exp(cs_last - cs_s) dt_s x_s for the chunk state
@@ -368,20 +373,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         store_xt_korder(raw, sc, xt, tid);
     }
 
-    // ---- first operands of the output phase, in flight during the wait (not
-    // hoisted above the chunk state)
-    __builtin_amdgcn_sched_barrier(0);
-    OutItem it;
-    it.ctp = (const u32x4 *)(a.ws_ct + cg * kBTChunk) + lane;
-    it.gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
-    it.tok0 = tok0;
-    it.Qc = Qc;
-    it.h = h;
-    it.Dh = Dh;
-    it.exact = exact;
-    u32x4 cop[8], gA[2][2], gB[3][2];
-    load_c_tile(it, wave, cop);
-
     // ---- h_{c-1}: the initial state, or chunk c-1's hand-off
     jitter_sleep(a, (unsigned)bh * 131u + (unsigned)c * 7u + 2u);
     if (c == 0) {
@@ -409,7 +400,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             tk[3] = ok && !(seen & kChainPoison);
         }
         __syncthreads();
-        load_h();
+        load_h(make_rsrc(slot, kP * kN * 4));
         if (!tk[3]) {
 #pragma unroll
             for (int acc = 0; acc < 2; ++acc)
@@ -424,6 +415,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
             for (int v = 0; v < 16; ++v) hp[acc][v] = __builtin_nanf("");
     }
+
+    // ---- first operands of the output phase, the C operands of both column
+    // tiles (not hoisted above the chunk state), requested after every load
+    // of h_{c-1} on every path: the combine below then waits for h_{c-1}
+    // alone, and these arrive while h_c is formed and published
+    __builtin_amdgcn_sched_barrier(0);
+    OutItem it;
+    it.ctp = (const u32x4 *)(a.ws_ct + cg * kBTChunk) + lane;
+    it.gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
+    it.tok0 = tok0;
+    it.Qc = Qc;
+    it.h = h;
+    it.Dh = Dh;
+    it.exact = exact;
+    u32x4 cop[8], copB[8];
+    out_first_loads(it, wave, cop, copB);
 
     // ---- h_c, rounded once: h + (expm1(cs_last) h + S); h_{c-1} into LDS
     // as bf16 ([P][N], 16-byte chunks XOR-swizzled by row) for the outputs
@@ -466,20 +473,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
     }
 
-    {
-        const int ltA = wave, ltB = kTiles - 1 - wave;
-        const u32x4 *pa = gt_tile(it, 0, ltA);
-        const u32x4 *pb = gt_tile(it, 0, ltB);
-        gA[0][0] = pa[0];
-        gA[0][1] = pa[64];
-        gB[0][0] = pb[0];
-        gB[0][1] = pb[64];
-        const u32x4 *pb1 = gt_tile(it, 1, ltB);
-        gB[1][0] = pb1[0];
-        gB[1][1] = pb1[64];
-    }
     __syncthreads();
-    out_tiles<kNtY>(a, it, smem, cop, gA, gB, tid);
+    out_tiles<kNtY>(a, it, smem, cop, copB, tid);
 }
 
 }  // namespace

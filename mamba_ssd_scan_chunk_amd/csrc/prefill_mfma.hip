@@ -227,9 +227,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     const int g = h / (a.H / a.G);
     const long cg = (long)bc * a.G + g;
 
-    // every global load of this workgroup is issued before the cumsum, dt
-    // first: loads retire in issue order, so the cumsum waits for dt only
-    const float dtv = load_dt(a, tok0, Qc, h, tid);
+    // every global load of this workgroup is issued before the cumsum, the
+    // step and A_log first: loads retire in issue order, so the cumsum waits
+    // for those only
+    const DecayIn din = load_decay_in(a, tok0, Qc, h, tid);
     u32x4 raw[8];
     load_x_raw<kNt>(a, tok0, Qc, h, raw, tid);
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
@@ -238,7 +239,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma(PrefillArgs a) {
     for (int gg = 0; gg < kQ / 16; ++gg) bq[gg] = bt[gg * 64];
 
     // cumsum within each 64-token wave (fp32); cs_last - cs_t from the wave totals
-    const float loc = wave_inclusive_sum(dtv * -expf(a.A_log[h]));
+    const float dtv = step_of(a, din, Qc, tid);
+    const float loc = wave_inclusive_sum(dtv * -expf(din.alog));
     if (lane == 63) wv[wave] = loc;
     __syncthreads();
     float after = 0.0f, total = 0.0f;
@@ -304,10 +306,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int g = h / (a.H / a.G);
     const long cg = (long)bc * a.G + g;
 
-    // ---- global loads, all issued before the cumsum: dt, x, h_{c-1}, the C
-    // operands of column tile ltA and the first G^T tiles
-    // dt first: loads retire in issue order, so the cumsum waits for dt only
-    const float dtv = load_dt(a, tok0, Qc, h, tid);
+    // ---- global loads, all issued before the cumsum: the step, A_log and D,
+    // x, h_{c-1} and the C operands of both column tiles.
+    // The step, A_log and D first: loads retire in issue order, so the cumsum
+    // waits for those only
+    const DecayIn din = load_decay_in(a, tok0, Qc, h, tid);
     u32x4 raw[8], hv[4];
     load_x_raw<kNt>(a, tok0, Qc, h, raw, tid);
     {
@@ -321,12 +324,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     it.tok0 = tok0;
     it.Qc = Qc;
     it.h = h;
-    it.Dh = a.D ? a.D[h] : 0.0f;
-    u32x4 cop[8], gA[2][2], gB[3][2];
-    out_first_loads(it, wave, cop, gA, gB);
+    it.Dh = din.D;
+    u32x4 cop[8], copB[8];
+    out_first_loads(it, wave, cop, copB);
 
     float total;
-    it.exact = chunk_decay(dtv, -expf(a.A_log[h]), it.Dh, Qc, vt, ut, dtt, wv, tid, lane, wave, &total);
+    const float dtv = step_of(a, din, Qc, tid);
+    it.exact = chunk_decay(dtv, -expf(din.alog), it.Dh, Qc, vt, ut, dtt, wv, tid, lane, wave, &total);
 
     // ---- x' into LDS (tokens in K order), h_{c-1} into LDS
     {
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
     }
     __syncthreads();
-    out_tiles<kNt>(a, it, smem, cop, gA, gB, tid);
+    out_tiles<kNt>(a, it, smem, cop, copB, tid);
 }
 
 // ------------------------------------------------------------------------

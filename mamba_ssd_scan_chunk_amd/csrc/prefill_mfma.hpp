@@ -106,14 +106,31 @@ __device__ __forceinline__ void load_x_raw(const PrefillArgs &a, long tok0, int 
     }
 }
 
-// dt of token tid of the chunk (0 at or past Qc), after the optional
-// preprocessing of the raw value.
-__device__ __forceinline__ float load_dt(const PrefillArgs &a, long tok0, int Qc, int h, int t) {
+// What the chunk's decay tables are made of: the step of token t as stored
+// (0 at or past Qc), A_log[h], D[h] and the step bias of head h (0 without
+// one).  An item requests these before any other global load: vector loads
+// retire in issue order, so the cumsum, which needs all four, then waits for
+// them alone while x and the operand tiles are still on their way (a per-head
+// value loaded after x makes the cumsum wait for x as well).  No arithmetic
+// is done on them here: that too would wait, and delay the loads after it.
+struct DecayIn {
+    float dt, alog, D, bias;
+};
+__device__ __forceinline__ DecayIn load_decay_in(const PrefillArgs &a, long tok0, int Qc, int h, int t) {
+    DecayIn d;
     const float *d0 = a.dt + tok0 * a.H + h;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(d0, (unsigned)((Qc - 1) * a.H + 1) * 4);
-    const float v = buf_load_f32(r, (unsigned)t * a.H * 4);
-    if (!a.dtp.dt_raw) return v;
-    return t < Qc ? dt_value(v, 1, a.dtp.dt_bias, h, a.dtp.dt_min, a.dtp.dt_max) : 0.0f;
+    d.dt = buf_load_f32(r, (unsigned)t * a.H * 4);
+    d.alog = a.A_log[h];
+    d.D = a.D ? a.D[h] : 0.0f;
+    d.bias = a.dtp.dt_raw && a.dtp.dt_bias ? a.dtp.dt_bias[h] : 0.0f;
+    return d;
+}
+// The step of token t the scan uses: the stored value, or with a raw step
+// softplus(raw + bias) clipped to [dt_min, dt_max] (0 at or past Qc).
+__device__ __forceinline__ float step_of(const PrefillArgs &a, const DecayIn &d, int Qc, int t) {
+    if (!a.dtp.dt_raw) return d.dt;
+    return t < Qc ? dt_softplus_clamp(d.dt + d.bias, a.dtp.dt_min, a.dtp.dt_max) : 0.0f;
 }
 
 constexpr int kXRow = kQ * 2 + 16;        // x'^T row stride in LDS (bytes), padded against bank conflicts
@@ -289,8 +306,8 @@ __device__ __forceinline__ void x_scales(const float *vt, bool exact, int tid, f
 // Step k applies token tile k to both column tiles (while k <= lt), so the
 // two Horner chains of a wave (four accumulators) hide each other's MFMA ->
 // VALU -> MFMA latency, and the x'^T operands of token tile k are read once
-// for both.  `cop` holds the C operands of column tile ltA, gA / gB the
-// G^T tiles of steps 0 (ltA) and 0, 1 (ltB), all already requested.
+// for both.  `cop` and `copB` hold the C operands of column tiles ltA and
+// ltB, already requested.
 // ------------------------------------------------------------------------
 struct OutItem {
     const u32x4 *ctp;  // C operands of the chunk and group (this lane's)
@@ -308,27 +325,17 @@ __device__ __forceinline__ void load_c_tile(const OutItem &it, int lt, u32x4 (&c
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) cop[kk] = it.ctp[(lt * 8 + kk) * 64];
 }
-// Requests of the first operands of wave `wave`: C of column tile ltA, G^T
-// of steps 0 (ltA) and 0, 1 (ltB >= 4).
-__device__ __forceinline__ void out_first_loads(const OutItem &it, int wave, u32x4 (&cop)[8], u32x4 (&gA)[2][2],
-                                                u32x4 (&gB)[3][2]) {
-    const int ltA = wave, ltB = kTiles - 1 - wave;
-    load_c_tile(it, ltA, cop);
-    const u32x4 *pa = gt_tile(it, 0, ltA);
-    const u32x4 *pb = gt_tile(it, 0, ltB);
-    gA[0][0] = pa[0];
-    gA[0][1] = pa[64];
-    gB[0][0] = pb[0];
-    gB[0][1] = pb[64];
-    const u32x4 *pb1 = gt_tile(it, 1, ltB);
-    gB[1][0] = pb1[0];
-    gB[1][1] = pb1[64];
+// Requests of the first operands of wave `wave`: the C operands of its
+// column tiles ltA and ltB.
+__device__ __forceinline__ void out_first_loads(const OutItem &it, int wave, u32x4 (&cop)[8], u32x4 (&copB)[8]) {
+    load_c_tile(it, wave, cop);
+    load_c_tile(it, kTiles - 1 - wave, copB);
 }
 
 // kNtY: the y rows are written with non-temporal stores.
 template <bool kNtY = false>
 __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &it, char *smem, u32x4 (&cop)[8],
-                                          u32x4 (&gA)[2][2], u32x4 (&gB)[3][2], int tid) {
+                                          u32x4 (&copB)[8], int tid) {
     const char *xt = smem + K3_XT;
     const char *hl = smem + K3_H;
     const float *vt = (const float *)(smem + K3_V);
@@ -350,17 +357,40 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
     const int hrow = li * 256;
     const int hsw = li & 15;
 
-    // carried-in state: acc = h_{c-1} C^T (K = N) for both column tiles
-    auto state_term = [&](const u32x4 (&cp)[8], f32x16 &y0, f32x16 &y1) {
+    // carried-in state: acc = h_{c-1} C^T (K = N) for both feature tiles of
+    // column tile ltA, and of ltB as well when `both` (each h_{c-1} operand
+    // is read once for the two column tiles).  The G^T tiles of the first
+    // steps (0 for ltA, 0 and 1 for ltB) are requested during it.
+    u32x4 gA[2][2], gB[3][2];
+    auto state_term = [&](bool both, f32x16 &y0, f32x16 &y1, f32x16 &z0, f32x16 &z1) {
         y0 = f32x16{};
         y1 = f32x16{};
+        z0 = f32x16{};
+        z1 = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
+            if (kk == 4) {
+                const u32x4 *pa = gt_tile(it, 0, ltA);
+                gA[0][0] = pa[0];
+                gA[0][1] = pa[64];
+                if (both) {
+                    const u32x4 *pb = gt_tile(it, 0, ltB);
+                    gB[0][0] = pb[0];
+                    gB[0][1] = pb[64];
+                    const u32x4 *pb1 = gt_tile(it, 1, ltB);
+                    gB[1][0] = pb1[0];
+                    gB[1][1] = pb1[64];
+                }
+            }
             const int off = hrow + (((2 * kk + lh) ^ hsw) << 4);
             const u32x4 a0 = *(const u32x4 *)(hl + off);
             const u32x4 a1 = *(const u32x4 *)(hl + off + 32 * 256);
-            y0 = mfma32(a0, cp[kk], y0);
-            y1 = mfma32(a1, cp[kk], y1);
+            y0 = mfma32(a0, cop[kk], y0);
+            y1 = mfma32(a1, cop[kk], y1);
+            if (both) {
+                z0 = mfma32(a0, copB[kk], z0);
+                z1 = mfma32(a1, copB[kk], z1);
+            }
         }
     };
     const int lA = ltA * 32 + li, lB = ltB * 32 + li;
@@ -401,9 +431,7 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
 
     f32x16 yA0 = {}, yA1 = {}, yB0 = {}, yB1 = {};
     if (doB) {
-        state_term(cop, yA0, yA1);
-        load_c_tile(it, ltB, cop);
-        state_term(cop, yB0, yB1);
+        state_term(true, yA0, yA1, yB0, yB1);
         if (exact) {
             const float eA = exp_fast(cst[lA]), eB = exp_fast(cst[lB]);
 #pragma unroll
@@ -469,7 +497,7 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
         }
     } else if (doA) {
         // column tile ltA alone (its tile ltB is past the chunk's last token)
-        state_term(cop, yA0, yA1);
+        state_term(false, yA0, yA1, yB0, yB1);
         if (exact) {
             const float eA = exp_fast(cst[lA]);
 #pragma unroll
