@@ -423,7 +423,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     __builtin_amdgcn_sched_barrier(0);
     OutItem it;
     it.ctp = (const u32x4 *)(a.ws_ct + cg * kBTChunk) + lane;
-    it.gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
+    it.gtr = gt_rsrc(a, cg);
+    it.lane16 = (unsigned)lane * 16u;
     it.tok0 = tok0;
     it.Qc = Qc;
     it.h = h;
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 
     __syncthreads();
-    out_tiles<kNtY>(a, it, smem, cop, copB, tid);
+    out_tiles<kNtY, false>(a, it, smem, cop, copB, tid);
 }
 
 }  // namespace

@@ -320,7 +320,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
     OutItem it;
     it.ctp = (const u32x4 *)(a.ws_ct + cg * kBTChunk) + lane;
-    it.gtp = (const u32x4 *)(a.ws_gt + cg * kGTChunk) + lane;
+    it.gtr = gt_rsrc(a, cg);
+    it.lane16 = (unsigned)lane * 16u;
     it.tok0 = tok0;
     it.Qc = Qc;
     it.h = h;
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
     }
     __syncthreads();
-    out_tiles<kNt>(a, it, smem, cop, copB, tid);
+    out_tiles<kNt, true>(a, it, smem, cop, copB, tid);
 }
 
 // ------------------------------------------------------------------------
@@ -363,17 +364,19 @@ __device__ __forceinline__ void state_walk(const PrefillArgs &a, long e) {
     const SeqEntry sq = seq_chunks(a, bh / a.H);
     float4 hv = a.init_state ? ((const float4 *)a.init_state)[bh * PN4 + pn] : make_float4(0.f, 0.f, 0.f, 0.f);
     const int nch = sq.n;
-    constexpr int kB = 8;
+    // 16 chunks of states and decays requested at once (a 4096-token
+    // sequence in one round trip), with the same loads on every path (past
+    // the last chunk the last chunk again, not used): vector loads retire in
+    // issue order, so each chunk's update waits for its own operands only
+    constexpr int kB = 16;
     for (int c0 = 0; c0 < nch; c0 += kB) {
         float4 sv[kB];
         float dv[kB];
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
-            if (c0 + j < nch) {
-                const long hc = ((long)sq.f0 + c0 + j) * a.H + h;
-                sv[j] = ((const float4 *)(a.ws_S + hc * kP * kN))[pn];
-                dv[j] = a.ws_dec[hc];
-            }
+            const long hc = ((long)sq.f0 + min(c0 + j, nch - 1)) * a.H + h;
+            sv[j] = ((const float4 *)(a.ws_S + hc * kP * kN))[pn];
+            dv[j] = a.ws_dec[hc];
         }
 #pragma unroll
         for (int j = 0; j < kB; ++j) {

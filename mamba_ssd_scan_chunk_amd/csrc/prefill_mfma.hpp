@@ -311,15 +311,28 @@ __device__ __forceinline__ void x_scales(const float *vt, bool exact, int tid, f
 // ------------------------------------------------------------------------
 struct OutItem {
     const u32x4 *ctp;  // C operands of the chunk and group (this lane's)
-    const u32x4 *gtp;  // G^T tiles of the chunk and group (this lane's)
+    __amdgpu_buffer_rsrc_t gtr;  // G^T tiles of the chunk and group
+    unsigned lane16;             // this lane's byte offset in a tile
     long tok0;
     int Qc, h;
     float Dh;
     bool exact;
 };
 
-__device__ __forceinline__ const u32x4 *gt_tile(const OutItem &it, int si, int lt) {
-    return it.gtp + gt_index(si, lt) * 128;  // halves at [0] and [64]
+// The G^T tiles of a chunk and group: per tile two 1 KiB halves of 16 bytes
+// per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gt_rsrc(const PrefillArgs &a, long cg) {
+    return make_rsrc(a.ws_gt + cg * kGTChunk, (unsigned)(kGTChunk * 2));
+}
+// G^T tile (si, lt) into g.  With `use` false the two loads are still issued,
+// past the end of the tiles: they return zeros without a memory access.  A
+// loop that requests tiles under conditions then issues the same loads in the
+// same order on every path, and as vector loads retire in issue order, each
+// step waits for its own tiles only, not for the ones requested after them.
+__device__ __forceinline__ void load_gt(const OutItem &it, int si, int lt, bool use, u32x4 (&g)[2]) {
+    const unsigned off = use ? (unsigned)gt_index(si, lt) * 2048u + it.lane16 : 0x40000000u;
+    g[0] = buf_load16(it.gtr, off);
+    g[1] = buf_load16(it.gtr, off + 1024u);
 }
 __device__ __forceinline__ void load_c_tile(const OutItem &it, int lt, u32x4 (&cop)[8]) {
 #pragma unroll
@@ -333,7 +346,12 @@ __device__ __forceinline__ void out_first_loads(const OutItem &it, int wave, u32
 }
 
 // kNtY: the y rows are written with non-temporal stores.
-template <bool kNtY = false>
+// kIssueAll: every G^T request of the loops is issued on every path (empty
+// where not needed, see load_gt); otherwise only the needed ones are.  The
+// output kernel runs faster with the former (B = 1, L = 4096 2.7B-shaped
+// layer: 64.3 -> 63.4 us per call), the chained kernel with the latter
+// (B = 8, L = 16384: 1271 against 1285 us).
+template <bool kNtY, bool kIssueAll>
 __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &it, char *smem, u32x4 (&cop)[8],
                                           u32x4 (&copB)[8], int tid) {
     const char *xt = smem + K3_XT;
@@ -362,6 +380,12 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
     // is read once for the two column tiles).  The G^T tiles of the first
     // steps (0 for ltA, 0 and 1 for ltB) are requested during it.
     u32x4 gA[2][2], gB[3][2];
+    auto want = [&](int si, int lt, bool use, u32x4 (&g)[2]) {
+        if (kIssueAll)
+            load_gt(it, si, lt, use, g);
+        else if (use)
+            load_gt(it, si, lt, true, g);
+    };
     auto state_term = [&](bool both, f32x16 &y0, f32x16 &y1, f32x16 &z0, f32x16 &z1) {
         y0 = f32x16{};
         y1 = f32x16{};
@@ -370,17 +394,9 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             if (kk == 4) {
-                const u32x4 *pa = gt_tile(it, 0, ltA);
-                gA[0][0] = pa[0];
-                gA[0][1] = pa[64];
-                if (both) {
-                    const u32x4 *pb = gt_tile(it, 0, ltB);
-                    gB[0][0] = pb[0];
-                    gB[0][1] = pb[64];
-                    const u32x4 *pb1 = gt_tile(it, 1, ltB);
-                    gB[1][0] = pb1[0];
-                    gB[1][1] = pb1[64];
-                }
+                want(0, ltA, true, gA[0]);
+                want(0, ltB, both, gB[0]);
+                want(1, ltB, both, gB[1]);
             }
             const int off = hrow + (((2 * kk + lh) ^ hsw) << 4);
             const u32x4 a0 = *(const u32x4 *)(hl + off);
@@ -445,17 +461,10 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
         // ---- intra-chunk term: step k applies token tile k to both column tiles
 #pragma unroll
         for (int k = 0; k < kTiles; ++k) {
+            // G^T tiles two steps (ltB) and one step (ltA) ahead
+            want(k + 2, ltB, k + 2 <= ltB, gB[(k + 2) % 3]);
+            want(k + 1, ltA, k + 1 <= ltA, gA[(k + 1) & 1]);
             if (k <= ltB) {
-                if (k + 2 <= ltB) {
-                    const u32x4 *pb = gt_tile(it, k + 2, ltB);
-                    gB[(k + 2) % 3][0] = pb[0];
-                    gB[(k + 2) % 3][1] = pb[64];
-                }
-                if (k + 1 <= ltA) {
-                    const u32x4 *pa = gt_tile(it, k + 1, ltA);
-                    gA[(k + 1) & 1][0] = pa[0];
-                    gA[(k + 1) & 1][1] = pa[64];
-                }
                 u32x4 xa[2][2];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
@@ -508,12 +517,8 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
         }
 #pragma unroll
         for (int k = 0; k < kTiles; ++k) {
+            want(k + 1, ltA, k + 1 <= ltA, gA[(k + 1) & 1]);
             if (k <= ltA) {
-                if (k + 1 <= ltA) {
-                    const u32x4 *pa = gt_tile(it, k + 1, ltA);
-                    gA[(k + 1) & 1][0] = pa[0];
-                    gA[(k + 1) & 1][1] = pa[64];
-                }
                 u32x4 xa[2][2];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
