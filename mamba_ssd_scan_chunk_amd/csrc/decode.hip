@@ -237,10 +237,13 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
     const int hpg = H / a.G;
     const int GR = hpg * P;                      // state rows per (batch, group)
     const int npb = (GR + S::PBLK - 1) / S::PBLK;
-    const int pb = blockIdx.x % npb;
-    const long bg = blockIdx.x / npb;            // b * G + g
-    const int g = (int)(bg % a.G);
-    const int b = (int)(bg / a.G);
+    // 32-bit quotients (the grid is below 2^31 workgroups): a 64-bit one
+    // costs the scalar unit about a hundred instructions before the first
+    // state load can be addressed
+    const int pb = (int)blockIdx.x % npb;
+    const int bg = (int)blockIdx.x / npb;        // b * G + g
+    const int g = bg % a.G;
+    const int b = bg / a.G;
     const int r0 = pb * S::PBLK;                 // first row within the group
     const int prows = min(S::PBLK, GR - r0);
     const long HP = (long)H * P, GN = (long)a.G * N, C = HP + 2 * GN;

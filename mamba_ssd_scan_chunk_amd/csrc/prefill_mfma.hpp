@@ -379,7 +379,9 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
     // column tile ltA, and of ltB as well when `both` (each h_{c-1} operand
     // is read once for the two column tiles).  The G^T tiles of the first
     // steps (0 for ltA, 0 and 1 for ltB) are requested during it.
-    u32x4 gA[2][2], gB[3][2];
+    // ltB's tiles are requested DB steps ahead
+    constexpr int DB = kIssueAll ? 2 : 1;
+    u32x4 gA[2][2], gB[DB + 1][2];
     auto want = [&](int si, int lt, bool use, u32x4 (&g)[2]) {
         if (kIssueAll)
             load_gt(it, si, lt, use, g);
@@ -396,7 +398,7 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
             if (kk == 4) {
                 want(0, ltA, true, gA[0]);
                 want(0, ltB, both, gB[0]);
-                want(1, ltB, both, gB[1]);
+                if (DB == 2) want(1, ltB, both, gB[1 % (DB + 1)]);
             }
             const int off = hrow + (((2 * kk + lh) ^ hsw) << 4);
             const u32x4 a0 = *(const u32x4 *)(hl + off);
@@ -461,8 +463,8 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
         // ---- intra-chunk term: step k applies token tile k to both column tiles
 #pragma unroll
         for (int k = 0; k < kTiles; ++k) {
-            // G^T tiles two steps (ltB) and one step (ltA) ahead
-            want(k + 2, ltB, k + 2 <= ltB, gB[(k + 2) % 3]);
+            // G^T tiles DB steps (ltB) and one step (ltA) ahead
+            want(k + DB, ltB, k + DB <= ltB, gB[(k + DB) % (DB + 1)]);
             want(k + 1, ltA, k + 1 <= ltA, gA[(k + 1) & 1]);
             if (k <= ltB) {
                 u32x4 xa[2][2];
@@ -488,7 +490,7 @@ __device__ __forceinline__ void out_tiles(const PrefillArgs &a, const OutItem &i
                     }
                 }
                 {
-                    u32x4 g2[2] = {gB[k % 3][0], gB[k % 3][1]};
+                    u32x4 g2[2] = {gB[k % (DB + 1)][0], gB[k % (DB + 1)][1]};
                     if (exact) scale_tile_exact(g2, cst, dtt, cslB, k, lh);
                     if (k == ltB) add_diagonal(g2, dlB, li, lh);
 #pragma unroll
