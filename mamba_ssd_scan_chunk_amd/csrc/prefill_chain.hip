@@ -262,11 +262,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const DecayIn din = load_decay_in(a, tok0, Qc, h, tid);
     u32x4 raw[8];
     load_x_raw<kNtX>(a, tok0, Qc, h, raw, tid);
-    // B operands of the first two token tiles (the rest are streamed)
+    // B operands of the first token tile (the rest are streamed one tile
+    // ahead: B = 8, L = 16384 1259 -> 1245 us against two tiles ahead; the
+    // kernel does better with fewer loads in flight); packed sequences: the
+    // first two, then two ahead
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[4];
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) bq[gg] = bt[gg * 64];
+    for (int gg = 0; gg < (kPacked ? 4 : 2); ++gg) bq[gg] = bt[gg * 64];
     const float Dh = din.D;
     if (tid == 0) tk[2] = early;
     float total;
@@ -334,6 +337,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                     s1[v] *= q;
                 }
             }
+            if (!kPacked && k + 1 < kTiles) {  // token tile k + 1, one step ahead
+                bq[(2 * k + 2) & 3] = bt[(2 * k + 2) * 64];
+                bq[(2 * k + 3) & 3] = bt[(2 * k + 3) * 64];
+            }
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const u32x4 a0 = *(const u32x4 *)(xt + xt_operand(li, lh, k, hf));
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 s0 = mfma32(a0, bq[(2 * k + hf) & 3], s0);
                 s1 = mfma32(a1, bq[(2 * k + hf) & 3], s1);
             }
-            if (k + 2 < ntl) {  // token tile k + 2 into the registers tile k used
+            if (kPacked && k + 2 < ntl) {  // token tile k + 2 into the registers tile k used
                 bq[(2 * k) & 3] = bt[(2 * k + 4) * 64];
                 bq[(2 * k + 1) & 3] = bt[(2 * k + 5) * 64];
             }
