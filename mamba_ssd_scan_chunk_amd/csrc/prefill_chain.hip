@@ -264,12 +264,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     load_x_raw<kNtX>(a, tok0, Qc, h, raw, tid);
     // B operands of the first token tile (the rest are streamed one tile
     // ahead: B = 8, L = 16384 1259 -> 1245 us against two tiles ahead; the
-    // kernel does better with fewer loads in flight); packed sequences: the
-    // first two, then two ahead
+    // kernel does better with fewer loads in flight)
     const u32x4 *bt = (const u32x4 *)(a.ws_bt + cg * kBTChunk) + (wave * (kQ / 16)) * 64 + lane;
     u32x4 bq[4];
 #pragma unroll
-    for (int gg = 0; gg < (kPacked ? 4 : 2); ++gg) bq[gg] = bt[gg * 64];
+    for (int gg = 0; gg < 2; ++gg) bq[gg] = bt[gg * 64];
+    // packed sequences: a tile past the chunk's last token is requested past
+    // the end of this resource (zeros, no memory access), so that every path
+    // issues the same loads
+    const __amdgpu_buffer_rsrc_t btr = make_rsrc(bt - lane, (unsigned)(kQ / 16) * 64 * 16);
     const float Dh = din.D;
     if (tid == 0) tk[2] = early;
     float total;
@@ -328,6 +331,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     f32x16 s0 = {}, s1 = {};
 #pragma unroll
     for (int k = 0; k < kTiles; ++k) {
+        if (kPacked && k + 1 < kTiles) {  // token tile k + 1, one step ahead
+            const unsigned off = k + 1 < ntl ? (unsigned)((2 * k + 2) * 64 + lane) * 16u : 0x40000000u;
+            bq[(2 * k + 2) & 3] = buf_load16(btr, off);
+            bq[(2 * k + 3) & 3] = buf_load16(btr, off + 1024u);
+        }
         if (k < ntl) {
             if (k > 0) {
                 const float q = wv[K3_WQ + k];
@@ -347,10 +355,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 const u32x4 a1 = *(const u32x4 *)(xt + xt_operand(32 + li, lh, k, hf));
                 s0 = mfma32(a0, bq[(2 * k + hf) & 3], s0);
                 s1 = mfma32(a1, bq[(2 * k + hf) & 3], s1);
-            }
-            if (kPacked && k + 2 < ntl) {  // token tile k + 2 into the registers tile k used
-                bq[(2 * k) & 3] = bt[(2 * k + 4) * 64];
-                bq[(2 * k + 1) & 3] = bt[(2 * k + 5) * 64];
             }
         }
     }
